@@ -1,0 +1,266 @@
+/*
+ * pkv.h -- C ABI of the paged-KV GQA decode library for MI355X (gfx950).
+ *
+ * The library runs the batched f16 decode step of a Llama/Qwen2-style decoder:
+ * per layer a fused RMSNorm + QKV projection with RoPE and the KV append into a
+ * block-table paged cache, paged GQA decode attention (split over the context
+ * plus a merge pass, f16 or FP8 E4M3 KV), the O projection with the residual
+ * add, a fused RMSNorm + gate/up projection with SiLU*mul, and the down
+ * projection with the residual add; then the final RMSNorm, the LM head and a
+ * greedy argmax.  The whole step can be captured once in a hipGraph and
+ * replayed on the caller's stream.
+ *
+ * Sources (rvLLM post on discuss.pytorch.kr, "rvLLM 소개"):
+ *   section "CUDA 그래프 리플레이"         -- per-step block tables and context
+ *       lengths uploaded before a replay on the caller's stream; the graph holds
+ *       the forward only (sampling stays outside);
+ *   section "퓨즈드 CUDA 커널"             -- the fused per-layer ops;
+ *   section "PagedAttention과 FlashAttention-3" -- block-table KV cache, GQA,
+ *       f16 KV by default, FP8 E4M3 KV as an option;
+ * zingnex.cn article "rvLLM：用Rust重写vLLM…", section 直接GPU调用 -- f16 GEMMs
+ *   for the batched projections.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless a comment says (host).
+ *   - Device memory belongs to the caller: the library never frees it.  Objects
+ *     made by *_create are freed by the matching *_destroy.
+ *   - Work is enqueued on the given stream (a hipStream_t passed as void*) and
+ *     the call does not synchronise it.  Host-side argument checks happen
+ *     before anything is enqueued; on an error nothing is enqueued.
+ *   - Every call returns pkv_status; no C++ exception and no abort crosses the
+ *     ABI.  pkv_last_error() returns a message for the calling thread's last
+ *     failed call.
+ *   - f16 is IEEE binary16; fp8 is OCP E4M3FN (1 sign, 4 exponent bits with
+ *     bias 7, 3 mantissa bits, no infinities, 0x7F/0xFF NaN, max 448).
+ *   - Device-side metadata (context lengths, block ids) is trusted: a context
+ *     length above max_context or a block id outside [0, num_blocks) is a
+ *     contract violation.  pkv_validate_metadata() checks host copies.
+ *
+ * Paged KV layout (block size BS = 16, Hkv KV heads, head_dim D in {64, 128}):
+ *   For layer l the cache memory holds the K pool, then the V pool:
+ *     K pool: [num_blocks][Hkv][BS][D]   (token-major inside a block)
+ *     V pool: [num_blocks][Hkv][D][BS]   (dim-major inside a block)
+ *   element size 2 bytes (f16) or 1 byte (fp8 codes).  Token t of sequence b is
+ *   in block block_tables[b * bt_stride + t / BS], slot t % BS.
+ *   context_lens[b] counts the cached tokens INCLUDING the token being decoded:
+ *   the new token's K/V go to position pos = context_lens[b] - 1 and attention
+ *   covers positions [0, context_lens[b]).  context_lens[b] == 0 marks an
+ *   inactive row (no append; attention output 0).  Block-table entries at
+ *   index >= ceil(context_lens[b] / BS) are never read.
+ *
+ * Query heads: head h reads KV head h / (Hq / Hkv) (contiguous groups);
+ * Hq / Hkv <= 16.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_E_ARG = 1,          /* invalid argument (null pointer, bad size, bad shape) */
+  PKV_E_UNSUPPORTED = 2,  /* valid but not implemented (head_dim, block size, dtype) */
+  PKV_E_NOMEM = 3,        /* host or device allocation failed */
+  PKV_E_CAPACITY = 4,     /* block allocator exhausted */
+  PKV_E_HIP = 5,          /* a HIP runtime call failed; message has hipGetErrorString */
+  PKV_E_STATE = 6         /* object used in a state that does not allow the call */
+} pkv_status;
+
+typedef enum { PKV_KV_F16 = 0, PKV_KV_FP8_E4M3 = 1 } pkv_kv_dtype;
+
+typedef void* pkv_stream_t; /* a hipStream_t; NULL is the null stream */
+
+typedef struct pkv_cache pkv_cache;
+typedef struct pkv_model pkv_model;
+typedef struct pkv_graph pkv_graph;
+typedef struct pkv_alloc pkv_alloc;
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* pkv_last_error(void);
+
+/* ------------------------------------------------------------------ KV cache */
+
+typedef struct {
+  int32_t num_layers;   /* >= 1 */
+  int32_t num_blocks;   /* physical blocks per layer, >= 1 */
+  int32_t block_size;   /* must be 16 */
+  int32_t num_kv_heads; /* Hkv >= 1 */
+  int32_t head_dim;     /* 64 or 128 */
+  int32_t dtype;        /* pkv_kv_dtype */
+} pkv_cache_desc;
+
+/* Bytes of device memory a cache with this description needs (host only). */
+pkv_status pkv_cache_bytes(const pkv_cache_desc* desc, size_t* bytes);
+
+/* Wrap caller-owned device memory (>= pkv_cache_bytes, 256-byte aligned) as a
+ * paged KV cache.  For fp8 caches k_scales / v_scales (host, [num_layers]) are
+ * the per-layer, per-tensor f32 scales (stored value = code value * scale);
+ * they must be NULL for f16 caches.  The memory is not initialised. */
+pkv_status pkv_kv_cache_create(const pkv_cache_desc* desc, void* dev_mem, size_t bytes,
+                               const float* k_scales, const float* v_scales, pkv_cache** out);
+void pkv_kv_cache_destroy(pkv_cache* cache);
+
+/* Device addresses of layer `layer`'s K and V pools (layout above). */
+pkv_status pkv_kv_cache_layer(const pkv_cache* cache, int layer, void** k_pool, void** v_pool);
+
+/* Append one token per row: k and v are f16 [batch][Hkv][D]; row b is stored
+ * at pos = context_lens[b] - 1 of layer `layer` (skipped when the length is 0).
+ * A pure copy: the stored bytes equal the input bytes.  f16 caches only
+ * (PKV_E_UNSUPPORTED for fp8).  block_tables: [batch][bt_stride] int32. */
+pkv_status pkv_kv_append(pkv_cache* cache, int layer, const void* k, const void* v,
+                         const int32_t* block_tables, int bt_stride,
+                         const int32_t* context_lens, int batch, pkv_stream_t stream);
+
+/* ----------------------------------------------------------------- attention */
+
+/* Scratch bytes paged_attn_decode needs for this shape (host only). */
+pkv_status pkv_attn_workspace_bytes(const pkv_cache* cache, int batch, int num_q_heads,
+                                    int max_context, size_t* bytes);
+
+/* Paged GQA decode attention for one layer (rvLLM post, section
+ * "PagedAttention과 FlashAttention-3"):
+ *   for query head h of row b, with g = h / (Hq / Hkv) and c = context_lens[b],
+ *     s_t = scale * <q[b][h], K_t>    (t < c)
+ *     out[b][h] = sum_t softmax(s)_t * V_t
+ *   with K_t, V_t read through the block table (fp8 codes are multiplied by the
+ *   layer's scales).  Accumulation is fp32; out is f16 [batch][Hq][D]; q is f16
+ *   [batch][Hq][D].  lse (nullable, f32 [batch][Hq]) receives max s +
+ *   ln(sum exp(s - max s)) (-inf for inactive rows).  The context is split into
+ *   partitions processed in parallel and merged in a second pass; workspace
+ *   (>= pkv_attn_workspace_bytes, 256-byte aligned) holds the partial results
+ *   and needs no initialisation.  bt_stride >= ceil(max_context / 16);
+ *   every context_lens[b] <= max_context. */
+pkv_status pkv_paged_attn_decode(const pkv_cache* cache, int layer, const void* q, void* out,
+                                 float* lse, const int32_t* block_tables, int bt_stride,
+                                 const int32_t* context_lens, int batch, int num_q_heads,
+                                 int max_context, float scale, void* workspace,
+                                 size_t workspace_bytes, pkv_stream_t stream);
+
+/* --------------------------------------------------------------------- model */
+
+typedef struct {
+  int32_t hidden;        /* H */
+  int32_t num_q_heads;   /* Hq */
+  int32_t num_kv_heads;  /* Hkv */
+  int32_t head_dim;      /* D: 64 or 128 */
+  int32_t ffn;           /* F */
+  int32_t vocab;         /* V */
+  int32_t num_layers;    /* L */
+  int32_t max_positions; /* RoPE table length: positions [0, max_positions) */
+  float rms_eps;
+  float rope_theta;
+} pkv_model_desc;
+
+/* Device pointers to one layer's f16 weights, matrices row-major [out][in]:
+ *   w_in [H]                    RMSNorm gain before attention
+ *   w_qkv [(Hq + 2 Hkv) D][H]   rows: q heads, then k heads, then v heads
+ *   b_qkv [(Hq + 2 Hkv) D]      QKV bias, nullable
+ *   w_o [H][Hq D]
+ *   w_post [H]                  RMSNorm gain before the MLP
+ *   w_gate_up [2F][H]           rows: gate (F rows), then up (F rows)
+ *   w_down [H][F] */
+typedef struct {
+  const void* w_in;
+  const void* w_qkv;
+  const void* b_qkv;
+  const void* w_o;
+  const void* w_post;
+  const void* w_gate_up;
+  const void* w_down;
+} pkv_layer_weights;
+
+/* Describe a model whose weights live in caller-owned device memory (borrowed,
+ * not copied; they must outlive the model).  embed [V][H], w_final_norm [H],
+ * w_lm_head [V][H] (untied).  layers: (host) array of num_layers entries.
+ * The model owns only a device RoPE table (cos, sin of pos * theta^(-2i/D),
+ * computed in double precision on the host).  Synchronous. */
+pkv_status pkv_model_create(const pkv_model_desc* desc, const void* embed,
+                            const pkv_layer_weights* layers, const void* w_final_norm,
+                            const void* w_lm_head, pkv_model** out);
+void pkv_model_destroy(pkv_model* model);
+
+/* Scratch bytes decode_layer / decode_step / graph_capture need (host only). */
+pkv_status pkv_step_workspace_bytes(const pkv_model* model, const pkv_cache* cache, int batch,
+                                    int max_context, size_t* bytes);
+
+/* One decoder layer for `batch` single-token rows (the pre-norm Llama/Qwen2
+ * layer; rvLLM post, section "퓨즈드 CUDA 커널"):
+ *   a = RMSNorm(h) * w_in; q,k,v = split(W_qkv a + b_qkv); q,k = RoPE(., pos)
+ *   append k, v at pos = context_lens[b] - 1; o = paged attention(q)
+ *   h1 = h + W_o o;  m = RMSNorm(h1) * w_post;  g,u = split(W_gate_up m)
+ *   h  = h1 + W_down (silu(g) * u)
+ * hidden: f16 [batch][H], updated in place.  The cache must be f16 with the
+ * model's Hkv and head_dim and at least layer+1 layers. */
+pkv_status pkv_decode_layer(const pkv_model* model, pkv_cache* cache, int layer, void* hidden,
+                            const int32_t* block_tables, int bt_stride,
+                            const int32_t* context_lens, int batch, int max_context,
+                            void* workspace, size_t workspace_bytes, pkv_stream_t stream);
+
+/* One decode step: h = embed[token_ids[b]], every layer, then
+ * logits = W_lm RMSNorm(h) * w_final_norm.  token_ids int32 [batch];
+ * logits f16 [batch][V]; hidden_out (nullable) f16 [batch][H] gets the final
+ * pre-norm hidden state.  Appends each row's token to the cache at
+ * pos = context_lens[b] - 1 in every layer. */
+pkv_status pkv_decode_step(const pkv_model* model, pkv_cache* cache, const int32_t* token_ids,
+                           const int32_t* block_tables, int bt_stride,
+                           const int32_t* context_lens, int batch, int max_context,
+                           void* logits, void* hidden_out, void* workspace,
+                           size_t workspace_bytes, pkv_stream_t stream);
+
+/* Greedy token per row: the lowest index of the largest f16 logit
+ * (zingnex.cn article, section 支持的参数: temperature 0 decodes greedily).
+ * logits f16 [batch][vocab]; tokens int32 [batch]. */
+pkv_status pkv_argmax(const void* logits, int batch, int vocab, int32_t* tokens,
+                      pkv_stream_t stream);
+
+/* ------------------------------------------------------------- graph replay */
+
+/* Capture one pkv_decode_step (same arguments) into a hipGraph on
+ * capture_stream (not the null stream).  Every pointer is baked into the
+ * graph: before each replay the caller rewrites the CONTENTS of token_ids,
+ * block_tables and context_lens (ordered on the replay stream, rvLLM post
+ * section "CUDA 그래프 리플레이").  Nothing is allocated inside the captured
+ * region. */
+pkv_status pkv_graph_capture(const pkv_model* model, pkv_cache* cache, const int32_t* token_ids,
+                             const int32_t* block_tables, int bt_stride,
+                             const int32_t* context_lens, int batch, int max_context,
+                             void* logits, void* hidden_out, void* workspace,
+                             size_t workspace_bytes, pkv_stream_t capture_stream,
+                             pkv_graph** out);
+/* Launch the captured step on the caller's stream. */
+pkv_status pkv_graph_replay(pkv_graph* graph, pkv_stream_t stream);
+void pkv_graph_destroy(pkv_graph* graph);
+
+/* ----------------------------------------------------- host block allocator */
+
+/* Free list of num_blocks physical block ids.  seed 0 hands ids out in
+ * ascending order; any other seed shuffles the free list once (deterministic
+ * for a given seed), which tests use to scatter a sequence's blocks. */
+pkv_status pkv_alloc_create(int num_blocks, uint64_t seed, pkv_alloc** out);
+/* Grow a (host) block-table row from old_len to new_len tokens: fills entries
+ * [ceil(old_len/16), ceil(new_len/16)) with fresh ids.  PKV_E_CAPACITY (row
+ * and allocator unchanged) when not enough blocks are free; PKV_E_ARG when
+ * new_len < old_len or the row is too short. */
+pkv_status pkv_alloc_grow(pkv_alloc* alloc, int32_t* row, int bt_stride, int old_len, int new_len);
+/* Return the ceil(len/16) blocks of a (host) row to the free list. */
+pkv_status pkv_alloc_release(pkv_alloc* alloc, const int32_t* row, int len);
+int pkv_alloc_free_blocks(const pkv_alloc* alloc);
+void pkv_alloc_destroy(pkv_alloc* alloc);
+
+/* Check (host) metadata: every length in [0, max_context], every needed block
+ * id in [0, num_blocks), no block used twice across rows, and
+ * bt_stride >= ceil(max_context / 16).  PKV_E_ARG with a message otherwise. */
+pkv_status pkv_validate_metadata(const int32_t* block_tables, int bt_stride,
+                                 const int32_t* context_lens, int batch, int num_blocks,
+                                 int max_context);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,233 @@
+"""Python binding of libpkv (include/pkv.h): argument marshalling only.
+
+Every call forwards torch tensors' device addresses and the current HIP
+stream to the C ABI; all arithmetic runs in the library's HIP kernels.  Import
+fails loudly when libpkv.so has not been built.
+"""
+import ctypes as C
+
+import torch
+
+from . import _abi
+from ._abi import CacheDesc, ModelDesc, LayerWeights, PkvError
+
+_lib = _abi.load()
+
+KV_F16 = 0
+KV_FP8_E4M3 = 1
+BLOCK_SIZE = 16
+
+
+def _check(status):
+    if status != 0:
+        raise PkvError(status, _lib.pkv_last_error().decode())
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor")
+
+
+def lib():
+    return _lib
+
+
+def _destroy(fn_name, obj):
+    h = getattr(obj, "handle", None)
+    if h and _lib is not None:
+        getattr(_lib, fn_name)(h)
+    obj.handle = None
+
+
+# ------------------------------------------------------------------ KV cache
+
+class KVCache:
+    """A paged KV cache in one torch-owned device buffer (layout in pkv.h)."""
+
+    def __init__(self, num_layers, num_blocks, num_kv_heads, head_dim, dtype=KV_F16,
+                 k_scales=None, v_scales=None, device="cuda"):
+        self.desc = CacheDesc(num_layers, num_blocks, BLOCK_SIZE, num_kv_heads, head_dim, dtype)
+        n = C.c_size_t()
+        _check(_lib.pkv_cache_bytes(C.byref(self.desc), C.byref(n)))
+        self.nbytes = n.value
+        self.mem = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        ks = vs = None
+        if dtype == KV_FP8_E4M3:
+            ks = (C.c_float * num_layers)(*[float(x) for x in k_scales])
+            vs = (C.c_float * num_layers)(*[float(x) for x in v_scales])
+        h = C.c_void_p()
+        _check(_lib.pkv_kv_cache_create(C.byref(self.desc), _p(self.mem), self.nbytes, ks, vs, C.byref(h)))
+        self.handle = h
+        self.num_layers, self.num_blocks = num_layers, num_blocks
+        self.num_kv_heads, self.head_dim, self.dtype = num_kv_heads, head_dim, dtype
+
+    def layer(self, layer):
+        """(K pool [NB, Hkv, 16, D], V pool [NB, Hkv, D, 16]) views of one layer."""
+        k, v = C.c_void_p(), C.c_void_p()
+        _check(_lib.pkv_kv_cache_layer(self.handle, layer, C.byref(k), C.byref(v)))
+        tdt = torch.uint8 if self.dtype == KV_FP8_E4M3 else torch.float16
+        elt = 1 if self.dtype == KV_FP8_E4M3 else 2
+        n = self.num_blocks * self.num_kv_heads * BLOCK_SIZE * self.head_dim * elt
+        base = self.mem.data_ptr()
+        kt = self.mem[k.value - base:k.value - base + n].view(tdt)
+        vt = self.mem[v.value - base:v.value - base + n].view(tdt)
+        nb, hkv, d = self.num_blocks, self.num_kv_heads, self.head_dim
+        return kt.view(nb, hkv, BLOCK_SIZE, d), vt.view(nb, hkv, d, BLOCK_SIZE)
+
+    def close(self):
+        _destroy("pkv_kv_cache_destroy", self)
+
+    __del__ = close
+
+
+def kv_append(cache, layer, k, v, block_tables, context_lens, stream=None):
+    _need(k, torch.float16, "k")
+    _need(v, torch.float16, "v")
+    _need(block_tables, torch.int32, "block_tables")
+    _need(context_lens, torch.int32, "context_lens")
+    _check(_lib.pkv_kv_append(cache.handle, layer, _p(k), _p(v), _p(block_tables), block_tables.shape[1],
+                              _p(context_lens), context_lens.shape[0], _stream(stream)))
+
+
+def attn_workspace_bytes(cache, batch, num_q_heads, max_context):
+    n = C.c_size_t()
+    _check(_lib.pkv_attn_workspace_bytes(cache.handle, batch, num_q_heads, max_context, C.byref(n)))
+    return n.value
+
+
+def paged_attn_decode(cache, layer, q, out, block_tables, context_lens, max_context, scale,
+                      workspace, lse=None, stream=None):
+    _need(q, torch.float16, "q")
+    _need(out, torch.float16, "out")
+    _need(block_tables, torch.int32, "block_tables")
+    _need(context_lens, torch.int32, "context_lens")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    _check(_lib.pkv_paged_attn_decode(cache.handle, layer, _p(q), _p(out), _p(lse), _p(block_tables),
+                                      block_tables.shape[1], _p(context_lens), q.shape[0], q.shape[1],
+                                      max_context, float(scale), _p(workspace), workspace.numel(),
+                                      _stream(stream)))
+
+
+# --------------------------------------------------------------------- model
+
+class Model:
+    """Borrows f16 device weights (dict as made by pkv_inputs.model_weights, on device)."""
+
+    def __init__(self, shape, weights, max_positions):
+        self.shape = shape
+        self.weights = weights  # keep the tensors alive
+        self.desc = ModelDesc(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn,
+                              shape.vocab, len(weights["layers"]), max_positions,
+                              float(shape.rms_eps), float(shape.rope_theta))
+        arr = (LayerWeights * len(weights["layers"]))()
+        for i, lw in enumerate(weights["layers"]):
+            arr[i] = LayerWeights(lw["w_in"].data_ptr(), lw["w_qkv"].data_ptr(),
+                                  lw["b_qkv"].data_ptr() if lw.get("b_qkv") is not None else None,
+                                  lw["w_o"].data_ptr(), lw["w_post"].data_ptr(),
+                                  lw["w_gate_up"].data_ptr(), lw["w_down"].data_ptr())
+        h = C.c_void_p()
+        _check(_lib.pkv_model_create(C.byref(self.desc), _p(weights["embed"]), arr,
+                                     _p(weights["w_final_norm"]), _p(weights["w_lm_head"]), C.byref(h)))
+        self.handle = h
+
+    def close(self):
+        _destroy("pkv_model_destroy", self)
+
+    __del__ = close
+
+
+def step_workspace_bytes(model, cache, batch, max_context):
+    n = C.c_size_t()
+    _check(_lib.pkv_step_workspace_bytes(model.handle, cache.handle, batch, max_context, C.byref(n)))
+    return n.value
+
+
+def decode_layer(model, cache, layer, hidden, block_tables, context_lens, max_context, workspace,
+                 stream=None):
+    _need(hidden, torch.float16, "hidden")
+    _check(_lib.pkv_decode_layer(model.handle, cache.handle, layer, _p(hidden), _p(block_tables),
+                                 block_tables.shape[1], _p(context_lens), hidden.shape[0], max_context,
+                                 _p(workspace), workspace.numel(), _stream(stream)))
+
+
+def decode_step(model, cache, token_ids, block_tables, context_lens, max_context, logits, workspace,
+                hidden_out=None, stream=None):
+    _need(token_ids, torch.int32, "token_ids")
+    _need(logits, torch.float16, "logits")
+    _check(_lib.pkv_decode_step(model.handle, cache.handle, _p(token_ids), _p(block_tables),
+                                block_tables.shape[1], _p(context_lens), token_ids.shape[0], max_context,
+                                _p(logits), _p(hidden_out), _p(workspace), workspace.numel(),
+                                _stream(stream)))
+
+
+def argmax(logits, tokens, stream=None):
+    _need(logits, torch.float16, "logits")
+    _need(tokens, torch.int32, "tokens")
+    _check(_lib.pkv_argmax(_p(logits), logits.shape[0], logits.shape[1], _p(tokens), _stream(stream)))
+
+
+class Graph:
+    """One captured decode step; replay() launches it on the caller's stream."""
+
+    def __init__(self, model, cache, token_ids, block_tables, context_lens, max_context, logits,
+                 workspace, hidden_out=None, capture_stream=None):
+        self.keep = (model, cache, token_ids, block_tables, context_lens, logits, workspace, hidden_out)
+        cs = capture_stream if capture_stream is not None else torch.cuda.Stream()
+        h = C.c_void_p()
+        _check(_lib.pkv_graph_capture(model.handle, cache.handle, _p(token_ids), _p(block_tables),
+                                      block_tables.shape[1], _p(context_lens), token_ids.shape[0],
+                                      max_context, _p(logits), _p(hidden_out), _p(workspace),
+                                      workspace.numel(), C.c_void_p(cs.cuda_stream), C.byref(h)))
+        self.handle = h
+
+    def replay(self, stream=None):
+        _check(_lib.pkv_graph_replay(self.handle, _stream(stream)))
+
+    def close(self):
+        _destroy("pkv_graph_destroy", self)
+
+    __del__ = close
+
+
+# ------------------------------------------------------------ host allocator
+
+class BlockAllocator:
+    def __init__(self, num_blocks, seed=0):
+        h = C.c_void_p()
+        _check(_lib.pkv_alloc_create(num_blocks, seed, C.byref(h)))
+        self.handle = h
+
+    def grow(self, row, old_len, new_len):
+        """row: a writable numpy int32 array (one block-table row)."""
+        ptr = row.ctypes.data_as(C.POINTER(C.c_int32))
+        _check(_lib.pkv_alloc_grow(self.handle, ptr, row.shape[0], old_len, new_len))
+
+    def release(self, row, length):
+        _check(_lib.pkv_alloc_release(self.handle, row.ctypes.data_as(C.POINTER(C.c_int32)), length))
+
+    @property
+    def free_blocks(self):
+        return _lib.pkv_alloc_free_blocks(self.handle)
+
+    def close(self):
+        _destroy("pkv_alloc_destroy", self)
+
+    __del__ = close
+
+
+def validate_metadata(block_tables, context_lens, num_blocks, max_context):
+    """Host (numpy int32) metadata check; raises PkvError on a violation."""
+    bt = block_tables
+    _check(_lib.pkv_validate_metadata(bt.ctypes.data_as(C.POINTER(C.c_int32)), bt.shape[1],
+                                      context_lens.ctypes.data_as(C.POINTER(C.c_int32)),
+                                      context_lens.shape[0], num_blocks, max_context))

@@ -1,0 +1,343 @@
+// Model object, decode layer / decode step orchestration, greedy argmax and
+// hipGraph capture / replay.
+//
+// Per layer (rvLLM post on discuss.pytorch.kr, section "퓨즈드 CUDA 커널" for
+// the fused ops; section "PagedAttention과 FlashAttention-3" for the paged GQA
+// attention):
+//   1. RMSNorm(h) * w_in + QKV projection + bias          (one kernel, fp32 qkv)
+//   2. RoPE of q and k + append of k, v into the cache   (one kernel)
+//   3. paged GQA attention: split + merge                (two kernels)
+//   4. O projection + residual add into h                (one kernel)
+//   5. RMSNorm(h) * w_post + gate/up projection + SiLU*mul (one kernel)
+//   6. down projection + residual add into h             (one kernel)
+// The step adds the embedding gather before the layers and RMSNorm + LM head
+// after them.  Section "CUDA 그래프 리플레이": the forward is captured once in
+// a graph and replayed on the caller's stream; sampling (argmax) stays outside.
+#include <cmath>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "linear.h"
+#include "ops.h"
+#include "pkv_internal.h"
+
+using namespace pkv;
+
+struct pkv_model {
+  pkv_model_desc d;
+  const void* embed;
+  std::vector<pkv_layer_weights> layers;
+  const void* w_final;
+  const void* w_lm;
+  void* rope;  // device float2 [max_positions][D/2]: (cos, sin)
+};
+
+struct pkv_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+struct StepBuffers {
+  _Float16* h;    // hidden [B][H] (when the caller gives none)
+  float* qkv;     // [B][(Hq + 2 Hkv) D]
+  _Float16* q;    // [B][Hq][D]
+  _Float16* o;    // [B][Hq][D]
+  _Float16* act;  // [B][F]
+  void* attn_ws;
+  size_t total;
+};
+
+StepBuffers carve(const pkv_model* m, int batch, const AttnPlan& plan, void* base) {
+  const pkv_model_desc& d = m->d;
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* r = p ? p + off : nullptr;
+    off += align_up(bytes, 256);
+    return r;
+  };
+  StepBuffers b{};
+  b.h = reinterpret_cast<_Float16*>(take((size_t)batch * d.hidden * 2));
+  b.qkv = reinterpret_cast<float*>(take((size_t)batch * (d.num_q_heads + 2 * d.num_kv_heads) * d.head_dim * 4));
+  b.q = reinterpret_cast<_Float16*>(take((size_t)batch * d.num_q_heads * d.head_dim * 2));
+  b.o = reinterpret_cast<_Float16*>(take((size_t)batch * d.num_q_heads * d.head_dim * 2));
+  b.act = reinterpret_cast<_Float16*>(take((size_t)batch * d.ffn * 2));
+  b.attn_ws = take(plan.ws_bytes);
+  b.total = off;
+  return b;
+}
+
+int cache_elt(const pkv_cache_desc& cd) { return cd.dtype == PKV_KV_FP8_E4M3 ? 1 : 2; }
+
+pkv_status check_step(const pkv_model* m, const pkv_cache* cache, const int32_t* bt, int bt_stride,
+                      const int32_t* lens, int batch, int max_context, void* ws, size_t ws_bytes,
+                      StepBuffers* bufs, AttnPlan* plan) {
+  if (!m || !cache) return fail(PKV_E_ARG, "model / cache is NULL");
+  const pkv_cache_desc& cd = cache->desc;
+  if (cd.dtype != PKV_KV_F16) return fail(PKV_E_UNSUPPORTED, "the decode step supports f16 KV caches");
+  if (cd.num_kv_heads != m->d.num_kv_heads || cd.head_dim != m->d.head_dim)
+    return fail(PKV_E_ARG, "cache heads / head_dim differ from the model's");
+  if (!bt || !lens) return fail(PKV_E_ARG, "block_tables / context_lens is NULL");
+  if (batch < 1) return fail(PKV_E_ARG, "batch must be >= 1");
+  if (max_context < 1 || max_context > m->d.max_positions)
+    return fail(PKV_E_ARG, "max_context must be in [1, max_positions]");
+  if (bt_stride < ceil_div(max_context, kBlock)) return fail(PKV_E_ARG, "bt_stride < ceil(max_context / 16)");
+  *plan = attn_plan(batch, m->d.num_q_heads, m->d.num_kv_heads, m->d.head_dim, cache_elt(cd), max_context);
+  const StepBuffers need = carve(m, batch, *plan, nullptr);
+  if (!ws || ws_bytes < need.total)
+    return fail(PKV_E_ARG, "workspace too small: need " + std::to_string(need.total) + " bytes");
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(PKV_E_ARG, "workspace must be 256-byte aligned");
+  *bufs = carve(m, batch, *plan, ws);
+  return PKV_OK;
+}
+
+hipError_t run_layer(const pkv_model* m, pkv_cache* cache, int layer, _Float16* h, const int32_t* bt,
+                     int bt_stride, const int32_t* lens, int batch, const StepBuffers& sb,
+                     const AttnPlan& plan, hipStream_t s) {
+  const pkv_model_desc& d = m->d;
+  const pkv_layer_weights& w = m->layers[layer];
+  const int qkv_n = (d.num_q_heads + 2 * d.num_kv_heads) * d.head_dim;
+  const int qd = d.num_q_heads * d.head_dim;
+  void* kp = cache->k_pool(layer);
+  void* vp = cache->v_pool(layer);
+  hipError_t e;
+
+  LinArgs a{};
+  a.eps = d.rms_eps;
+  // 1. RMSNorm + QKV (+ bias) -> fp32 qkv
+  a.A = h; a.lda = d.hidden; a.K = d.hidden; a.M = batch;
+  a.W = static_cast<const _Float16*>(w.w_qkv);
+  a.gain = static_cast<const _Float16*>(w.w_in); a.norm = 1;
+  a.bias = static_cast<const _Float16*>(w.b_qkv);
+  a.out = sb.qkv; a.ldo = qkv_n; a.n_out = qkv_n;
+  if ((e = launch_linear(a, EPI_F32, s)) != hipSuccess) return e;
+  // 2. RoPE + KV append
+  if ((e = launch_rope_append(sb.qkv, m->rope, sb.q, kp, vp, bt, bt_stride, lens, batch, d.num_q_heads,
+                              d.num_kv_heads, d.head_dim, s)) != hipSuccess)
+    return e;
+  // 3. paged attention
+  AttnArgs at{};
+  at.k_pool = kp; at.v_pool = vp; at.q = sb.q; at.out = sb.o; at.lse = nullptr;
+  at.bt = bt; at.bt_stride = bt_stride; at.lens = lens; at.batch = batch;
+  at.hq = d.num_q_heads; at.hkv = d.num_kv_heads; at.head_dim = d.head_dim; at.fp8 = false;
+  at.scale = 1.0f / std::sqrt((float)d.head_dim); at.k_scale = at.v_scale = 1.f; at.ws = sb.attn_ws;
+  if ((e = launch_paged_attention(at, plan, s)) != hipSuccess) return e;
+  // 4. O projection + residual add
+  a = LinArgs{};
+  a.eps = d.rms_eps;
+  a.A = sb.o; a.lda = qd; a.K = qd; a.M = batch;
+  a.W = static_cast<const _Float16*>(w.w_o);
+  a.out = h; a.ldo = d.hidden; a.n_out = d.hidden;
+  if ((e = launch_linear(a, EPI_RESID, s)) != hipSuccess) return e;
+  // 5. RMSNorm + gate/up + SiLU*mul -> act
+  a = LinArgs{};
+  a.eps = d.rms_eps;
+  a.A = h; a.lda = d.hidden; a.K = d.hidden; a.M = batch;
+  a.W = static_cast<const _Float16*>(w.w_gate_up);
+  a.gain = static_cast<const _Float16*>(w.w_post); a.norm = 1;
+  a.out = sb.act; a.ldo = d.ffn; a.n_out = d.ffn;
+  if ((e = launch_linear(a, EPI_SILU, s)) != hipSuccess) return e;
+  // 6. down projection + residual add
+  a = LinArgs{};
+  a.eps = d.rms_eps;
+  a.A = sb.act; a.lda = d.ffn; a.K = d.ffn; a.M = batch;
+  a.W = static_cast<const _Float16*>(w.w_down);
+  a.out = h; a.ldo = d.hidden; a.n_out = d.hidden;
+  return launch_linear(a, EPI_RESID, s);
+}
+
+hipError_t run_step(const pkv_model* m, pkv_cache* cache, const int32_t* tokens, const int32_t* bt,
+                    int bt_stride, const int32_t* lens, int batch, void* logits, _Float16* h,
+                    const StepBuffers& sb, const AttnPlan& plan, hipStream_t s) {
+  const pkv_model_desc& d = m->d;
+  hipError_t e = launch_embed(m->embed, tokens, h, batch, d.hidden, s);
+  if (e != hipSuccess) return e;
+  for (int l = 0; l < d.num_layers; ++l) {
+    e = run_layer(m, cache, l, h, bt, bt_stride, lens, batch, sb, plan, s);
+    if (e != hipSuccess) return e;
+  }
+  LinArgs a{};
+  a.eps = d.rms_eps;
+  a.A = h; a.lda = d.hidden; a.K = d.hidden; a.M = batch;
+  a.W = static_cast<const _Float16*>(m->w_lm);
+  a.gain = static_cast<const _Float16*>(m->w_final); a.norm = 1;
+  a.out = logits; a.ldo = d.vocab; a.n_out = d.vocab;
+  return launch_linear(a, EPI_F16, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_model_create(const pkv_model_desc* desc, const void* embed, const pkv_layer_weights* layers,
+                            const void* w_final_norm, const void* w_lm_head, pkv_model** out) {
+  if (!out) return fail(PKV_E_ARG, "out is NULL");
+  *out = nullptr;
+  if (!desc || !embed || !layers || !w_final_norm || !w_lm_head) return fail(PKV_E_ARG, "NULL argument");
+  const pkv_model_desc& d = *desc;
+  if (d.hidden < 8 || d.num_q_heads < 1 || d.num_kv_heads < 1 || d.ffn < 8 || d.vocab < 1 ||
+      d.num_layers < 1 || d.max_positions < 1)
+    return fail(PKV_E_ARG, "model desc: sizes must be positive");
+  if (d.head_dim != 64 && d.head_dim != 128) return fail(PKV_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (d.num_q_heads % d.num_kv_heads) return fail(PKV_E_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  if (d.num_q_heads / d.num_kv_heads > kMaxGroup) return fail(PKV_E_UNSUPPORTED, "more than 16 query heads per KV head");
+  if (d.hidden % 8 || d.ffn % 8) return fail(PKV_E_UNSUPPORTED, "hidden and ffn must be multiples of 8");
+  if (!(d.rms_eps > 0.f) || !(d.rope_theta > 1.f)) return fail(PKV_E_ARG, "rms_eps > 0 and rope_theta > 1 required");
+  for (int l = 0; l < d.num_layers; ++l) {
+    const pkv_layer_weights& w = layers[l];
+    if (!w.w_in || !w.w_qkv || !w.w_o || !w.w_post || !w.w_gate_up || !w.w_down)
+      return fail(PKV_E_ARG, "layer " + std::to_string(l) + ": NULL weight");
+  }
+  pkv_model* m = new (std::nothrow) pkv_model();
+  if (!m) return fail(PKV_E_NOMEM, "host allocation failed");
+  m->d = d;
+  m->embed = embed;
+  m->layers.assign(layers, layers + d.num_layers);
+  m->w_final = w_final_norm;
+  m->w_lm = w_lm_head;
+  // RoPE table: angle pos * theta^(-2i/D) in double, stored as f32 (cos, sin)
+  const int half = d.head_dim / 2;
+  std::vector<float> tab((size_t)d.max_positions * half * 2);
+  for (int i = 0; i < half; ++i) {
+    const double inv = std::pow((double)d.rope_theta, -2.0 * i / d.head_dim);
+    for (int p = 0; p < d.max_positions; ++p) {
+      const double ang = (double)p * inv;
+      tab[((size_t)p * half + i) * 2] = (float)std::cos(ang);
+      tab[((size_t)p * half + i) * 2 + 1] = (float)std::sin(ang);
+    }
+  }
+  hipError_t e = hipMalloc(&m->rope, tab.size() * sizeof(float));
+  if (e != hipSuccess) {
+    delete m;
+    return hip_fail(e, "hipMalloc(rope table)");
+  }
+  e = hipMemcpy(m->rope, tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(m->rope);
+    delete m;
+    return hip_fail(e, "hipMemcpy(rope table)");
+  }
+  *out = m;
+  return PKV_OK;
+}
+
+void pkv_model_destroy(pkv_model* m) {
+  if (!m) return;
+  if (m->rope) (void)hipFree(m->rope);
+  delete m;
+}
+
+pkv_status pkv_step_workspace_bytes(const pkv_model* m, const pkv_cache* cache, int batch, int max_context,
+                                    size_t* bytes) {
+  if (!m || !cache || !bytes) return fail(PKV_E_ARG, "NULL argument");
+  if (batch < 1 || max_context < 1) return fail(PKV_E_ARG, "batch and max_context must be >= 1");
+  const pkv_cache_desc& cd = cache->desc;
+  const AttnPlan plan =
+      attn_plan(batch, m->d.num_q_heads, m->d.num_kv_heads, m->d.head_dim, cache_elt(cd), max_context);
+  *bytes = carve(m, batch, plan, nullptr).total;
+  return PKV_OK;
+}
+
+pkv_status pkv_decode_layer(const pkv_model* m, pkv_cache* cache, int layer, void* hidden,
+                            const int32_t* bt, int bt_stride, const int32_t* lens, int batch,
+                            int max_context, void* ws, size_t ws_bytes, pkv_stream_t stream) {
+  StepBuffers sb{};
+  AttnPlan plan{};
+  pkv_status st = check_step(m, cache, bt, bt_stride, lens, batch, max_context, ws, ws_bytes, &sb, &plan);
+  if (st != PKV_OK) return st;
+  if (!hidden) return fail(PKV_E_ARG, "hidden is NULL");
+  if (layer < 0 || layer >= m->d.num_layers || layer >= cache->desc.num_layers)
+    return fail(PKV_E_ARG, "layer out of range");
+  PKV_HIP(run_layer(m, cache, layer, static_cast<_Float16*>(hidden), bt, bt_stride, lens, batch, sb, plan,
+                    static_cast<hipStream_t>(stream)));
+  return PKV_OK;
+}
+
+static pkv_status enqueue_step(const pkv_model* m, pkv_cache* cache, const int32_t* tokens, const int32_t* bt,
+                               int bt_stride, const int32_t* lens, int batch, int max_context, void* logits,
+                               void* hidden_out, void* ws, size_t ws_bytes, hipStream_t s) {
+  StepBuffers sb{};
+  AttnPlan plan{};
+  pkv_status st = check_step(m, cache, bt, bt_stride, lens, batch, max_context, ws, ws_bytes, &sb, &plan);
+  if (st != PKV_OK) return st;
+  if (!tokens || !logits) return fail(PKV_E_ARG, "token_ids / logits is NULL");
+  if (cache->desc.num_layers < m->d.num_layers) return fail(PKV_E_ARG, "cache has fewer layers than the model");
+  _Float16* h = hidden_out ? static_cast<_Float16*>(hidden_out) : sb.h;
+  PKV_HIP(run_step(m, cache, tokens, bt, bt_stride, lens, batch, logits, h, sb, plan, s));
+  return PKV_OK;
+}
+
+pkv_status pkv_decode_step(const pkv_model* m, pkv_cache* cache, const int32_t* tokens, const int32_t* bt,
+                           int bt_stride, const int32_t* lens, int batch, int max_context, void* logits,
+                           void* hidden_out, void* ws, size_t ws_bytes, pkv_stream_t stream) {
+  return enqueue_step(m, cache, tokens, bt, bt_stride, lens, batch, max_context, logits, hidden_out, ws,
+                      ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+pkv_status pkv_argmax(const void* logits, int batch, int vocab, int32_t* tokens, pkv_stream_t stream) {
+  if (!logits || !tokens) return fail(PKV_E_ARG, "NULL argument");
+  if (batch < 1 || vocab < 1) return fail(PKV_E_ARG, "batch and vocab must be >= 1");
+  PKV_HIP(launch_argmax(logits, batch, vocab, tokens, static_cast<hipStream_t>(stream)));
+  return PKV_OK;
+}
+
+pkv_status pkv_graph_capture(const pkv_model* m, pkv_cache* cache, const int32_t* tokens, const int32_t* bt,
+                             int bt_stride, const int32_t* lens, int batch, int max_context, void* logits,
+                             void* hidden_out, void* ws, size_t ws_bytes, pkv_stream_t capture_stream,
+                             pkv_graph** out) {
+  if (!out) return fail(PKV_E_ARG, "out is NULL");
+  *out = nullptr;
+  if (!capture_stream) return fail(PKV_E_ARG, "capture_stream must not be the null stream");
+  hipStream_t cs = static_cast<hipStream_t>(capture_stream);
+  // validate before capturing so that a bad argument leaves no open capture
+  {
+    StepBuffers sb{};
+    AttnPlan plan{};
+    pkv_status st = check_step(m, cache, bt, bt_stride, lens, batch, max_context, ws, ws_bytes, &sb, &plan);
+    if (st != PKV_OK) return st;
+    if (!tokens || !logits) return fail(PKV_E_ARG, "token_ids / logits is NULL");
+  }
+  pkv_graph* g = new (std::nothrow) pkv_graph();
+  if (!g) return fail(PKV_E_NOMEM, "host allocation failed");
+  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    delete g;
+    return hip_fail(e, "hipStreamBeginCapture");
+  }
+  pkv_status st = enqueue_step(m, cache, tokens, bt, bt_stride, lens, batch, max_context, logits, hidden_out,
+                               ws, ws_bytes, cs);
+  hipGraph_t graph = nullptr;
+  e = hipStreamEndCapture(cs, &graph);
+  if (st != PKV_OK || e != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    delete g;
+    return st != PKV_OK ? st : hip_fail(e, "hipStreamEndCapture");
+  }
+  g->graph = graph;
+  e = hipGraphInstantiate(&g->exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    delete g;
+    return hip_fail(e, "hipGraphInstantiate");
+  }
+  *out = g;
+  return PKV_OK;
+}
+
+pkv_status pkv_graph_replay(pkv_graph* g, pkv_stream_t stream) {
+  if (!g || !g->exec) return fail(PKV_E_STATE, "graph is not instantiated");
+  PKV_HIP(hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream)));
+  return PKV_OK;
+}
+
+void pkv_graph_destroy(pkv_graph* g) {
+  if (!g) return;
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  delete g;
+}
+
+}  // extern "C"

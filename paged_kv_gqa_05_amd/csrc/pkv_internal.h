@@ -1,0 +1,73 @@
+// Internal declarations shared by the host runtime and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/pkv.h"
+
+// A paged KV cache over caller-owned device memory: per layer the K pool
+// [num_blocks][Hkv][16][D] followed by the V pool [num_blocks][Hkv][D][16].
+struct pkv_cache {
+  pkv_cache_desc desc;
+  char* base;
+  size_t pool_bytes;  // bytes of one K (or V) pool of one layer
+  std::vector<float> k_scales, v_scales;
+  int elt() const { return desc.dtype == PKV_KV_FP8_E4M3 ? 1 : 2; }
+  void* k_pool(int l) const { return base + (size_t)l * 2 * pool_bytes; }
+  void* v_pool(int l) const { return base + ((size_t)l * 2 + 1) * pool_bytes; }
+};
+
+namespace pkv {
+
+constexpr int kBlock = 16;   // tokens per KV block
+constexpr int kMaxGroup = 16;  // query heads per KV head handled by one MFMA tile
+
+// Thread-local error message + status helpers (host).
+pkv_status fail(pkv_status st, const std::string& msg);
+pkv_status hip_fail(hipError_t e, const char* what);
+#define PKV_HIP(call)                                   \
+  do {                                                  \
+    hipError_t e_ = (call);                             \
+    if (e_ != hipSuccess) return ::pkv::hip_fail(e_, #call); \
+  } while (0)
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- attention
+struct AttnPlan {
+  int part;         // tokens per partition (multiple of 64)
+  int n_parts_max;  // partitions per (row, kv head) for max_context
+  int grid;         // workgroups of the split kernel
+  size_t ws_bytes;  // workspace bytes
+};
+AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int max_context);
+
+struct AttnArgs {
+  const void* k_pool;
+  const void* v_pool;
+  const void* q;      // f16 [B][Hq][D]
+  void* out;          // f16 [B][Hq][D]
+  float* lse;         // nullable [B][Hq]
+  const int32_t* bt;
+  int bt_stride;
+  const int32_t* lens;
+  int batch, hq, hkv, head_dim;
+  bool fp8;
+  float scale;        // softmax scale
+  float k_scale, v_scale;
+  void* ws;
+};
+hipError_t launch_paged_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
+
+// ------------------------------------------------------------------ KV ops
+hipError_t launch_kv_append(void* k_pool, void* v_pool, const void* k, const void* v,
+                            const int32_t* bt, int bt_stride, const int32_t* lens, int batch,
+                            int hkv, int head_dim, hipStream_t s);
+
+}  // namespace pkv

@@ -1,0 +1,58 @@
+"""Helpers shared by the GPU tests: move seeded inputs to the device and compare
+with the oracle at the tolerance of the parity bar."""
+import numpy as np
+import torch
+
+ATOL, RTOL = 2e-2, 1e-2   # |gpu - ref| <= 2e-2 + 1e-2 |ref| on f16 outputs
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def load_case_into_cache(pkv, case, num_layers=1, layer=0, cache=None):
+    """A KVCache holding the case's pools at `layer` (other layers left uninitialised)."""
+    fp8 = case.k_pool.dtype == np.uint8
+    if cache is None:
+        kw = {}
+        if fp8:
+            kw = dict(dtype=pkv.KV_FP8_E4M3, k_scales=[case.k_scale] * num_layers,
+                      v_scales=[case.v_scale] * num_layers)
+        cache = pkv.KVCache(num_layers, case.num_blocks, case.k_pool.shape[1], case.k_pool.shape[3], **kw)
+    k, v = cache.layer(layer)
+    k.copy_(torch.from_numpy(case.k_pool))
+    v.copy_(torch.from_numpy(case.v_pool))
+    return cache
+
+
+def assert_parity(gpu, ref, what, atol=ATOL, rtol=RTOL):
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
+    err = np.abs(g - r)
+    bad = err > atol + rtol * np.abs(r)
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside atol {atol} + rtol {rtol}; "
+                           f"max abs err {err.max():.3e}")
+    return float(err.max())
+
+
+def weights_to_device(w):
+    """numpy weight dict (pkv_inputs.model_weights) -> same structure of CUDA tensors."""
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return {
+        "embed": t(w["embed"]),
+        "w_final_norm": t(w["w_final_norm"]),
+        "w_lm_head": t(w["w_lm_head"]),
+        "layers": [{k: t(v) for k, v in lw.items()} for lw in w["layers"]],
+    }
+
+
+def oracle_config(shape, n_layers=None):
+    import oracle
+    return oracle.ModelConfig(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn,
+                              shape.vocab, shape.n_layers if n_layers is None else n_layers,
+                              shape.rms_eps, shape.rope_theta)

@@ -1,0 +1,166 @@
+"""GPU parity of the decoder layer, the decode step, greedy argmax and graph
+replay (through the C ABI) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pkv_inputs as inp
+from gpu_util import dev, assert_parity, weights_to_device, oracle_config
+
+pytestmark = pytest.mark.gpu
+
+MID = inp.Shape(hidden=512, n_q_heads=12, n_kv_heads=2, head_dim=128, ffn=1408, vocab=1000, n_layers=2)
+
+
+def _layer_case(shape, batch, seed, lo=1, hi=64):
+    return inp.tiny_layer_case(seed=seed, batch=batch, ctx_lo=lo, ctx_hi=hi, shape=shape)
+
+
+def _run_layer_gpu(pkv, shape, case, max_context=None):
+    w = weights_to_device(case["weights"])
+    model = pkv.Model(shape, w, max_positions=4096)
+    nb = case["num_blocks"]
+    cache = pkv.KVCache(1, nb, shape.n_kv_heads, shape.head_dim)
+    k, v = cache.layer(0)
+    k.copy_(torch.from_numpy(case["k_pool"]))
+    v.copy_(torch.from_numpy(case["v_pool"]))
+    b = case["hidden"].shape[0]
+    mc = max_context or int(case["ctx_lens"].max())
+    bt = case["block_tables"]
+    if bt.shape[1] * 16 < mc:
+        bt = np.concatenate([bt, np.full((b, (mc + 15) // 16 - bt.shape[1]), -1, np.int32)], axis=1)
+    hidden = dev(case["hidden"])
+    ws = torch.empty(pkv.step_workspace_bytes(model, cache, b, mc), dtype=torch.uint8, device="cuda")
+    pkv.decode_layer(model, cache, 0, hidden, dev(bt), dev(case["ctx_lens"]), mc, ws)
+    torch.cuda.synchronize()
+    return hidden.cpu().numpy(), k.cpu().numpy(), v.cpu().numpy()
+
+
+def _oracle_layer(shape, case):
+    kp, vp = case["k_pool"].copy(), case["v_pool"].copy()
+    h = oracle.decode_layer(oracle_config(shape, 1), case["weights"]["layers"][0], case["hidden"], kp, vp,
+                            case["block_tables"], case["ctx_lens"])
+    return h, kp, vp
+
+
+@pytest.mark.parametrize("shape,batch,seed,hi", [
+    (inp.TINY, 4, 1001, 64),       # the one-layer workload (GEMV path)
+    (inp.TINY, 40, 1011, 64),      # MFMA path, ragged last M tile
+    (MID, 3, 1021, 300),           # D = 128, G = 6
+    (MID, 70, 1031, 200),          # MFMA path at D = 128
+])
+def test_decode_layer_parity(lib, shape, batch, seed, hi):
+    case = _layer_case(shape, batch, seed, hi=hi)
+    h, k, v = _run_layer_gpu(lib, shape, case)
+    rh, rk, rv = _oracle_layer(shape, case)
+    assert_parity(h, rh, "hidden after layer")
+    # cache: appended slots within the parity bar, every other byte untouched
+    changed = np.zeros(rk.shape, bool)
+    for b, c in enumerate(case["ctx_lens"]):
+        changed[case["block_tables"][b][(c - 1) // 16], :, (c - 1) % 16, :] = True
+    keep = ~changed
+    assert np.array_equal(k[keep].view(np.uint16), case["k_pool"][keep].view(np.uint16))
+    assert_parity(k[changed], rk[changed], "appended K")
+    vchanged = np.moveaxis(changed, 2, 3)
+    assert np.array_equal(v[~vchanged].view(np.uint16), case["v_pool"][~vchanged].view(np.uint16))
+    assert_parity(v[vchanged], rv[vchanged], "appended V")
+
+
+def test_decode_layer_without_bias_and_unit_gains(lib):
+    case = inp.tiny_layer_case(seed=1041, batch=5, bias=False, norm_jitter=False, shape=MID)
+    h, _, _ = _run_layer_gpu(lib, MID, case)
+    rh, _, _ = _oracle_layer(MID, case)
+    assert_parity(h, rh, "no-bias layer")
+
+
+class StepRig:
+    """A small model decoding several rows through the GPU step and the oracle."""
+
+    def __init__(self, pkv, shape, batch, seed, prompt_len, max_context):
+        self.pkv, self.shape, self.batch = pkv, shape, batch
+        self.w = inp.model_weights(shape, seed, bias=True, norm_jitter=True, std=0.05)
+        self.model = pkv.Model(shape, weights_to_device(self.w), max_positions=max_context)
+        self.mc = max_context
+        stride = (max_context + 15) // 16
+        self.nb = batch * stride + 7
+        self.cache = pkv.KVCache(shape.n_layers, self.nb, shape.n_kv_heads, shape.head_dim)
+        rng = np.random.default_rng(seed + 1)
+        perm = rng.permutation(self.nb).astype(np.int32)
+        self.bt = perm[: batch * stride].reshape(batch, stride)
+        self.prompts = rng.integers(0, shape.vocab, size=(batch, prompt_len)).astype(np.int32)
+        self.lens = np.zeros(batch, np.int32)
+        self.ws = torch.empty(pkv.step_workspace_bytes(self.model, self.cache, batch, max_context),
+                              dtype=torch.uint8, device="cuda")
+        self.logits = torch.empty(batch, shape.vocab, dtype=torch.float16, device="cuda")
+        self.hidden = torch.empty(batch, shape.hidden, dtype=torch.float16, device="cuda")
+        self.kp = [np.full((self.nb, shape.n_kv_heads, 16, shape.head_dim), np.nan, np.float16)
+                   for _ in range(shape.n_layers)]
+        self.vp = [np.full((self.nb, shape.n_kv_heads, shape.head_dim, 16), np.nan, np.float16)
+                   for _ in range(shape.n_layers)]
+        self.cfg = oracle_config(shape)
+        self.d_bt = dev(self.bt)
+
+    def gpu_step(self, tokens):
+        self.lens += 1
+        self.pkv.decode_step(self.model, self.cache, dev(tokens), self.d_bt, dev(self.lens), self.mc,
+                             self.logits, self.ws, hidden_out=self.hidden)
+        torch.cuda.synchronize()
+        return self.logits.cpu().numpy(), self.hidden.cpu().numpy()
+
+    def oracle_step(self, tokens):
+        return oracle.decode_step(self.cfg, self.w, self.kp, self.vp, tokens, self.bt, self.lens)
+
+
+@pytest.mark.parametrize("batch", [3, 33])
+def test_decode_step_parity_and_greedy(lib, batch):
+    rig = StepRig(lib, MID, batch, seed=2001, prompt_len=20, max_context=64)
+    agree = total = 0
+    tok = rig.prompts[:, 0]
+    for t in range(30):
+        lg, hd = rig.gpu_step(tok)
+        rl, rh = rig.oracle_step(tok)
+        assert_parity(lg, rl, f"logits step {t}")
+        assert_parity(hd, rh, f"hidden step {t}")
+        g_tok = lg.argmax(-1)
+        agree += int(np.sum(g_tok == oracle.greedy_argmax(rl)))
+        total += batch
+        # teacher forcing: both sides get the prompt, then the GPU's own tokens
+        tok = rig.prompts[:, t + 1] if t + 1 < rig.prompts.shape[1] else g_tok.astype(np.int32)
+    assert agree / total >= 0.99
+
+
+def test_argmax_kernel(lib):
+    rng = np.random.default_rng(3)
+    lg = rng.standard_normal((6, 151936)).astype(np.float16)
+    lg[1, [5, 77, 150000]] = 30.0          # ties: lowest index wins
+    lg[2, :] = -1.0
+    lg[3, 100] = np.nan
+    out = torch.empty(6, dtype=torch.int32, device="cuda")
+    lib.argmax(dev(lg), out)
+    torch.cuda.synchronize()
+    assert out.cpu().numpy().tolist() == oracle.greedy_argmax(np.nan_to_num(lg, nan=-np.inf)).tolist()
+
+
+def test_graph_replay_matches_eager_and_sees_new_metadata(lib):
+    """Capture one step, then replay it with rewritten tokens / lengths: every
+    replay equals the eager step on the same metadata, bit for bit."""
+    shape = MID
+    batch, mc = 5, 64
+    eager = StepRig(lib, shape, batch, seed=3001, prompt_len=12, max_context=mc)
+    graph_rig = StepRig(lib, shape, batch, seed=3001, prompt_len=12, max_context=mc)
+    toks = dev(graph_rig.prompts[:, 0])
+    lens = dev(graph_rig.lens)
+    g = lib.Graph(graph_rig.model, graph_rig.cache, toks, graph_rig.d_bt, lens, mc, graph_rig.logits,
+                  graph_rig.ws, hidden_out=graph_rig.hidden)
+    for t in range(12):
+        graph_rig.lens += 1
+        # metadata for this step written on the replay stream, then replay there
+        toks.copy_(torch.from_numpy(graph_rig.prompts[:, t]))
+        lens.copy_(torch.from_numpy(graph_rig.lens))
+        g.replay()
+        torch.cuda.synchronize()
+        gl = graph_rig.logits.cpu().numpy()
+        el, _ = eager.gpu_step(eager.prompts[:, t])
+        assert np.array_equal(gl.view(np.uint16), el.view(np.uint16)), t
+    g.close()
