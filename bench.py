@@ -1,0 +1,319 @@
+"""Decode throughput of the paged-KV GQA decode step on one MI355X.
+
+Workload (headline): the 28-layer Qwen2.5-1.5B-shaped decoder (hidden 1536,
+12/2 heads, head_dim 128, FFN 8960, vocab 151936) with seeded random-init f16
+weights N(0, 0.02), 256 sequences with 128-token random prompts prefilled by
+teacher-forced decode steps, then greedy decode.  One timed step is the whole
+hot path for one batch: the host block allocator grows block tables, the
+per-step metadata (context lengths, block tables) is uploaded from pinned
+staging on the stream, the captured step graph is replayed on that stream and
+the greedy argmax writes the next tokens into the graph's token buffer.
+
+Also reported (same JSON line): decode tok/s at batch 1 / 64 / 128, paged
+attention alone at the 1.5B layer shape (batch 64, contexts U[128, 2048],
+28 rotated pools so that every call reads HBM) and at the fp8 long-context
+7B layer shape, the roofline of the dominant kernel, and the CPU oracle timed
+on the host cores on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 32] [--warmup 5]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0
+PAGES_TOKS_N256 = 40714.0  # rvLLM post, H100 1.5B table, N = 256 (other hardware)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- decode run
+
+class DecodeRun:
+    """One batch size: cache, allocator, staging ring, captured graph."""
+
+    def __init__(self, pkv, torch, model, shape, batch, prompt_len, total_steps, seed):
+        self.pkv, self.torch, self.model, self.shape, self.batch = pkv, torch, model, shape, batch
+        self.prompt_len = prompt_len
+        self.max_context = total_steps + 1  # total_steps counts the prompt steps too
+        self.stride = math.ceil(self.max_context / 16)
+        need = batch * self.stride
+        self.num_blocks = int(math.ceil(1.25 * need))
+        self.cache = pkv.KVCache(shape.n_layers, self.num_blocks, shape.n_kv_heads, shape.head_dim)
+        self.alloc = pkv.BlockAllocator(self.num_blocks, seed=seed)
+        rng = np.random.default_rng(seed)
+        self.prompts = rng.integers(0, shape.vocab, size=(batch, prompt_len)).astype(np.int32)
+        self.lens = np.zeros(batch, np.int32)
+        self.bt = np.full((batch, self.stride), -1, np.int32)
+        dev = "cuda"
+        self.tok_d = torch.zeros(batch, dtype=torch.int32, device=dev)
+        self.lens_d = torch.zeros(batch, dtype=torch.int32, device=dev)
+        self.bt_d = torch.full((batch, self.stride), -1, dtype=torch.int32, device=dev)
+        self.logits = torch.empty(batch, shape.vocab, dtype=torch.float16, device=dev)
+        ws_bytes = pkv.step_workspace_bytes(model, self.cache, batch, self.max_context)
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        # one pinned staging slot per step: an async copy never reads a slot
+        # that a later step has already rewritten
+        n_slots = total_steps + 2
+        self.stage_lens = torch.empty((n_slots, batch), dtype=torch.int32).pin_memory()
+        self.stage_bt = torch.empty((n_slots, batch, self.stride), dtype=torch.int32).pin_memory()
+        self.stage_tok = torch.empty((n_slots, batch), dtype=torch.int32).pin_memory()
+        self.slot = 0
+        self.graph = pkv.Graph(model, self.cache, self.tok_d, self.bt_d, self.lens_d, self.max_context,
+                               self.logits, self.ws)
+
+    def step(self, tokens=None):
+        """Grow tables, upload metadata, replay, argmax.  tokens: host ids to
+        teacher-force (prompt ingestion); None = greedy from the last argmax."""
+        for b in np.nonzero(self.lens % 16 == 0)[0]:
+            self.alloc.grow(self.bt[b], int(self.lens[b]), int(self.lens[b]) + 1)
+        self.lens += 1
+        s = self.slot
+        self.slot += 1
+        self.stage_lens[s].numpy()[:] = self.lens
+        self.stage_bt[s].numpy()[:] = self.bt
+        self.lens_d.copy_(self.stage_lens[s], non_blocking=True)
+        self.bt_d.copy_(self.stage_bt[s], non_blocking=True)
+        if tokens is not None:
+            self.stage_tok[s].numpy()[:] = tokens
+            self.tok_d.copy_(self.stage_tok[s], non_blocking=True)
+        self.graph.replay()
+        self.pkv.argmax(self.logits, self.tok_d)
+
+    def prefill(self):
+        for t in range(self.prompt_len):
+            self.step(self.prompts[:, t])
+
+    def close(self):
+        self.graph.close()
+        self.cache.close()
+
+
+def time_decode(pkv, torch, model, shape, batch, prompt_len, warmup, steps, seed):
+    run = DecodeRun(pkv, torch, model, shape, batch, prompt_len, prompt_len + warmup + steps, seed)
+    run.prefill()
+    for _ in range(warmup):
+        run.step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        run.step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1)
+    ctx_mean = float(run.lens.mean()) - steps / 2.0
+    run.close()
+    return {"batch": batch, "ms_per_step": ms / steps, "tok_s": batch * steps / (ms / 1e3),
+            "wall_s": wall, "mean_context": ctx_mean}
+
+
+def step_bytes(shape, batch, mean_ctx):
+    """Algorithmic HBM bytes of one decode step: weights once, the KV read for
+    every row's context, the new KV written, embedding rows read, logits written."""
+    h, d, f, v = shape.hidden, shape.head_dim, shape.ffn, shape.vocab
+    qkv = (shape.n_q_heads + 2 * shape.n_kv_heads) * d
+    per_layer_w = 2 * (h + qkv * h + qkv + h * shape.n_q_heads * d + h + 2 * f * h + h * f)
+    weights = shape.n_layers * per_layer_w + 2 * (h + v * h)
+    kv_tok = shape.n_layers * shape.n_kv_heads * d * 2 * 2
+    return weights + batch * mean_ctx * kv_tok + batch * kv_tok + batch * h * 2 + batch * v * 2
+
+
+# ---------------------------------------------------------- attention alone
+
+def time_attention(pkv, torch, w, n_pools, rounds, seed):
+    """Per-call time of paged_attn_decode over n_pools rotated layer pools."""
+    import pkv_inputs as inp
+    rng = np.random.default_rng(w.seed)
+    lens = inp.context_lengths(rng, w.batch, w.ctx_lo, w.ctx_hi, w.dist)
+    mc = int(lens.max())
+    bt, nb = inp.deal_block_tables(rng, lens, mc)
+    fp8 = w.kv_dtype == "fp8"
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    if fp8:
+        cache = pkv.KVCache(n_pools, nb, w.n_kv_heads, w.head_dim, dtype=pkv.KV_FP8_E4M3,
+                            k_scales=[1.0 / 64] * n_pools, v_scales=[1.0 / 64] * n_pools)
+    else:
+        cache = pkv.KVCache(n_pools, nb, w.n_kv_heads, w.head_dim)
+    for layer in range(n_pools):
+        k, v = cache.layer(layer)
+        if fp8:  # finite E4M3 codes: magnitude codes 0..0x7E, either sign
+            for t in (k, v):
+                t.copy_(torch.randint(0, 0x7F, t.shape, device="cuda", generator=g, dtype=torch.int32)
+                        .to(torch.uint8) | (torch.randint(0, 2, t.shape, device="cuda", generator=g,
+                                                          dtype=torch.int32).to(torch.uint8) << 7))
+        else:
+            k.normal_(generator=g)
+            v.normal_(generator=g)
+    q = torch.empty(w.batch, w.n_q_heads, w.head_dim, dtype=torch.float16, device="cuda").normal_(generator=g)
+    out = torch.empty_like(q)
+    bt_d = torch.from_numpy(bt).cuda()
+    lens_d = torch.from_numpy(lens).cuda()
+    ws = torch.empty(pkv.attn_workspace_bytes(cache, w.batch, w.n_q_heads, mc), dtype=torch.uint8,
+                     device="cuda")
+    scale = 1.0 / math.sqrt(w.head_dim)
+
+    def call(layer):
+        pkv.paged_attn_decode(cache, layer, q, out, bt_d, lens_d, mc, scale, ws)
+
+    for layer in range(n_pools):
+        call(layer)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(rounds):
+        for layer in range(n_pools):
+            call(layer)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (rounds * n_pools)
+    elt = 1 if fp8 else 2
+    kv_bytes = int(lens.sum()) * w.n_kv_heads * w.head_dim * 2 * elt
+    other = 2 * q.numel() * 2 + bt.nbytes + lens.nbytes
+    nbytes = kv_bytes + other
+    cache.close()
+    return {"batch": w.batch, "heads": f"{w.n_q_heads}/{w.n_kv_heads}", "head_dim": w.head_dim,
+            "kv_dtype": w.kv_dtype, "sum_context": int(lens.sum()), "bytes_per_call": nbytes,
+            "us_per_call": ms * 1e3, "GBs": nbytes / (ms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "rotated_pools": n_pools}
+
+
+# ---------------------------------------------------------- CPU oracle leg
+
+def cpu_baseline(torch, weights, shape, batch_sample, ctx):
+    """The oracle (as it stands, default precision) running one decode step of
+    the same model for a few rows with a pre-filled context of `ctx` tokens."""
+    import oracle
+    import pkv_inputs as inp
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    host = {
+        "embed": weights["embed"].cpu().numpy(), "w_final_norm": weights["w_final_norm"].cpu().numpy(),
+        "w_lm_head": weights["w_lm_head"].cpu().numpy(),
+        "layers": [{k: (None if t is None else t.cpu().numpy()) for k, t in lw.items()}
+                   for lw in weights["layers"]],
+    }
+    cfg = oracle.ModelConfig(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn,
+                             shape.vocab, shape.n_layers, shape.rms_eps, shape.rope_theta)
+    rng = np.random.default_rng(7)
+    lens = np.full(batch_sample, ctx, np.int32)
+    bt, nb = inp.deal_block_tables(rng, lens, ctx)
+    valid = inp.valid_slot_masks(bt, lens - 1, nb)
+    kps, vps = [], []
+    for _ in range(shape.n_layers):
+        k, v = inp.random_pools(rng, nb, shape.n_kv_heads, shape.head_dim, valid)
+        kps.append(k)
+        vps.append(v)
+    toks = rng.integers(0, shape.vocab, size=batch_sample).astype(np.int32)
+    t0 = time.perf_counter()
+    oracle.decode_step(cfg, host, kps, vps, toks, bt, lens)
+    dt = time.perf_counter() - t0
+    return {"value": batch_sample / dt, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one oracle decode step (fp64) of the 28-layer 1.5B-shape model for "
+                      f"{batch_sample} rows at context {ctx}: {dt:.1f} s"}
+
+
+# ---------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--batches", default="1,64,128,256")
+    ap.add_argument("--prompt", type=int, default=128)
+    ap.add_argument("--attn-rounds", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-attn", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_gqa_05_amd as pkv
+    import pkv_inputs as inp
+
+    torch.cuda.set_device(0)
+    shape = inp.QWEN15
+    batches = [int(x) for x in args.batches.split(",")]
+    head = max(batches)
+    log(f"generating {shape} weights on the device")
+    weights = inp.model_weights_torch(shape, seed=1003)
+    model = pkv.Model(shape, weights, max_positions=max(4096, args.prompt + args.warmup + args.steps + 1))
+
+    per_batch = {}
+    for n in batches:
+        r = time_decode(pkv, torch, model, shape, n, args.prompt, args.warmup, args.steps, seed=2003 + n)
+        nbytes = step_bytes(shape, n, r["mean_context"])
+        r["bytes_per_step"] = nbytes
+        r["roofline_ms"] = nbytes / (HBM_PEAK_GBS * 1e9) * 1e3
+        r["frac_of_roofline"] = r["roofline_ms"] / r["ms_per_step"]
+        per_batch[n] = r
+        log(f"batch {n}: {r['ms_per_step']:.3f} ms/step, {r['tok_s']:.0f} tok/s, "
+            f"{100 * r['frac_of_roofline']:.1f}% of the HBM roofline")
+
+    attn = {}
+    if not args.no_attn:
+        attn["attn15"] = time_attention(pkv, torch, inp.ATTN15, 28, args.attn_rounds, seed=11)
+        log(f"attn15: {attn['attn15']['us_per_call']:.2f} us/call, {attn['attn15']['GBs']:.0f} GB/s")
+        attn["fp8long"] = time_attention(pkv, torch, inp.FP8LONG, 8, args.attn_rounds, seed=12)
+        log(f"fp8long: {attn['fp8long']['us_per_call']:.2f} us/call, {attn['fp8long']['GBs']:.0f} GB/s")
+
+    h = per_batch[head]
+    a = attn.get("attn15")
+    roofline = None
+    if a:
+        roofline = {"bound": "hbm", "kernel": "paged attention (split + merge), 1.5B layer shape",
+                    "achieved": round(a["GBs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(a["GBs"] / HBM_PEAK_GBS, 4), "traffic": None}
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(torch, weights, shape, 4, args.prompt)
+        log(f"cpu oracle: {cpu['value']:.3f} tok/s ({cpu['sample']})")
+
+    line = {
+        "metric": "decode tok/s at N=1/64/128/256 + paged-attn HBM GB/s (% of 8 TB/s peak)",
+        "value": round(h["tok_s"], 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(h["tok_s"] / PAGES_TOKS_N256, 3) if head == 256 else None,
+        "dtype": "f16",
+        "data": "synthetic: seeded random-init weights N(0,0.02), random 128-token prompts",
+        "config": {"workload": f"Qwen2.5-1.5B-shape 28-layer f16 decode, batch {head}, "
+                               f"{args.prompt}-token prompts, greedy, graph replay",
+                   "global_batch": head, "seq_len": args.prompt + args.warmup + args.steps},
+        "decode": {str(n): {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+                   for n, r in per_batch.items()},
+        "attention": attn,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -234,3 +234,33 @@ def tiny_layer_case(seed=1001, batch=4, ctx_lo=1, ctx_hi=64, norm_jitter=True, b
 
 def prompts(rng, batch, length, vocab):
     return rng.integers(0, vocab, size=(batch, length)).astype(np.int32)
+
+
+def model_weights_torch(shape: Shape, seed, device="cuda", bias=True, std=0.02, n_layers=None):
+    """The same recipe as model_weights (N(0, std) matrices and bias, unit
+    RMSNorm gains) drawn with torch's Philox generator on the device, for
+    full-size models where host generation would dominate the run time."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    n_layers = shape.n_layers if n_layers is None else n_layers
+    h, d = shape.hidden, shape.head_dim
+    qkv = (shape.n_q_heads + 2 * shape.n_kv_heads) * d
+
+    def mat(*s):
+        t = torch.empty(s, dtype=torch.float16, device=device)
+        t.normal_(0.0, std, generator=g)
+        return t
+
+    def gain(n):
+        return torch.ones(n, dtype=torch.float16, device=device)
+
+    layers = []
+    for _ in range(n_layers):
+        layers.append({
+            "w_in": gain(h), "w_qkv": mat(qkv, h), "b_qkv": mat(qkv) if bias else None,
+            "w_o": mat(h, shape.n_q_heads * d), "w_post": gain(h),
+            "w_gate_up": mat(2 * shape.ffn, h), "w_down": mat(h, shape.ffn),
+        })
+    return {"embed": mat(shape.vocab, h), "layers": layers, "w_final_norm": gain(h),
+            "w_lm_head": mat(shape.vocab, h)}
