@@ -242,6 +242,9 @@ def main():
     ap.add_argument("--attn-rounds", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-attn", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size "
+                         "kernel for scaling rocprof FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -253,12 +256,24 @@ def main():
     import pkv_inputs as inp
 
     torch.cuda.set_device(0)
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n} bytes read, {n} bytes written")
+        del src, dst
     shape = inp.QWEN15
-    batches = [int(x) for x in args.batches.split(",")]
-    head = max(batches)
-    log(f"generating {shape} weights on the device")
-    weights = inp.model_weights_torch(shape, seed=1003)
-    model = pkv.Model(shape, weights, max_positions=max(4096, args.prompt + args.warmup + args.steps + 1))
+    batches = [int(x) for x in args.batches.split(",") if x.strip()]
+    head = max(batches) if batches else None
+    weights = model = None
+    if batches:
+        log(f"generating {shape} weights on the device")
+        weights = inp.model_weights_torch(shape, seed=1003)
+        model = pkv.Model(shape, weights,
+                          max_positions=max(4096, args.prompt + args.warmup + args.steps + 1))
 
     per_batch = {}
     for n in batches:
@@ -278,6 +293,9 @@ def main():
         attn["fp8long"] = time_attention(pkv, torch, inp.FP8LONG, 8, args.attn_rounds, seed=12)
         log(f"fp8long: {attn['fp8long']['us_per_call']:.2f} us/call, {attn['fp8long']['GBs']:.0f} GB/s")
 
+    if head is None:  # profiling runs: attention only
+        print(json.dumps({"attention": attn}))
+        return
     h = per_batch[head]
     a = attn.get("attn15")
     roofline = None
