@@ -1,0 +1,458 @@
+// Batched projections (batch >= 32) on MFMA: y = W a with W [rows][K] f16
+// row-major, fp32 accumulation, the RMSNorm fused in front and the consumer op
+// fused behind (rvLLM post on discuss.pytorch.kr, section "퓨즈드 CUDA 커널":
+// Add+RMSNorm+QKV, Add+RMSNorm+GateUp and SiLU*Mul+Down are single kernels;
+// zingnex.cn article, section 直接GPU调用: batched projections are f16 GEMMs).
+//
+// Structure (one workgroup of 4 waves per MT x NT output tile and K range):
+//  * Stages of 64 K elements.  A stage holds MT activation rows and NT weight
+//    rows of 128 bytes each, copied from global memory straight into LDS with
+//    the gfx950 direct-to-LDS load (global_load_lds_dwordx4): no VGPRs are
+//    spent on staging, so NS stages are kept in flight.  Each load writes 1 KB
+//    = 8 rows; lane i fetches the 16-byte chunk (i%8) ^ (i/8) of row i/8, so the
+//    chunk c of row r lands in slot c ^ (r%8) (XOR swizzle: the fragment reads
+//    below are free of bank conflicts) and every load covers 8 whole 128-byte
+//    lines of global memory.
+//  * 2 x 2 waves, each (MT/2) x (NT/2) of the tile with
+//    v_mfma_f32_16x16x32_f16; both operands are read from LDS with one
+//    ds_read_b128 per lane and fragment.
+//  * RMSNorm by linearity: W (g . h * r) = r * (W (g . h)).  The gain g is
+//    staged with the stage (one 128-byte row per wave) and multiplied into the
+//    activation fragments; sum(h^2) accumulates from the same fragments and the
+//    row scale r = 1/sqrt(mean(h^2) + eps) is applied in the epilogue.
+//  * Split-K: when the weight matrix alone cannot fill the chip, the K range is
+//    cut into S parts.  Each part writes its fp32 tile (and partial sum(h^2))
+//    to the workspace; the last part to finish a tile (per-tile arrival
+//    counter, reset by that same workgroup) adds the S parts in a fixed order
+//    and runs the epilogue, so results do not depend on arrival order.
+//  * Tile order is XCD-aware: the hardware deals workgroups round-robin over
+//    the 8 XCDs; each XCD takes a contiguous range of tiles, M tiles fastest,
+//    so the M tiles that share a weight tile share one L2.
+#include "linear.h"
+
+namespace pkv {
+namespace {
+
+typedef _Float16 h16;
+typedef h16 h16x8 __attribute__((ext_vector_type(8)));
+typedef h16 h16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr int BK = 64;  // K elements per stage (one 128-byte chunk of a row)
+
+__device__ __forceinline__ float dot8(h16x8 a, h16x8 b, float c) {
+  c = __builtin_amdgcn_fdot2(h16x2{a[0], a[1]}, h16x2{b[0], b[1]}, c, false);
+  c = __builtin_amdgcn_fdot2(h16x2{a[2], a[3]}, h16x2{b[2], b[3]}, c, false);
+  c = __builtin_amdgcn_fdot2(h16x2{a[4], a[5]}, h16x2{b[4], b[5]}, c, false);
+  c = __builtin_amdgcn_fdot2(h16x2{a[6], a[7]}, h16x2{b[6], b[7]}, c, false);
+  return c;
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// One direct-to-LDS load: every lane copies the 16 bytes at g to LDS address
+// m0 + 16 * lane, where m0 = lds (wave-uniform).  Written as inline asm so that
+// the compiler does not treat later LDS reads as possibly aliasing an
+// in-flight copy (it would drain every copy before each read, which removes
+// the pipelining); completion is tracked explicitly with wait_vmcnt.
+__device__ __forceinline__ void load_to_lds(const void* g, const _Float16* lds) {
+  const unsigned off = (unsigned)(size_t)(lds_char*)(lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(off) : "memory");
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding global load).
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+// Split-K partials cross XCDs, whose L2 caches are not coherent with each
+// other.  They are written and read with agent-scope relaxed atomics (sc1:
+// coherent at device scope without flushing or invalidating the whole L2,
+// which a device-scope fence would do once per workgroup).
+__device__ __forceinline__ void st_agent(float* p, f32x4 v) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  __hip_atomic_store(q, __builtin_bit_cast(uint64_t, float2{v[0], v[1]}), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, __builtin_bit_cast(uint64_t, float2{v[2], v[3]}), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4 ld_agent(const float* p) {
+  uint64_t* q = const_cast<uint64_t*>(reinterpret_cast<const uint64_t*>(p));
+  const float2 a = __builtin_bit_cast(float2, __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const float2 b = __builtin_bit_cast(float2, __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return f32x4{a.x, a.y, b.x, b.y};
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int MT, int NT, int NS, int EPI, bool NORM>
+struct Cfg {
+  static constexpr bool PAIR = (EPI == EPI_SILU);
+  static constexpr int WTM = MT / 2, WTN = NT / 2;   // wave tile
+  static constexpr int FM = WTM / 16, FN = WTN / 16;  // 16 x 16 fragments per wave
+  static constexpr int ROWS = MT + NT;
+  static constexpr int LPS = ROWS / 32;               // row loads per wave per stage
+  static constexpr int LPW = LPS + (NORM ? 1 : 0);    // + the gain row
+  static constexpr int GAIN_OFF = ROWS * BK;          // f16 offset of the 4 gain rows
+  static constexpr int STAGE = ROWS * BK + (NORM ? 4 * BK : 0);  // f16 per stage
+  static_assert(ROWS % 32 == 0 && FM >= 1 && FN >= 1, "tile shape");
+  static_assert(!PAIR || (FN % 2 == 0), "paired tiles need an even fragment count");
+  static_assert(NS >= 2 && (NS - 2) * LPW < 64, "stages");
+};
+
+template <int NPEND, int LPW>
+__device__ __forceinline__ void wait_stage(int pending) {
+  // pending in [0, NPEND]; s_waitcnt takes an immediate
+  if constexpr (NPEND >= 2) {
+    if (pending >= 2) { wait_vmcnt<2 * LPW>(); return; }
+  }
+  if constexpr (NPEND >= 1) {
+    if (pending >= 1) { wait_vmcnt<LPW>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+template <int MT, int NT, int NS, int EPI, bool NORM>
+__global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
+  using C = Cfg<MT, NT, NS, EPI, NORM>;
+  constexpr bool PAIR = C::PAIR;
+  constexpr int FM = C::FM, FN = C::FN;
+  __shared__ __attribute__((aligned(1024))) h16 smem[NS * C::STAGE];
+  __shared__ float s_ss[MT];
+  __shared__ int s_last;
+
+  // ---- tile of this workgroup (XCD-aware order, M tiles fastest)
+  const int L = blockIdx.x;
+  const int T = (L & 7) * p.per_xcd + (L >> 3);
+  if (T >= p.n_mt * p.n_nt * p.splits) return;
+  const int mt = T % p.n_mt;
+  const int rest = T / p.n_mt;
+  const int sp = rest % p.splits;
+  const int nt = rest / p.splits;
+  const int m0 = mt * MT;
+  const int n_kc = (p.K + BK - 1) / BK;
+  const int kc0 = sp * p.kc_per_split;
+  const int n_iter = min(n_kc, kc0 + p.kc_per_split) - kc0;  // >= 1 by construction
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- per-lane sources of this wave's direct-to-LDS row loads
+  // load j of wave w covers stage rows 8 * (4 j + w) .. + 8
+  const int lrow = lane >> 3;                  // row within the 8-row group
+  const int lchunk = (lane & 7) ^ lrow;        // 16-byte chunk this lane fetches
+  const h16* src[C::LPS];
+#pragma unroll
+  for (int j = 0; j < C::LPS; ++j) {
+    const int r = 8 * (4 * j + wave) + lrow;   // stage row
+    if (r < MT) {
+      src[j] = p.A + (size_t)min(m0 + r, p.M - 1) * p.lda;
+    } else {
+      const int t = r - MT;
+      int wr;
+      if (PAIR) {
+        const int jj = min(nt * (NT / 2) + (t % (NT / 2)), p.n_out - 1);
+        wr = t < NT / 2 ? jj : jj + p.n_out;
+      } else {
+        wr = min(nt * NT + t, p.n_out - 1);
+      }
+      src[j] = p.W + (size_t)wr * p.K;
+    }
+  }
+  const int kmax = p.K - 8;  // last valid 8-element chunk start
+
+  auto issue = [&](int it) {
+    const int buf = it % NS;
+    const int kbase = (kc0 + it) * BK;
+    const int k = min(kbase + 8 * lchunk, kmax);
+    h16* sb = smem + buf * C::STAGE;
+#pragma unroll
+    for (int j = 0; j < C::LPS; ++j) load_to_lds(src[j] + k, sb + (4 * j + wave) * 8 * BK);
+    if constexpr (NORM) {
+      if (lane < 8) {  // this wave's copy of the 64 gain values of the stage
+        const int kg = min(kbase + 8 * lane, kmax);
+        load_to_lds(p.gain + kg, sb + C::GAIN_OFF + wave * BK);
+      }
+    }
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) ss[i] = 0.f;
+
+  // fragment rows (stage row index) of this lane
+  const int fr = lane & 15, fg = lane >> 4;
+  int arow[FM], wrow_t[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) arow[i] = wm * C::WTM + i * 16 + fr;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    int t;
+    if (PAIR) {
+      t = (j < FN / 2) ? wn * (NT / 4) + j * 16 : NT / 2 + wn * (NT / 4) + (j - FN / 2) * 16;
+    } else {
+      t = wn * C::WTN + j * 16;
+    }
+    wrow_t[j] = MT + t + fr;
+  }
+
+  // ---- main loop: NS - 1 stages in flight
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < n_iter) issue(s);
+
+  for (int it = 0; it < n_iter; ++it) {
+    const int pending = min(n_iter - 1, it + NS - 2) - it;
+    wait_stage<NS - 2, C::LPW>(pending);
+    barrier_only();
+    if (it + NS - 1 < n_iter) issue(it + NS - 1);
+
+    const h16* sb = smem + (it % NS) * C::STAGE;
+    const int kbase = (kc0 + it) * BK;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int c = 4 * s + fg;  // logical 16-byte chunk of this lane
+      const bool kin = kbase + 8 * c < p.K;
+      h16x8 af[FM], wf[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = arow[i];
+        af[i] = *reinterpret_cast<const h16x8*>(sb + r * BK + ((c ^ (r & 7)) * 8));
+        if (!kin) af[i] = h16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wrow_t[j];
+        wf[j] = *reinterpret_cast<const h16x8*>(sb + r * BK + ((c ^ (r & 7)) * 8));
+      }
+      if constexpr (NORM) {
+        const h16x8 g = *reinterpret_cast<const h16x8*>(sb + C::GAIN_OFF + wave * BK + 8 * c);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          ss[i] = dot8(af[i], af[i], ss[i]);
+          af[i] = af[i] * g;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], wf[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // ---- sum(h^2) per activation row: reduce the four k-groups of a row
+  if constexpr (NORM) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      ss[i] += __shfl_xor(ss[i], 16, 64);
+      ss[i] += __shfl_xor(ss[i], 32, 64);
+    }
+  }
+
+  const int tile = mt + p.n_mt * nt;
+  if (p.splits > 1) {
+    // partial tile in the accumulator layout: lane-contiguous float4s
+    constexpr int TILE_F = MT * NT;
+    float* part = p.part + ((size_t)tile * p.splits + sp) * TILE_F + wave * (FM * FN * 256);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) st_agent(part + ((i * FN + j) * 64 + lane) * 4, acc[i][j]);
+    if constexpr (NORM) {
+      if (wn == 0 && fg == 0) {
+        float* ssp = p.part_ss + ((size_t)tile * p.splits + sp) * MT;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          __hip_atomic_store(ssp + arow[i], ss[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    wait_vmcnt<0>();  // this thread's partials have reached the coherent level
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(p.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               p.splits - 1;
+    __syncthreads();
+    if (!s_last) return;
+    // the last part: add all parts in split order
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // G parts in flight at a time, added in split order
+    constexpr int G = (FM * FN >= 8) ? 1 : (FM * FN >= 4 ? 2 : 4);
+    for (int q0 = 0; q0 < p.splits; q0 += G) {
+      f32x4 t[G][FM][FN];
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        const int q = min(q0 + u, p.splits - 1);
+        const float* pq = p.part + ((size_t)tile * p.splits + q) * TILE_F + wave * (FM * FN * 256);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) t[u][i][j] = ld_agent(pq + ((i * FN + j) * 64 + lane) * 4);
+      }
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        if (q0 + u < p.splits) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] += t[u][i][j];
+        }
+      }
+    }
+    if constexpr (NORM) {
+      if (wn == 0 && fg == 0) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          float t = 0.f;
+          for (int q = 0; q < p.splits; ++q)
+            t += __hip_atomic_load(p.part_ss + ((size_t)tile * p.splits + q) * MT + arow[i], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+          ss[i] = t;
+        }
+      }
+    }
+    if (tid == 0) __hip_atomic_store(p.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  if constexpr (NORM) {
+    if (wn == 0 && fg == 0) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) s_ss[arow[i]] = rsqrtf(ss[i] / (float)p.K + p.eps);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds column fr of each fragment, rows 4 fg + v
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int ml = wm * C::WTM + i * 16 + 4 * fg + v;
+      const int m = m0 + ml;
+      if (m >= p.M) continue;
+      const float r = NORM ? s_ss[ml] : 1.0f;
+      if constexpr (PAIR) {
+#pragma unroll
+        for (int j = 0; j < FN / 2; ++j) {
+          const int col = nt * (NT / 2) + wn * (NT / 4) + j * 16 + fr;
+          if (col < p.n_out) {
+            const float g = acc[i][j][v] * r, u = acc[i][j + FN / 2][v] * r;
+            static_cast<h16*>(p.out)[(size_t)m * p.ldo + col] = (h16)(silu(g) * u);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = nt * NT + wn * C::WTN + j * 16 + fr;
+          if (col >= p.n_out) continue;
+          float y = acc[i][j][v] * r;
+          if constexpr (EPI == EPI_F32) {
+            if (p.bias) y += (float)p.bias[col];
+            static_cast<float*>(p.out)[(size_t)m * p.ldo + col] = y;
+          } else if constexpr (EPI == EPI_F16) {
+            if (p.bias) y += (float)p.bias[col];
+            static_cast<h16*>(p.out)[(size_t)m * p.ldo + col] = (h16)y;
+          } else {  // EPI_RESID
+            h16* o = static_cast<h16*>(p.out) + (size_t)m * p.ldo + col;
+            *o = (h16)((float)*o + y);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int MT, int NT, int NS, int EPI>
+hipError_t launch_cfg(const GemmParams& gp, bool norm, hipStream_t s) {
+  const int total = gp.n_mt * gp.n_nt * gp.splits;
+  const int grid = gp.per_xcd * 8;
+  (void)total;
+  if (norm)
+    hipLaunchKernelGGL((gemm_kernel<MT, NT, NS, EPI, true>), dim3(grid), dim3(256), 0, s, gp);
+  else
+    hipLaunchKernelGGL((gemm_kernel<MT, NT, NS, EPI, false>), dim3(grid), dim3(256), 0, s, gp);
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_epi(const GemmPlan& pl, const GemmParams& gp, bool norm, hipStream_t s) {
+  switch (pl.cfg) {
+    case GEMM_32x64: return launch_cfg<32, 64, 4, EPI>(gp, norm, s);
+    case GEMM_64x128: return launch_cfg<64, 128, 3, EPI>(gp, norm, s);
+    case GEMM_128x128: return launch_cfg<128, 128, 2, EPI>(gp, norm, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+// Tile shape and K split for an M x rows x K projection (host only).
+// Tile table (measured at the 1.5B decode shapes, batch 64 and 256): small
+// 32 x 64 tiles with 4 stages win until they exceed ~1024 tiles (the grid then
+// re-reads the activations from L2 too often); larger weight matrices use
+// 64 x 128 (3 stages) and then 128 x 128 (2 stages: two workgroups per CU).
+GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
+  const bool pair = (epi == EPI_SILU);
+  static const int kCfg[3][3] = {{GEMM_32x64, 32, 64}, {GEMM_64x128, 64, 128}, {GEMM_128x128, 128, 128}};
+  GemmPlan pl{};
+  for (int c = 0; c < 3; ++c) {
+    pl.cfg = kCfg[c][0];
+    pl.mt = kCfg[c][1];
+    pl.nt = kCfg[c][2];
+    pl.n_mt = ceil_div(M, pl.mt);
+    pl.n_nt = ceil_div(n_out, pair ? pl.nt / 2 : pl.nt);
+    if (pl.n_mt * pl.n_nt < 1024) break;
+  }
+  const int n_kc = ceil_div(K, 64);
+  const int tiles = pl.n_mt * pl.n_nt;
+  // split K while the grid holds fewer than ~one workgroup per CU and every
+  // part keeps at least 4 stages; a split tile needs an arrival counter
+  int splits = 1;
+  while (tiles * splits < 240 && n_kc / (splits + 1) >= 4 && splits < 16 && tiles <= kGemmMaxCounters) ++splits;
+  pl.kc_per_split = ceil_div(n_kc, splits);
+  pl.splits = ceil_div(n_kc, pl.kc_per_split);  // every part non-empty
+  pl.part_bytes = pl.splits > 1
+                      ? align_up((size_t)tiles * pl.splits * pl.mt * pl.nt * 4, 256) +
+                            align_up((size_t)tiles * pl.splits * pl.mt * 4, 256)
+                      : 0;
+  return pl;
+}
+
+hipError_t launch_gemm(const LinArgs& a, int epi, const GemmPlan& pl, void* part_ws, int* counters,
+                       hipStream_t s) {
+  GemmParams gp{};
+  gp.A = a.A; gp.W = a.W; gp.gain = a.gain; gp.bias = a.bias; gp.out = a.out;
+  gp.M = a.M; gp.K = a.K; gp.lda = a.lda; gp.ldo = a.ldo; gp.n_out = a.n_out;
+  gp.eps = a.eps;
+  gp.n_mt = pl.n_mt; gp.n_nt = pl.n_nt; gp.splits = pl.splits; gp.kc_per_split = pl.kc_per_split;
+  gp.per_xcd = ceil_div(pl.n_mt * pl.n_nt * pl.splits, 8);
+  gp.counters = counters;
+  if (pl.splits > 1) {
+    gp.part = static_cast<float*>(part_ws);
+    gp.part_ss = reinterpret_cast<float*>(static_cast<char*>(part_ws) +
+                                          align_up((size_t)pl.n_mt * pl.n_nt * pl.splits * pl.mt * pl.nt * 4, 256));
+  }
+  const bool norm = a.norm != 0;
+  switch (epi) {
+    case EPI_F32: return launch_epi<EPI_F32>(pl, gp, norm, s);
+    case EPI_F16: return launch_epi<EPI_F16>(pl, gp, norm, s);
+    case EPI_RESID: return launch_epi<EPI_RESID>(pl, gp, norm, s);
+    case EPI_SILU: return launch_epi<EPI_SILU>(pl, gp, norm, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pkv

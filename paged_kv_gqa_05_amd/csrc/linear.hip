@@ -15,15 +15,10 @@
 // (h = f16(h + y) in place: the residual add of the next norm), SILU (rows
 // [gate | up]: act = f16(silu(g) * u)), F16 (logits).
 //
-// Two kernels:
-//  * batch < 32: GEMV.  A group of LPC lanes (16, 32 or 64) streams one
-//    output row of W (one gate/up pair for SILU) with 16-byte loads and v_dot2
-//    against every batch row, then reduces across its lanes.
-//  * batch >= 32: MFMA GEMM.  64 x 64 tiles (W rows), K step 64 staged through
-//    LDS (double buffered), 4 waves each 32 x 32 with v_mfma_f32_16x16x32_f16.
-//    Workgroup ids are remapped so that the M tiles sharing one W tile run on
-//    the same XCD (the hardware deals workgroups round-robin over the 8 XCDs),
-//    so each W tile is fetched from HBM into one L2 only.
+// This file holds the GEMV for batch < 32: a group of LPC lanes (16, 32 or
+// 64) streams one output row of W (one gate/up pair for SILU) with 16-byte
+// loads and v_dot2 against every batch row, then reduces across its lanes.
+// Batches of 32 and more go to the MFMA GEMM in gemm.hip.
 #include "linear.h"
 
 namespace pkv {
@@ -133,167 +128,31 @@ hipError_t gemv_dispatch(const LinArgs& a, hipStream_t s) {
   return gemv_dispatch_mt<64, EPI>(a, s);
 }
 
-// ------------------------------------------------------------------ GEMM
-
-constexpr int BM = 64, BNW = 64, BK = 64, LDSK = BK + 8;
-
-template <int EPI>
-__global__ void __launch_bounds__(256) gemm_kernel(LinArgs a, int n_mt, int n_nt, int per_xcd) {
-  constexpr bool PAIR = (EPI == EPI_SILU);
-  __shared__ h16 sA[2][BM][LDSK];
-  __shared__ h16 sW[2][BNW][LDSK];
-  __shared__ float s_r[BM];
-
-  // XCD-aware tile order: the 8 XCDs each take a contiguous range of tiles,
-  // M tiles fastest, so the M tiles of one W tile share an L2.
-  const int L = blockIdx.x;
-  const int T = (L & 7) * per_xcd + (L >> 3);
-  if (T >= n_mt * n_nt) return;
-  const int mt = T % n_mt, nt = T / n_mt;
-  const int m0 = mt * BM;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  // W row (global) held in tile row rr; -1 past the end
-  auto wrow = [&](int rr) -> int {
-    if (PAIR) {
-      const int j = nt * (BNW / 2) + (rr & 31);
-      return j < a.n_out ? j + (rr >= 32 ? a.n_out : 0) : -1;
-    }
-    const int n = nt * BNW + rr;
-    return n < a.n_out ? n : -1;
-  };
-
-  // each thread stages rows lr and lr + 32 (A and W) at k-chunk lc
-  const int lr = tid >> 3, lc = (tid & 7) * 8;
-  const int ar0 = m0 + lr, ar1 = m0 + lr + 32;
-  const int wr0 = wrow(lr), wr1 = wrow(lr + 32);
-  const h16x8 zero = h16x8{0, 0, 0, 0, 0, 0, 0, 0};
-  const h16x8 one = h16x8{1, 1, 1, 1, 1, 1, 1, 1};
-  float ss0 = 0.f, ss1 = 0.f;
-
-  h16x8 ra0, ra1, rw0, rw1;
-  auto gload = [&](int k0) {
-    const int k = k0 + lc;
-    const bool kin = k < a.K;
-    ra0 = (kin && ar0 < a.M) ? *reinterpret_cast<const h16x8*>(a.A + (size_t)ar0 * a.lda + k) : zero;
-    ra1 = (kin && ar1 < a.M) ? *reinterpret_cast<const h16x8*>(a.A + (size_t)ar1 * a.lda + k) : zero;
-    rw0 = (kin && wr0 >= 0) ? *reinterpret_cast<const h16x8*>(a.W + (size_t)wr0 * a.K + k) : zero;
-    rw1 = (kin && wr1 >= 0) ? *reinterpret_cast<const h16x8*>(a.W + (size_t)wr1 * a.K + k) : zero;
-    if (a.norm) {
-      ss0 = dot8(ra0, ra0, ss0);
-      ss1 = dot8(ra1, ra1, ss1);
-    }
-    if (a.gain) {
-      const h16x8 g = kin ? *reinterpret_cast<const h16x8*>(a.gain + k) : one;
-      ra0 = ra0 * g;
-      ra1 = ra1 * g;
-    }
-  };
-  auto lstore = [&](int buf) {
-    *reinterpret_cast<h16x8*>(&sA[buf][lr][lc]) = ra0;
-    *reinterpret_cast<h16x8*>(&sA[buf][lr + 32][lc]) = ra1;
-    *reinterpret_cast<h16x8*>(&sW[buf][lr][lc]) = rw0;
-    *reinterpret_cast<h16x8*>(&sW[buf][lr + 32][lc]) = rw1;
-  };
-
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // tile-row base of N fragment fn for this wave: pairs keep gate and up of
-  // the same logical column in the same lane
-  const int wb0 = PAIR ? wn * 16 : wn * 32;
-  const int wb1 = PAIR ? 32 + wn * 16 : wn * 32 + 16;
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-
-  const int nk = (a.K + BK - 1) / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      h16x8 af[2], wf[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const h16x8*>(&sA[buf][wm * 32 + i * 16 + fr][kk + fk]);
-      wf[0] = *reinterpret_cast<const h16x8*>(&sW[buf][wb0 + fr][kk + fk]);
-      wf[1] = *reinterpret_cast<const h16x8*>(&sW[buf][wb1 + fr][kk + fk]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], wf[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // per-row 1/rms: 8 consecutive threads share a row
-  if (a.norm) {
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-      ss0 += __shfl_xor(ss0, o, 64);
-      ss1 += __shfl_xor(ss1, o, 64);
-    }
-    if ((tid & 7) == 0) {
-      s_r[lr] = rsqrtf(ss0 / (float)a.K + a.eps);
-      s_r[lr + 32] = rsqrtf(ss1 / (float)a.K + a.eps);
-    }
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int ml = wm * 32 + i * 16 + (lane >> 4) * 4 + rr;
-      const int m = m0 + ml;
-      if (m >= a.M) continue;
-      const float r = a.norm ? s_r[ml] : 1.0f;
-      if (PAIR) {
-        const int col = nt * (BNW / 2) + wn * 16 + fr;
-        if (col < a.n_out) epilogue<EPI>(a, m, col, acc[i][0][rr] * r, acc[i][1][rr] * r);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = nt * BNW + (j ? wb1 : wb0) + fr;
-          if (col < a.n_out) epilogue<EPI>(a, m, col, acc[i][j][rr] * r, 0.f);
-        }
-      }
-    }
-  }
-}
-
-template <int EPI>
-hipError_t gemm_dispatch(const LinArgs& a, hipStream_t s) {
-  const int n_mt = (a.M + BM - 1) / BM;
-  const int cols_per_tile = (EPI == EPI_SILU) ? BNW / 2 : BNW;
-  const int n_nt = (a.n_out + cols_per_tile - 1) / cols_per_tile;
-  const int tiles = n_mt * n_nt;
-  const int per_xcd = (tiles + 7) / 8;
-  hipLaunchKernelGGL((gemm_kernel<EPI>), dim3(per_xcd * 8), dim3(256), 0, s, a, n_mt, n_nt, per_xcd);
-  return hipGetLastError();
-}
-
 }  // namespace
 
-hipError_t launch_linear(const LinArgs& a, int epi, hipStream_t s) {
-  const bool mfma = a.M >= kMfmaMinBatch;
+__global__ void zero_i32_kernel(int* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+size_t linear_ws_bytes(int M, int n_out, int K, int epi) {
+  if (M < kMfmaMinBatch) return 0;
+  return gemm_plan(M, n_out, K, epi).part_bytes;
+}
+
+hipError_t launch_linear(const LinArgs& a, int epi, void* part_ws, int* counters, hipStream_t s) {
+  if (a.M >= kMfmaMinBatch) return launch_gemm(a, epi, gemm_plan(a.M, a.n_out, a.K, epi), part_ws, counters, s);
   switch (epi) {
-    case EPI_F32: return mfma ? gemm_dispatch<EPI_F32>(a, s) : gemv_dispatch<EPI_F32>(a, s);
-    case EPI_F16: return mfma ? gemm_dispatch<EPI_F16>(a, s) : gemv_dispatch<EPI_F16>(a, s);
-    case EPI_RESID: return mfma ? gemm_dispatch<EPI_RESID>(a, s) : gemv_dispatch<EPI_RESID>(a, s);
-    case EPI_SILU: return mfma ? gemm_dispatch<EPI_SILU>(a, s) : gemv_dispatch<EPI_SILU>(a, s);
+    case EPI_F32: return gemv_dispatch<EPI_F32>(a, s);
+    case EPI_F16: return gemv_dispatch<EPI_F16>(a, s);
+    case EPI_RESID: return gemv_dispatch<EPI_RESID>(a, s);
+    case EPI_SILU: return gemv_dispatch<EPI_SILU>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_zero_i32(int* p, int n, hipStream_t s) {
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(std::min(64, (n + 255) / 256)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
 }
 
 }  // namespace pkv

@@ -13,6 +13,7 @@
 // The step adds the embedding gather before the layers and RMSNorm + LM head
 // after them.  Section "CUDA 그래프 리플레이": the forward is captured once in
 // a graph and replayed on the caller's stream; sampling (argmax) stays outside.
+#include <algorithm>
 #include <cmath>
 #include <new>
 #include <string>
@@ -47,6 +48,8 @@ struct StepBuffers {
   _Float16* o;    // [B][Hq][D]
   _Float16* act;  // [B][F]
   void* attn_ws;
+  void* gemm_ws;  // split-K partial tiles of the MFMA projections
+  int* counters;  // split-K arrival counters, zeroed at the start of each call
   size_t total;
 };
 
@@ -66,6 +69,15 @@ StepBuffers carve(const pkv_model* m, int batch, const AttnPlan& plan, void* bas
   b.o = reinterpret_cast<_Float16*>(take((size_t)batch * d.num_q_heads * d.head_dim * 2));
   b.act = reinterpret_cast<_Float16*>(take((size_t)batch * d.ffn * 2));
   b.attn_ws = take(plan.ws_bytes);
+  const int qkv_n = (d.num_q_heads + 2 * d.num_kv_heads) * d.head_dim;
+  size_t g = 0;
+  g = std::max(g, linear_ws_bytes(batch, qkv_n, d.hidden, EPI_F32));
+  g = std::max(g, linear_ws_bytes(batch, d.hidden, d.num_q_heads * d.head_dim, EPI_RESID));
+  g = std::max(g, linear_ws_bytes(batch, d.ffn, d.hidden, EPI_SILU));
+  g = std::max(g, linear_ws_bytes(batch, d.hidden, d.ffn, EPI_RESID));
+  g = std::max(g, linear_ws_bytes(batch, d.vocab, d.hidden, EPI_F16));
+  b.gemm_ws = take(g);
+  b.counters = reinterpret_cast<int*>(take((size_t)kGemmMaxCounters * sizeof(int)));
   b.total = off;
   return b;
 }
@@ -113,7 +125,7 @@ hipError_t run_layer(const pkv_model* m, pkv_cache* cache, int layer, _Float16* 
   a.gain = static_cast<const _Float16*>(w.w_in); a.norm = 1;
   a.bias = static_cast<const _Float16*>(w.b_qkv);
   a.out = sb.qkv; a.ldo = qkv_n; a.n_out = qkv_n;
-  if ((e = launch_linear(a, EPI_F32, s)) != hipSuccess) return e;
+  if ((e = launch_linear(a, EPI_F32, sb.gemm_ws, sb.counters, s)) != hipSuccess) return e;
   // 2. RoPE + KV append
   if ((e = launch_rope_append(sb.qkv, m->rope, sb.q, kp, vp, bt, bt_stride, lens, batch, d.num_q_heads,
                               d.num_kv_heads, d.head_dim, s)) != hipSuccess)
@@ -131,7 +143,7 @@ hipError_t run_layer(const pkv_model* m, pkv_cache* cache, int layer, _Float16* 
   a.A = sb.o; a.lda = qd; a.K = qd; a.M = batch;
   a.W = static_cast<const _Float16*>(w.w_o);
   a.out = h; a.ldo = d.hidden; a.n_out = d.hidden;
-  if ((e = launch_linear(a, EPI_RESID, s)) != hipSuccess) return e;
+  if ((e = launch_linear(a, EPI_RESID, sb.gemm_ws, sb.counters, s)) != hipSuccess) return e;
   // 5. RMSNorm + gate/up + SiLU*mul -> act
   a = LinArgs{};
   a.eps = d.rms_eps;
@@ -139,21 +151,21 @@ hipError_t run_layer(const pkv_model* m, pkv_cache* cache, int layer, _Float16* 
   a.W = static_cast<const _Float16*>(w.w_gate_up);
   a.gain = static_cast<const _Float16*>(w.w_post); a.norm = 1;
   a.out = sb.act; a.ldo = d.ffn; a.n_out = d.ffn;
-  if ((e = launch_linear(a, EPI_SILU, s)) != hipSuccess) return e;
+  if ((e = launch_linear(a, EPI_SILU, sb.gemm_ws, sb.counters, s)) != hipSuccess) return e;
   // 6. down projection + residual add
   a = LinArgs{};
   a.eps = d.rms_eps;
   a.A = sb.act; a.lda = d.ffn; a.K = d.ffn; a.M = batch;
   a.W = static_cast<const _Float16*>(w.w_down);
   a.out = h; a.ldo = d.hidden; a.n_out = d.hidden;
-  return launch_linear(a, EPI_RESID, s);
+  return launch_linear(a, EPI_RESID, sb.gemm_ws, sb.counters, s);
 }
 
 hipError_t run_step(const pkv_model* m, pkv_cache* cache, const int32_t* tokens, const int32_t* bt,
                     int bt_stride, const int32_t* lens, int batch, void* logits, _Float16* h,
                     const StepBuffers& sb, const AttnPlan& plan, hipStream_t s) {
   const pkv_model_desc& d = m->d;
-  hipError_t e = launch_embed(m->embed, tokens, h, batch, d.hidden, s);
+  hipError_t e = launch_embed(m->embed, tokens, h, batch, d.hidden, sb.counters, kGemmMaxCounters, s);
   if (e != hipSuccess) return e;
   for (int l = 0; l < d.num_layers; ++l) {
     e = run_layer(m, cache, l, h, bt, bt_stride, lens, batch, sb, plan, s);
@@ -165,7 +177,7 @@ hipError_t run_step(const pkv_model* m, pkv_cache* cache, const int32_t* tokens,
   a.W = static_cast<const _Float16*>(m->w_lm);
   a.gain = static_cast<const _Float16*>(m->w_final); a.norm = 1;
   a.out = logits; a.ldo = d.vocab; a.n_out = d.vocab;
-  return launch_linear(a, EPI_F16, s);
+  return launch_linear(a, EPI_F16, sb.gemm_ws, sb.counters, s);
 }
 
 }  // namespace
@@ -185,6 +197,7 @@ pkv_status pkv_model_create(const pkv_model_desc* desc, const void* embed, const
   if (d.num_q_heads % d.num_kv_heads) return fail(PKV_E_ARG, "num_q_heads must be a multiple of num_kv_heads");
   if (d.num_q_heads / d.num_kv_heads > kMaxGroup) return fail(PKV_E_UNSUPPORTED, "more than 16 query heads per KV head");
   if (d.hidden % 8 || d.ffn % 8) return fail(PKV_E_UNSUPPORTED, "hidden and ffn must be multiples of 8");
+  if (d.hidden > 16384 || d.ffn > 65536) return fail(PKV_E_UNSUPPORTED, "hidden <= 16384 and ffn <= 65536 required");
   if (!(d.rms_eps > 0.f) || !(d.rope_theta > 1.f)) return fail(PKV_E_ARG, "rms_eps > 0 and rope_theta > 1 required");
   for (int l = 0; l < d.num_layers; ++l) {
     const pkv_layer_weights& w = layers[l];
@@ -251,6 +264,7 @@ pkv_status pkv_decode_layer(const pkv_model* m, pkv_cache* cache, int layer, voi
   if (!hidden) return fail(PKV_E_ARG, "hidden is NULL");
   if (layer < 0 || layer >= m->d.num_layers || layer >= cache->desc.num_layers)
     return fail(PKV_E_ARG, "layer out of range");
+  PKV_HIP(launch_zero_i32(sb.counters, kGemmMaxCounters, static_cast<hipStream_t>(stream)));
   PKV_HIP(run_layer(m, cache, layer, static_cast<_Float16*>(hidden), bt, bt_stride, lens, batch, sb, plan,
                     static_cast<hipStream_t>(stream)));
   return PKV_OK;

@@ -12,8 +12,10 @@ namespace {
 
 typedef _Float16 h16;
 
+// Also zeroes zero_n ints at zero_p (the split-K arrival counters of the step).
 __global__ void embed_kernel(const h16* __restrict__ table, const int32_t* __restrict__ tokens,
-                             h16* __restrict__ h, int hidden) {
+                             h16* __restrict__ h, int hidden, int* __restrict__ zero_p, int zero_n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < zero_n; i += gridDim.x * blockDim.x) zero_p[i] = 0;
   const int b = blockIdx.x;
   const h16* src = table + (size_t)tokens[b] * hidden;
   h16* dst = h + (size_t)b * hidden;
@@ -109,9 +111,9 @@ __global__ void argmax_kernel(const h16* __restrict__ logits, int vocab, int32_t
 }  // namespace
 
 hipError_t launch_embed(const void* table, const int32_t* tokens, void* h, int batch, int hidden,
-                        hipStream_t s) {
+                        int* zero_p, int zero_n, hipStream_t s) {
   hipLaunchKernelGGL(embed_kernel, dim3(batch), dim3(256), 0, s, static_cast<const h16*>(table), tokens,
-                     static_cast<h16*>(h), hidden);
+                     static_cast<h16*>(h), hidden, zero_p, zero_n);
   return hipGetLastError();
 }
 
