@@ -264,3 +264,20 @@ def model_weights_torch(shape: Shape, seed, device="cuda", bias=True, std=0.02, 
         })
     return {"embed": mat(shape.vocab, h), "layers": layers, "w_final_norm": gain(h),
             "w_lm_head": mat(shape.vocab, h)}
+
+
+def random_pools_torch(seed, num_blocks, n_kv_heads, head_dim, valid, device="cuda"):
+    """The random_pools recipe (N(0, 1) in valid slots, NaN elsewhere) drawn
+    with torch's Philox generator on the device, for full-size caches whose
+    host generation would dominate a test.  valid: bool [num_blocks, 16]."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    k = torch.empty(num_blocks, n_kv_heads, BLOCK_SIZE, head_dim, dtype=torch.float16, device=device)
+    v = torch.empty(num_blocks, n_kv_heads, head_dim, BLOCK_SIZE, dtype=torch.float16, device=device)
+    k.normal_(generator=g)
+    v.normal_(generator=g)
+    inval = torch.from_numpy(~np.asarray(valid, dtype=bool)).to(device)
+    k.masked_fill_(inval[:, None, :, None], float("nan"))
+    v.masked_fill_(inval[:, None, None, :], float("nan"))
+    return k, v
