@@ -37,11 +37,15 @@
  *     contract violation.  pkv_validate_metadata() checks host copies.
  *
  * Paged KV layout (block size BS = 16, Hkv KV heads, head_dim D in {64, 128}):
- *   For layer l the cache memory holds the K pool, then the V pool:
- *     K pool: [num_blocks][Hkv][BS][D]   (token-major inside a block)
- *     V pool: [num_blocks][Hkv][D][BS]   (dim-major inside a block)
- *   element size 2 bytes (f16) or 1 byte (fp8 codes).  Token t of sequence b is
- *   in block block_tables[b * bt_stride + t / BS], slot t % BS.
+ *   For layer l the cache memory holds the K pool, then the V pool, each
+ *   [num_blocks][Hkv] tiles of 16 tokens:
+ *     K tile, f16: [D/8][BS][8]   element (t, d) at ((d/8)*BS + t)*8 + d%8
+ *     K tile, fp8: [D/16][BS][16] element (t, d) at ((d/16)*BS + t)*16 + d%16
+ *     V tile (both): [D][BS]      element (t, d) at d*BS + t
+ *   (16-byte chunks of one token's dims, so a wave reads a K tile with
+ *   contiguous 1 KB loads; V dim-major).  Element size 2 bytes (f16) or 1 byte
+ *   (fp8 codes).  Token t of sequence b is in block
+ *   block_tables[b * bt_stride + t / BS], slot t % BS.
  *   context_lens[b] counts the cached tokens INCLUDING the token being decoded:
  *   the new token's K/V go to position pos = context_lens[b] - 1 and attention
  *   covers positions [0, context_lens[b]).  context_lens[b] == 0 marks an
@@ -105,7 +109,7 @@ pkv_status pkv_kv_cache_create(const pkv_cache_desc* desc, void* dev_mem, size_t
                                const float* k_scales, const float* v_scales, pkv_cache** out);
 void pkv_kv_cache_destroy(pkv_cache* cache);
 
-/* Device addresses of layer `layer`'s K and V pools (layout above). */
+/* Device addresses of layer `layer`'s K and V pools (tile layouts above). */
 pkv_status pkv_kv_cache_layer(const pkv_cache* cache, int layer, void** k_pool, void** v_pool);
 
 /* Append one token per row: k and v are f16 [batch][Hkv][D]; row b is stored
@@ -131,10 +135,11 @@ pkv_status pkv_attn_workspace_bytes(const pkv_cache* cache, int batch, int num_q
  *   layer's scales).  Accumulation is fp32; out is f16 [batch][Hq][D]; q is f16
  *   [batch][Hq][D].  lse (nullable, f32 [batch][Hq]) receives max s +
  *   ln(sum exp(s - max s)) (-inf for inactive rows).  The context is split into
- *   partitions processed in parallel and merged in a second pass; workspace
- *   (>= pkv_attn_workspace_bytes, 256-byte aligned) holds the partial results
- *   and needs no initialisation.  bt_stride >= ceil(max_context / 16);
- *   every context_lens[b] <= max_context. */
+ *   partitions processed in parallel and merged in a second pass (fixed
+ *   order, so results are deterministic); workspace (>=
+ *   pkv_attn_workspace_bytes, 256-byte aligned) holds the partial results and
+ *   needs no initialisation.  bt_stride >= ceil(max_context / 16); every
+ *   context_lens[b] <= max_context <= 262144 (PKV_E_UNSUPPORTED above). */
 pkv_status pkv_paged_attn_decode(const pkv_cache* cache, int layer, const void* q, void* out,
                                  float* lse, const int32_t* block_tables, int bt_stride,
                                  const int32_t* context_lens, int batch, int num_q_heads,

@@ -71,7 +71,8 @@ class KVCache:
         self.num_kv_heads, self.head_dim, self.dtype = num_kv_heads, head_dim, dtype
 
     def layer(self, layer):
-        """(K pool [NB, Hkv, 16, D], V pool [NB, Hkv, D, 16]) views of one layer."""
+        """Views of one layer's pools in the library layout (include/pkv.h):
+        K [NB, Hkv, D/c, 16, c] with c = 8 (f16) or 16 (fp8), V [NB, Hkv, D, 16]."""
         k, v = C.c_void_p(), C.c_void_p()
         _check(_lib.pkv_kv_cache_layer(self.handle, layer, C.byref(k), C.byref(v)))
         tdt = torch.uint8 if self.dtype == KV_FP8_E4M3 else torch.float16
@@ -81,7 +82,8 @@ class KVCache:
         kt = self.mem[k.value - base:k.value - base + n].view(tdt)
         vt = self.mem[v.value - base:v.value - base + n].view(tdt)
         nb, hkv, d = self.num_blocks, self.num_kv_heads, self.head_dim
-        return kt.view(nb, hkv, BLOCK_SIZE, d), vt.view(nb, hkv, d, BLOCK_SIZE)
+        c = 16 if self.dtype == KV_FP8_E4M3 else 8
+        return kt.view(nb, hkv, d // c, BLOCK_SIZE, c), vt.view(nb, hkv, d, BLOCK_SIZE)
 
     def close(self):
         _destroy("pkv_kv_cache_destroy", self)

@@ -1,4 +1,5 @@
-// Paged GQA decode attention for gfx950: split over the context + merge pass.
+// Paged GQA decode attention for gfx950: split over the context with the merge
+// of the partitions fused into the same kernel.
 //
 // What it computes (rvLLM post on discuss.pytorch.kr, section
 // "PagedAttention과 FlashAttention-3": block-table KV cache, GQA reads each KV
@@ -7,24 +8,32 @@
 // with K_t, V_t gathered through the row's block table.
 //
 // Design (MI355X, not the pages' FlashAttention-3 kernels):
-//  * One workgroup (4 waves) per (row b, KV head g, partition of `part`
-//    tokens).  Workgroup ids are mapped onto the list of non-empty partitions
-//    (a prefix sum over the rows' partition counts), so active work is packed
-//    at the front of the grid whatever the context-length mix.
-//  * Each wave takes every 4th 16-token block of the partition.  The block's
-//    K tile [16][D] feeds v_mfma_f32_16x16x32_f16 directly from registers as
-//    the A operand (token = MFMA row, 8 contiguous dims per lane), the group's
-//    query rows (G <= 16, zero padded) are the B operand, giving S^T
-//    [token][head].  That C layout is exactly the B operand of
-//    v_mfma_f32_16x16x16f16 for O^T += V^T P^T, whose A operand is read from
-//    the dim-major V block [D][16] with one 8-byte load per 16 dims.  No LDS
-//    staging and no shuffles between the two products.
-//  * Online softmax in the log2 domain per head column; the running max lives
-//    in the four lanes of a column, the running sum per lane.  The four waves'
-//    (max, sum, O) are combined through LDS at the end.
-//  * A row with a single partition writes its normalised f16 output directly;
-//    otherwise the partition writes (max, sum, unnormalised O) in fp32 and the
-//    merge kernel combines them.  Nothing is zero-filled.
+//  * One workgroup (4 waves) per (row b, KV head g, partition of 64 NT tokens),
+//    blockIdx = (b * Hkv + g) * P + partition; partitions beyond a row's
+//    context exit at once.  The row's block-table entries and the query rows
+//    are loaded together with the context length, so a workgroup waits one
+//    memory round trip before its KV loads.
+//  * Wave w of a partition owns its blocks w, w + 4, ... (at most NT) and loads
+//    all of their K and V at once.  K blocks are stored in 16-byte chunks of
+//    8 dims x 16 tokens (fp8: 16 dims), so each K load instruction of a wave
+//    reads 1 KB of contiguous memory; V blocks are dim-major [D][16].
+//  * Scores: the K block feeds v_mfma_f32_16x16x32_f16 from registers as the A
+//    operand (token = MFMA row), the group's query rows (G <= 16, zero padded)
+//    are the B operand, giving S^T [token][head].  The dot product over D is
+//    taken in a permuted dim order (the same for q and K), which is what makes
+//    the K loads contiguous.  That C layout is exactly the B operand of
+//    v_mfma_f32_16x16x16f16 for O^T += V^T P^T, whose A operand comes from the
+//    V block with one 8-byte load per 16 dims: no LDS, no shuffles.
+//  * Softmax per wave in two passes over registers: all scores first, one max
+//    per head, then P = exp2(S - max) and the PV products with no rescaling
+//    (an online softmax rescales the 32 output accumulators at every block,
+//    which cost more than the loads).  The four waves' (max, sum, O) are
+//    combined through LDS.
+//  * A row with a single partition writes its normalised f16 output directly.
+//    Otherwise each partition stores (max, sum, unnormalised O) in fp32 and a
+//    merge kernel combines them in partition order (deterministic; launched
+//    only when some row can span more than one partition).  Nothing is
+//    zero-filled.
 //  * FP8 E4M3 codes are converted to f16 in registers with the gfx950
 //    conversion instruction (exact: every E4M3 value is an f16 value); the
 //    per-tensor K scale is folded into the score scale and the V scale into
@@ -44,6 +53,9 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLog2e = 1.44269504088896341f;
+// Partitions per (row, KV head) the merge kernel can hold (kMaxGroup x
+// kMaxParts weights in LDS).
+constexpr int kMaxParts = 512;
 
 struct SplitParams {
   const unsigned char* k_pool;
@@ -53,8 +65,8 @@ struct SplitParams {
   float* lse;
   const int* bt;
   const int* lens;
-  float2* ws_ml;
-  float* ws_o;
+  float2* ws_ml;   // [B][Hq][P] (max, sum) per partition
+  float* ws_o;     // [B][Hq][P][D] unnormalised O per partition
   int bt_stride;
   int batch, hq, hkv, group, part, n_parts_max;
   float scale_log2;  // softmax scale * log2(e) * K dequant scale
@@ -77,21 +89,34 @@ __device__ __forceinline__ h16x8 e4m3x8_to_h16x8(int lo, int hi) {
   return h16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// Registers of one 16-token tile for one lane.
+// The 8-dim chunk that lane group q4 feeds at QK step s (D/32 steps).  f16 K
+// is stored as [D/8][16 tokens][8 dims]: step s reads chunks 4s..4s+3.  fp8 K
+// is stored as [D/16][16 tokens][16 dims]: one 16-byte load covers steps 2u and
+// 2u+1, i.e. chunks 8u + 2 q4 and 8u + 2 q4 + 1.
+template <bool FP8>
+__device__ __forceinline__ int q_chunk(int s, int q4) {
+  return FP8 ? 8 * (s >> 1) + 2 * q4 + (s & 1) : 4 * s + q4;
+}
+
+// Registers of one 16-token block for one lane (n = token of the K rows and
+// dim-in-group of the V rows, q4 = lane group).
 template <int D, bool FP8>
 struct Tile;
 
 template <int D>
 struct Tile<D, false> {
-  h16x8 k[D / 32];  // K[token n][dims q4*D/4 + 8s .. +8]
+  h16x8 k[D / 32];  // step s: token n, dims of chunk 4s + q4
   h16x4 v[D / 16];  // V^T[dim 16j + n][tokens 4*q4 .. +4]
-  __device__ __forceinline__ void load(const SplitParams& p, int blk, int g, int n, int q4) {
-    const h16* kp = reinterpret_cast<const h16*>(p.k_pool) +
-                    ((size_t)(blk * p.hkv + g) * kBlock + n) * D + q4 * (D / 4);
+  __device__ __forceinline__ void load_k(const SplitParams& p, int blk, int g, int lane) {
+    const size_t tile = (size_t)blk * p.hkv + g;
+    const h16* kp = reinterpret_cast<const h16*>(p.k_pool) + tile * kBlock * D + lane * 8;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) k[s] = *reinterpret_cast<const h16x8*>(kp + 8 * s);
-    const h16* vp = reinterpret_cast<const h16*>(p.v_pool) +
-                    (size_t)(blk * p.hkv + g) * D * kBlock + n * kBlock + q4 * 4;
+    for (int s = 0; s < D / 32; ++s) k[s] = *reinterpret_cast<const h16x8*>(kp + s * 512);
+  }
+  __device__ __forceinline__ void load_v(const SplitParams& p, int blk, int g, int lane) {
+    const size_t tile = (size_t)blk * p.hkv + g;
+    const h16* vp = reinterpret_cast<const h16*>(p.v_pool) + tile * D * kBlock + (lane & 15) * kBlock +
+                    (lane >> 4) * 4;
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) v[j] = *reinterpret_cast<const h16x4*>(vp + j * 16 * kBlock);
   }
@@ -101,14 +126,17 @@ struct Tile<D, false> {
 
 template <int D>
 struct Tile<D, true> {
-  int4 k[D / 64];  // 16 codes per int4: dims q4*D/4 + 16i .. +16
+  int4 k[D / 64];  // 16 codes: token n, dims 16 (4u + q4) .. +16 (steps 2u, 2u + 1)
   int v[D / 16];   // 4 codes: V^T[dim 16j + n][tokens 4*q4 .. +4]
-  __device__ __forceinline__ void load(const SplitParams& p, int blk, int g, int n, int q4) {
-    const unsigned char* kp =
-        p.k_pool + ((size_t)(blk * p.hkv + g) * kBlock + n) * D + q4 * (D / 4);
+  __device__ __forceinline__ void load_k(const SplitParams& p, int blk, int g, int lane) {
+    const size_t tile = (size_t)blk * p.hkv + g;
+    const unsigned char* kp = p.k_pool + tile * kBlock * D + lane * 16;
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) k[i] = *reinterpret_cast<const int4*>(kp + 16 * i);
-    const unsigned char* vp = p.v_pool + (size_t)(blk * p.hkv + g) * D * kBlock + n * kBlock + q4 * 4;
+    for (int u = 0; u < D / 64; ++u) k[u] = *reinterpret_cast<const int4*>(kp + u * 1024);
+  }
+  __device__ __forceinline__ void load_v(const SplitParams& p, int blk, int g, int lane) {
+    const size_t tile = (size_t)blk * p.hkv + g;
+    const unsigned char* vp = p.v_pool + tile * D * kBlock + (lane & 15) * kBlock + (lane >> 4) * 4;
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) v[j] = *reinterpret_cast<const int*>(vp + j * 16 * kBlock);
   }
@@ -119,146 +147,131 @@ struct Tile<D, true> {
   __device__ __forceinline__ h16x4 vfrag(int j) const { return e4m3x4_to_h16x4(v[j]); }
 };
 
-// Inclusive block-wide prefix sum of one int per thread (256 threads).
-__device__ __forceinline__ int block_incl_scan(int x, int* s_wsum, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) s_wsum[wave] = x;
-  __syncthreads();
-  int pre = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    int v = s_wsum[w];
-    pre += (w < wave) ? v : 0;
-    tot += v;
-  }
-  *total = tot;
-  __syncthreads();
-  return x + pre;
-}
-
-template <int D, bool FP8>
-__global__ void __launch_bounds__(kThreads) attn_split_kernel(SplitParams p) {
-  constexpr int OSTR = D + 4;  // padded LDS row (floats)
+template <int D, bool FP8, int NT>
+__global__ void __launch_bounds__(kThreads) attn_kernel(SplitParams p) {
+  // padded LDS row (floats) for the combine of the four waves
+  constexpr int OSTR = D + 4;
   __shared__ float s_o[kWaves][kMaxGroup][OSTR];
   __shared__ float s_m[kWaves][kMaxGroup];
   __shared__ float s_l[kWaves][kMaxGroup];
-  __shared__ int s_wsum[kWaves];
-  __shared__ int s_item[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, q4 = lane >> 4;
 
-  // ---- map this workgroup onto the packed list of (row, kv head, partition)
+  // ---- this workgroup's (row, KV head, partition): blockIdx = (b * Hkv + g) * P + part
   const int wg = blockIdx.x;
-  if (tid == 0) s_item[0] = -1;
-  int carry = 0;
-  for (int base = 0; base < p.batch; base += kThreads) {
-    const int b = base + tid;
-    const int cnt = (b < p.batch) ? (p.lens[b] + p.part - 1) / p.part * p.hkv : 0;
-    int total;
-    const int incl = block_incl_scan(cnt, s_wsum, &total) + carry;
-    if (cnt > 0 && wg >= incl - cnt && wg < incl) {
-      s_item[0] = b;
-      s_item[1] = incl - cnt;
-    }
-    carry += total;
-    __syncthreads();
-    if (s_item[0] >= 0) break;  // uniform: read after the barrier
-  }
-  const int b = s_item[0];
-  if (b < 0) return;
-  const int c = p.lens[b];
-  const int np = (c + p.part - 1) / p.part;
-  const int r = wg - s_item[1];
-  const int g = r / np, part_idx = r - g * np;
-
+  const int part_idx = wg % p.n_parts_max;
+  const int bg = wg / p.n_parts_max;
+  const int b = bg / p.hkv, g = bg - b * p.hkv;
   const int tok0 = part_idx * p.part;
+  const int hbase = g * p.group;
+  // issued together, before the context length is known: the block-table
+  // entries of this wave's blocks (clamped inside the row) and the query rows
+  const int* btrow = p.bt + (size_t)b * p.bt_stride;
+  const int blk_l = btrow[min(tok0 / kBlock + wave + kWaves * min(lane, NT - 1), p.bt_stride - 1)];
+  h16x8 qf[D / 32];
+  {
+    const h16* qrow = p.q + ((size_t)b * p.hq + hbase + min(n, p.group - 1)) * D;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) qf[s] = *reinterpret_cast<const h16x8*>(qrow + 8 * q_chunk<FP8>(s, q4));
+  }
+  const int c = p.lens[b];
+  if (tok0 >= c) {  // beyond the row's context (or an inactive row)
+    if (c == 0 && g == 0 && part_idx == 0) {
+      for (int idx = tid; idx < p.hq * D; idx += kThreads) p.out[(size_t)b * p.hq * D + idx] = (h16)0.f;
+      if (p.lse)
+        for (int h = tid; h < p.hq; h += kThreads) p.lse[(size_t)b * p.hq + h] = -INFINITY;
+    }
+    return;
+  }
+  if (n >= p.group) {
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) qf[s] = h16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  const int np = (c + p.part - 1) / p.part;
   const int tok_end = min(c, tok0 + p.part);
   const int n_tiles = (tok_end - tok0 + kBlock - 1) / kBlock;
-  const int hbase = g * p.group;
+  const int my_tiles = wave < n_tiles ? (n_tiles - wave + kWaves - 1) / kWaves : 0;  // <= NT
 
-  // ---- query rows of this group as the B operand of the QK^T product
-  h16x8 qf[D / 32];
-#pragma unroll
-  for (int s = 0; s < D / 32; ++s) {
-    if (n < p.group) {
-      qf[s] = *reinterpret_cast<const h16x8*>(p.q + ((size_t)b * p.hq + hbase + n) * D +
-                                              q4 * (D / 4) + 8 * s);
-    } else {
-      qf[s] = h16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  }
-
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_w = -INFINITY, l_w = 0.f;  // this lane's head column (n), over the wave's tiles
   f32x4 o[D / 16];
 #pragma unroll
   for (int j = 0; j < D / 16; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int my_tiles = wave < n_tiles ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
-  const int* btrow = p.bt + (size_t)b * p.bt_stride + tok0 / kBlock;
-  const int blk_l = lane < my_tiles ? btrow[wave + kWaves * lane] : 0;
-
-  Tile<D, FP8> cur, nxt;
-  if (my_tiles > 0) cur.load(p, __shfl(blk_l, 0, 64), g, n, q4);
-  for (int t = 0; t < my_tiles; ++t) {
-    if (t + 1 < my_tiles) nxt.load(p, __shfl(blk_l, t + 1, 64), g, n, q4);
-    const int i = wave + kWaves * t;
-
-    // S^T[token][head] over the head dim
-    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (my_tiles > 0) {  // wave-uniform
+    // (1) every K and then every V block of this wave in flight at once (a
+    //     missing block re-reads the wave's last one, so the loads in flight
+    //     never depend on data and the compiler waits for exactly the ones it
+    //     uses); the scores start as soon as the K blocks land
+    Tile<D, FP8> tl[NT];
+    int blk[NT];
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.kfrag(s), qf[s], sacc, 0, 0, 0);
-
-    const int tb = tok0 + i * kBlock + 4 * q4;  // this lane's first token
-    float x[4];
+    for (int t = 0; t < NT; ++t) blk[t] = __shfl(blk_l, min(t, my_tiles - 1), 64);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) x[rr] = (tb + rr < tok_end) ? sacc[rr] * p.scale_log2 : -INFINITY;
-    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    for (int t = 0; t < NT; ++t) tl[t].load_k(p, blk[t], g, lane);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) tl[t].load_v(p, blk[t], g, lane);
+
+    // (2) scores S^T[token][head] of every block, in the log2 domain
+    float x[NT][4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(tl[t].kfrag(s), qf[s], sacc, 0, 0, 0);
+      const int tb = tok0 + (wave + kWaves * t) * kBlock + 4 * q4;  // this lane's first token
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        x[t][rr] = (t < my_tiles && tb + rr < tok_end) ? sacc[rr] * p.scale_log2 : -INFINITY;
+    }
+    // (3) one max per head over the wave's tokens (in-lane, then the 4 lane groups)
+    float mt = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) mt = fmaxf(mt, fmaxf(fmaxf(x[t][0], x[t][1]), fmaxf(x[t][2], x[t][3])));
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float pr[4];
+    m_w = mt;
+    // (4) P = exp2(S - m) and O^T += V^T P^T, no rescaling
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) pr[rr] = __builtin_amdgcn_exp2f(x[rr] - m_new);
-    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    if (__ballot(alpha != 1.0f)) {
+    for (int t = 0; t < NT; ++t) {
+      if (t < my_tiles) {
+        float pr[4];
 #pragma unroll
-      for (int j = 0; j < D / 16; ++j) o[j] *= alpha;
-    }
-    m_run = m_new;
-    const h16x4 pf = h16x4{(h16)pr[0], (h16)pr[1], (h16)pr[2], (h16)pr[3]};
-
-    const bool partial = (tok0 + (i + 1) * kBlock > tok_end);
+        for (int rr = 0; rr < 4; ++rr) pr[rr] = __builtin_amdgcn_exp2f(x[t][rr] - mt);
+        l_w += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        const h16x4 pf = h16x4{(h16)pr[0], (h16)pr[1], (h16)pr[2], (h16)pr[3]};
+        const int tb = tok0 + (wave + kWaves * t) * kBlock + 4 * q4;
+        if (tok0 + (wave + kWaves * t + 1) * kBlock > tok_end) {
+          // the row's last, partial block: slots past the context may hold
+          // anything (NaN included), so zero them before the product
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-      h16x4 vf = cur.vfrag(j);
-      if (partial) {
+          for (int j = 0; j < D / 16; ++j) {
+            h16x4 vf = tl[t].vfrag(j);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          if (tb + rr >= tok_end) vf[rr] = (h16)0.f;
+            for (int rr = 0; rr < 4; ++rr)
+              if (tb + rr >= tok_end) vf[rr] = (h16)0.f;
+            o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, pf, o[j], 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < D / 16; ++j)
+            o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(tl[t].vfrag(j), pf, o[j], 0, 0, 0);
+        }
       }
-      o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, pf, o[j], 0, 0, 0);
     }
-    if (t + 1 < my_tiles) cur = nxt;
   }
 
   // ---- combine the four lane groups' sums, then the four waves
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_w += __shfl_xor(l_w, 16, 64);
+  l_w += __shfl_xor(l_w, 32, 64);
 #pragma unroll
   for (int j = 0; j < D / 16; ++j)
     *reinterpret_cast<f32x4*>(&s_o[wave][n][16 * j + 4 * q4]) = o[j];
   if (q4 == 0) {
-    s_m[wave][n] = m_run;
-    s_l[wave][n] = l_run;
+    s_m[wave][n] = m_w;
+    s_l[wave][n] = l_w;
   }
   __syncthreads();
 
@@ -275,7 +288,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(SplitParams p) {
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float e = __builtin_amdgcn_exp2f(mw[w] - mx);
+      const float e = __builtin_amdgcn_exp2f(mw[w] - mx);  // 0 for a wave without tokens
       L += s_l[w][h] * e;
       O += s_o[w][h][d] * e;
     }
@@ -283,7 +296,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(SplitParams p) {
     if (single) {
       p.out[bh * D + d] = (h16)(O * p.v_scale / L);
       if (d == 0 && p.lse) p.lse[bh] = (mx + __log2f(L)) * kLn2;
-    } else {
+    } else {  // read by the merge kernel after this kernel has finished
       const size_t slot = bh * p.n_parts_max + part_idx;
       p.ws_o[slot * D + d] = O * p.v_scale;
       if (d == 0) p.ws_ml[slot] = make_float2(mx, L);
@@ -291,63 +304,95 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(SplitParams p) {
   }
 }
 
+// Merge of the partitions of rows with more than one: one workgroup per
+// (row, KV head); per-partition weights exp2(m_i - M) / L in LDS, then
+// O = sum_i w_i O_i in partition order with independent loads.
 template <int D>
-__global__ void __launch_bounds__(D) attn_merge_kernel(SplitParams p) {
-  const int bh = blockIdx.x;
-  const int b = bh / p.hq;
-  const int d = threadIdx.x;
+__global__ void __launch_bounds__(kThreads) attn_merge_kernel(SplitParams p) {
+  __shared__ float s_w[kMaxGroup][kMaxParts];
+  const int bg = blockIdx.x;
+  const int b = bg / p.hkv, g = bg - b * p.hkv;
   const int c = p.lens[b];
-  if (c == 0) {  // inactive row
-    p.out[(size_t)bh * D + d] = (h16)0.f;
-    if (d == 0 && p.lse) p.lse[bh] = -INFINITY;
-    return;
-  }
   const int np = (c + p.part - 1) / p.part;
-  if (np == 1) return;  // written by the split kernel
-  const float2* ml = p.ws_ml + (size_t)bh * p.n_parts_max;
-  const float* po = p.ws_o + (size_t)bh * p.n_parts_max * D + d;
-  float mx = -INFINITY;
-  for (int i = 0; i < np; ++i) mx = fmaxf(mx, ml[i].x);
-  float L = 0.f, O = 0.f;
-  for (int i = 0; i < np; ++i) {
-    const float2 v = ml[i];
-    const float e = __builtin_amdgcn_exp2f(v.x - mx);
-    L += v.y * e;
-    O += po[(size_t)i * D] * e;
+  if (np <= 1) return;  // written by the attention kernel (or an inactive row)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hbase = g * p.group;
+  for (int h = wave; h < p.group; h += kWaves) {
+    const float2* ml = p.ws_ml + ((size_t)b * p.hq + hbase + h) * p.n_parts_max;
+    float mloc = -INFINITY;
+    for (int i = lane; i < np; i += 64) mloc = fmaxf(mloc, ml[i].x);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o, 64));
+    float lloc = 0.f;
+    for (int i = lane; i < np; i += 64) {
+      const float2 v = ml[i];
+      const float e = __builtin_amdgcn_exp2f(v.x - mloc);
+      s_w[h][i] = e;
+      lloc += v.y * e;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o, 64);
+    const float inv = 1.0f / lloc;
+    for (int i = lane; i < np; i += 64) s_w[h][i] *= inv;
+    if (lane == 0 && p.lse) p.lse[(size_t)b * p.hq + hbase + h] = (mloc + __log2f(lloc)) * kLn2;
   }
-  p.out[(size_t)bh * D + d] = (h16)(O / L);
-  if (d == 0 && p.lse) p.lse[bh] = (mx + __log2f(L)) * kLn2;
+  __syncthreads();
+  for (int idx = tid; idx < p.group * D; idx += kThreads) {
+    const int h = idx / D, d = idx - h * D;
+    const size_t bh = (size_t)b * p.hq + hbase + h;
+    const float* po = p.ws_o + bh * p.n_parts_max * D + d;
+    float O = 0.f;
+    int i = 0;
+    for (; i + 8 <= np; i += 8) {
+      float t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = po[(size_t)(i + u) * D];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) O += s_w[h][i + u] * t[u];
+    }
+    for (; i < np; ++i) O += s_w[h][i] * po[(size_t)i * D];
+    p.out[bh * D + d] = (h16)O;
+  }
+}
+
+template <int D, bool FP8, int NT>
+void launch_nt(const SplitParams& sp, const AttnPlan& plan, hipStream_t s) {
+  hipLaunchKernelGGL((attn_kernel<D, FP8, NT>), dim3(plan.grid), dim3(kThreads), 0, s, sp);
+  if (plan.n_parts_max > 1)
+    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(sp.batch * sp.hkv), dim3(kThreads), 0, s, sp);
 }
 
 template <int D, bool FP8>
 hipError_t launch_impl(const SplitParams& sp, const AttnPlan& plan, hipStream_t s) {
-  if (plan.grid > 0) {
-    hipLaunchKernelGGL((attn_split_kernel<D, FP8>), dim3(plan.grid), dim3(kThreads), 0, s, sp);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  switch (plan.nt) {
+    case 2: launch_nt<D, FP8, 2>(sp, plan, s); break;
+    case 4: launch_nt<D, FP8, 4>(sp, plan, s); break;
+    default: launch_nt<D, FP8, 8>(sp, plan, s); break;
   }
-  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(sp.batch * sp.hq), dim3(D), 0, s, sp);
   return hipGetLastError();
 }
 
 }  // namespace
 
 AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int max_context) {
-  (void)hq;
   AttnPlan p{};
-  // About 128 KB of K+V per workgroup, but shrink partitions (down to 64
-  // tokens) while the whole grid would hold fewer than 1024 workgroups.
-  const int bytes_per_token = 2 * head_dim * elt_bytes;
-  int part = 64;
-  while (part * 2 * bytes_per_token <= 128 * 1024 && part * 2 <= 4096) part *= 2;
+  // NT blocks of 16 tokens per wave, 4 waves: partitions of 64 NT tokens.
+  // Eight blocks per wave (all of a wave's K and V in registers at once):
+  // the loads of a whole wave are in flight together, and contexts of up to
+  // 512 tokens need no merge pass.  Fewer only when the grid would hold fewer
+  // workgroups than CUs.
   const int mc = max_context > 0 ? max_context : 1;
-  while (part > 64 && (long)batch * hkv * ceil_div(mc, part) < 1024) part /= 2;
-  p.part = part;
-  p.n_parts_max = ceil_div(mc, part);
+  (void)elt_bytes;
+  int nt = 8;
+  while (nt > 2 && (long)batch * hkv * ceil_div(mc, 64 * nt) < 256 && ceil_div(mc, 64 * nt) > 1) nt /= 2;
+  if (ceil_div(mc, 64 * nt) > kMaxParts) nt = 8;  // callers keep max_context <= 64 * 8 * kMaxParts
+  p.nt = nt;
+  p.part = 64 * nt;
+  p.n_parts_max = ceil_div(mc, p.part);
   p.grid = batch * hkv * p.n_parts_max;
   const size_t ml = align_up((size_t)batch * hq * p.n_parts_max * sizeof(float2), 256);
   const size_t o = align_up((size_t)batch * hq * p.n_parts_max * head_dim * sizeof(float), 256);
-  p.ws_bytes = ml + o;
+  p.ws_bytes = p.n_parts_max > 1 ? ml + o : 256;
   return p;
 }
 
@@ -372,9 +417,7 @@ hipError_t launch_paged_attention(const AttnArgs& a, const AttnPlan& plan, hipSt
   const size_t ml = align_up((size_t)a.batch * a.hq * plan.n_parts_max * sizeof(float2), 256);
   sp.ws_ml = static_cast<float2*>(a.ws);
   sp.ws_o = reinterpret_cast<float*>(static_cast<char*>(a.ws) + ml);
-  if (a.head_dim == 128) {
-    return a.fp8 ? launch_impl<128, true>(sp, plan, s) : launch_impl<128, false>(sp, plan, s);
-  }
+  if (a.head_dim == 128) return a.fp8 ? launch_impl<128, true>(sp, plan, s) : launch_impl<128, false>(sp, plan, s);
   return a.fp8 ? launch_impl<64, true>(sp, plan, s) : launch_impl<64, false>(sp, plan, s);
 }
 

@@ -104,16 +104,19 @@ struct Cfg {
   static_assert(NS >= 2 && (NS - 2) * LPW < 64, "stages");
 };
 
+// Wait until at most `pending` stages (of LPW loads each) are still in flight;
+// pending in [0, NPEND] (s_waitcnt takes an immediate).
 template <int NPEND, int LPW>
 __device__ __forceinline__ void wait_stage(int pending) {
-  // pending in [0, NPEND]; s_waitcnt takes an immediate
-  if constexpr (NPEND >= 2) {
-    if (pending >= 2) { wait_vmcnt<2 * LPW>(); return; }
+  if constexpr (NPEND > 0) {
+    if (pending >= NPEND) {
+      wait_vmcnt<NPEND * LPW>();
+      return;
+    }
+    wait_stage<NPEND - 1, LPW>(pending);
+  } else {
+    wait_vmcnt<0>();
   }
-  if constexpr (NPEND >= 1) {
-    if (pending >= 1) { wait_vmcnt<LPW>(); return; }
-  }
-  wait_vmcnt<0>();
 }
 
 template <int MT, int NT, int NS, int EPI, bool NORM>
@@ -409,6 +412,7 @@ GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
   static const int kCfg[3][3] = {{GEMM_32x64, 32, 64}, {GEMM_64x128, 64, 128}, {GEMM_128x128, 128, 128}};
   GemmPlan pl{};
   for (int c = 0; c < 3; ++c) {
+    if (c > 0 && kCfg[c][1] > ceil_div(M, 32) * 32) break;  // no tile taller than the batch
     pl.cfg = kCfg[c][0];
     pl.mt = kCfg[c][1];
     pl.nt = kCfg[c][2];

@@ -113,6 +113,7 @@ static pkv_status check_meta_args(const pkv_cache* cache, int layer, const int32
   if (!bt || !lens) return fail(PKV_E_ARG, "block_tables / context_lens is NULL");
   if (batch < 1) return fail(PKV_E_ARG, "batch must be >= 1");
   if (max_context < 1) return fail(PKV_E_ARG, "max_context must be >= 1");
+  if (max_context > kAttnMaxContext) return fail(PKV_E_UNSUPPORTED, "max_context above 262144");
   if (bt_stride < ceil_div(max_context, kBlock))
     return fail(PKV_E_ARG, "bt_stride < ceil(max_context / 16)");
   return PKV_OK;

@@ -20,7 +20,8 @@ __global__ void kv_append_kernel(uint16_t* __restrict__ kpool, uint16_t* __restr
   for (int idx = threadIdx.x; idx < hkv * head_dim; idx += blockDim.x) {
     const int g = idx / head_dim, d = idx - g * head_dim;
     const size_t bg = (size_t)blk * hkv + g;
-    kpool[(bg * kBlock + slot) * head_dim + d] = k[(size_t)b * hkv * head_dim + idx];
+    // K tile [D/8][16][8]: 8-dim chunk, token, dim within the chunk
+    kpool[bg * kBlock * head_dim + (d >> 3) * (kBlock * 8) + slot * 8 + (d & 7)] = k[(size_t)b * hkv * head_dim + idx];
     vpool[(bg * head_dim + d) * kBlock + slot] = v[(size_t)b * hkv * head_dim + idx];
   }
 }

@@ -50,6 +50,7 @@ struct StepBuffers {
   void* attn_ws;
   void* gemm_ws;  // split-K partial tiles of the MFMA projections
   int* counters;  // split-K arrival counters, zeroed at the start of each call
+  int n_counters;
   size_t total;
 };
 
@@ -77,7 +78,8 @@ StepBuffers carve(const pkv_model* m, int batch, const AttnPlan& plan, void* bas
   g = std::max(g, linear_ws_bytes(batch, d.hidden, d.ffn, EPI_RESID));
   g = std::max(g, linear_ws_bytes(batch, d.vocab, d.hidden, EPI_F16));
   b.gemm_ws = take(g);
-  b.counters = reinterpret_cast<int*>(take((size_t)kGemmMaxCounters * sizeof(int)));
+  b.n_counters = kGemmMaxCounters;
+  b.counters = reinterpret_cast<int*>(take((size_t)b.n_counters * sizeof(int)));
   b.total = off;
   return b;
 }
@@ -96,6 +98,7 @@ pkv_status check_step(const pkv_model* m, const pkv_cache* cache, const int32_t*
   if (batch < 1) return fail(PKV_E_ARG, "batch must be >= 1");
   if (max_context < 1 || max_context > m->d.max_positions)
     return fail(PKV_E_ARG, "max_context must be in [1, max_positions]");
+  if (max_context > kAttnMaxContext) return fail(PKV_E_UNSUPPORTED, "max_context above 262144");
   if (bt_stride < ceil_div(max_context, kBlock)) return fail(PKV_E_ARG, "bt_stride < ceil(max_context / 16)");
   *plan = attn_plan(batch, m->d.num_q_heads, m->d.num_kv_heads, m->d.head_dim, cache_elt(cd), max_context);
   const StepBuffers need = carve(m, batch, *plan, nullptr);
@@ -165,7 +168,7 @@ hipError_t run_step(const pkv_model* m, pkv_cache* cache, const int32_t* tokens,
                     int bt_stride, const int32_t* lens, int batch, void* logits, _Float16* h,
                     const StepBuffers& sb, const AttnPlan& plan, hipStream_t s) {
   const pkv_model_desc& d = m->d;
-  hipError_t e = launch_embed(m->embed, tokens, h, batch, d.hidden, sb.counters, kGemmMaxCounters, s);
+  hipError_t e = launch_embed(m->embed, tokens, h, batch, d.hidden, sb.counters, sb.n_counters, s);
   if (e != hipSuccess) return e;
   for (int l = 0; l < d.num_layers; ++l) {
     e = run_layer(m, cache, l, h, bt, bt_stride, lens, batch, sb, plan, s);
@@ -264,7 +267,7 @@ pkv_status pkv_decode_layer(const pkv_model* m, pkv_cache* cache, int layer, voi
   if (!hidden) return fail(PKV_E_ARG, "hidden is NULL");
   if (layer < 0 || layer >= m->d.num_layers || layer >= cache->desc.num_layers)
     return fail(PKV_E_ARG, "layer out of range");
-  PKV_HIP(launch_zero_i32(sb.counters, kGemmMaxCounters, static_cast<hipStream_t>(stream)));
+  PKV_HIP(launch_zero_i32(sb.counters, sb.n_counters, static_cast<hipStream_t>(stream)));
   PKV_HIP(run_layer(m, cache, layer, static_cast<_Float16*>(hidden), bt, bt_stride, lens, batch, sb, plan,
                     static_cast<hipStream_t>(stream)));
   return PKV_OK;

@@ -54,9 +54,10 @@ __global__ void rope_append_kernel(const float* __restrict__ qkv, const float2* 
       qo[half + i] = (h16)y2;
     } else if (c > 0) {
       const int g = head - hq;
-      h16* kp = kpool + (((size_t)blk * hkv + g) * kBlock + slot) * d;
-      kp[i] = (h16)y1;
-      kp[half + i] = (h16)y2;
+      // K tile [D/8][16][8]: 8-dim chunk, token, dim within the chunk
+      h16* kp = kpool + ((size_t)blk * hkv + g) * kBlock * d + slot * 8;
+      kp[(i >> 3) * (kBlock * 8) + (i & 7)] = (h16)y1;
+      kp[((half + i) >> 3) * (kBlock * 8) + ((half + i) & 7)] = (h16)y2;
     }
   }
   if (c > 0) {

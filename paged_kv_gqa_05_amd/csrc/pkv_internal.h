@@ -11,7 +11,9 @@
 #include "../../include/pkv.h"
 
 // A paged KV cache over caller-owned device memory: per layer the K pool
-// [num_blocks][Hkv][16][D] followed by the V pool [num_blocks][Hkv][D][16].
+// followed by the V pool.  One (block, KV head) tile of K holds 16 tokens in
+// 16-byte chunks: f16 [D/8][16][8], fp8 [D/16][16][16] (dims within a chunk
+// contiguous); a V tile is dim-major [D][16].
 struct pkv_cache {
   pkv_cache_desc desc;
   char* base;
@@ -26,6 +28,7 @@ namespace pkv {
 
 constexpr int kBlock = 16;   // tokens per KV block
 constexpr int kMaxGroup = 16;  // query heads per KV head handled by one MFMA tile
+constexpr int kAttnMaxContext = 262144;  // 512 partitions of 512 tokens
 
 // Thread-local error message + status helpers (host).
 pkv_status fail(pkv_status st, const std::string& msg);
@@ -41,10 +44,11 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ---------------------------------------------------------------- attention
 struct AttnPlan {
-  int part;         // tokens per partition (multiple of 64)
+  int nt;           // 16-token blocks per wave (2, 4 or 8)
+  int part;         // tokens per partition (64 nt)
   int n_parts_max;  // partitions per (row, kv head) for max_context
-  int grid;         // workgroups of the split kernel
-  size_t ws_bytes;  // workspace bytes
+  int grid;         // workgroups of the attention kernel
+  size_t ws_bytes;  // workspace bytes (partials of multi-partition rows)
 };
 AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int max_context);
 
@@ -61,7 +65,7 @@ struct AttnArgs {
   bool fp8;
   float scale;        // softmax scale
   float k_scale, v_scale;
-  void* ws;
+  void* ws;           // partials (layout of attn_plan)
 };
 hipError_t launch_paged_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
 

@@ -13,6 +13,24 @@ def dev(a, dtype=None):
     return t.cuda()
 
 
+def k_to_lib(k):
+    """K pool [NB, Hkv, 16, D] (numpy or torch) -> the library's tile layout
+    [NB, Hkv, D/c, 16, c] with 16-byte chunks: c = 8 (f16) or 16 (fp8 codes)."""
+    nb, hkv, bs, d = k.shape
+    c = 16 if k.dtype in (np.uint8, torch.uint8) else 8
+    if isinstance(k, torch.Tensor):
+        return k.reshape(nb, hkv, bs, d // c, c).permute(0, 1, 3, 2, 4).contiguous()
+    return np.ascontiguousarray(k.reshape(nb, hkv, bs, d // c, c).transpose(0, 1, 3, 2, 4))
+
+
+def k_from_lib(k):
+    """Inverse of k_to_lib: [NB, Hkv, D/c, 16, c] -> [NB, Hkv, 16, D]."""
+    nb, hkv, nc, bs, c = k.shape
+    if isinstance(k, torch.Tensor):
+        return k.permute(0, 1, 3, 2, 4).reshape(nb, hkv, bs, nc * c)
+    return np.ascontiguousarray(k.transpose(0, 1, 3, 2, 4).reshape(nb, hkv, bs, nc * c))
+
+
 def load_case_into_cache(pkv, case, num_layers=1, layer=0, cache=None):
     """A KVCache holding the case's pools at `layer` (other layers left uninitialised)."""
     fp8 = case.k_pool.dtype == np.uint8
@@ -23,7 +41,7 @@ def load_case_into_cache(pkv, case, num_layers=1, layer=0, cache=None):
                       v_scales=[case.v_scale] * num_layers)
         cache = pkv.KVCache(num_layers, case.num_blocks, case.k_pool.shape[1], case.k_pool.shape[3], **kw)
     k, v = cache.layer(layer)
-    k.copy_(torch.from_numpy(case.k_pool))
+    k.copy_(torch.from_numpy(k_to_lib(case.k_pool)))
     v.copy_(torch.from_numpy(case.v_pool))
     return cache
 

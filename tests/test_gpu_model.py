@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import pkv_inputs as inp
-from gpu_util import dev, assert_parity, weights_to_device, oracle_config
+from gpu_util import dev, assert_parity, weights_to_device, oracle_config, k_to_lib, k_from_lib
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +23,7 @@ def _run_layer_gpu(pkv, shape, case, max_context=None):
     nb = case["num_blocks"]
     cache = pkv.KVCache(1, nb, shape.n_kv_heads, shape.head_dim)
     k, v = cache.layer(0)
-    k.copy_(torch.from_numpy(case["k_pool"]))
+    k.copy_(torch.from_numpy(k_to_lib(case["k_pool"])))
     v.copy_(torch.from_numpy(case["v_pool"]))
     b = case["hidden"].shape[0]
     mc = max_context or int(case["ctx_lens"].max())
@@ -34,7 +34,7 @@ def _run_layer_gpu(pkv, shape, case, max_context=None):
     ws = torch.empty(pkv.step_workspace_bytes(model, cache, b, mc), dtype=torch.uint8, device="cuda")
     pkv.decode_layer(model, cache, 0, hidden, dev(bt), dev(case["ctx_lens"]), mc, ws)
     torch.cuda.synchronize()
-    return hidden.cpu().numpy(), k.cpu().numpy(), v.cpu().numpy()
+    return hidden.cpu().numpy(), k_from_lib(k.cpu().numpy()), v.cpu().numpy()
 
 
 def _oracle_layer(shape, case):
