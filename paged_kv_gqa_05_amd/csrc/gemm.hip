@@ -91,7 +91,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 template <int MT, int NT, int NS, int EPI, bool NORM>
 struct Cfg {
-  static constexpr bool PAIR = (EPI == EPI_SILU);
+  static constexpr bool PAIR = epi_pair(EPI);
   static constexpr int WTM = MT / 2, WTN = NT / 2;   // wave tile
   static constexpr int FM = WTM / 16, FN = WTN / 16;  // 16 x 16 fragments per wave
   static constexpr int ROWS = MT + NT;
@@ -160,7 +160,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
       int wr;
       if (PAIR) {
         const int jj = min(nt * (NT / 2) + (t % (NT / 2)), p.n_out - 1);
-        wr = t < NT / 2 ? jj : jj + p.n_out;
+        wr = pair_row(EPI == EPI_ROPE, p.n_out, p.rope.d, jj, t >= NT / 2);
       } else {
         wr = min(nt * NT + t, p.n_out - 1);
       }
@@ -353,7 +353,11 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
           const int col = nt * (NT / 2) + wn * (NT / 4) + j * 16 + fr;
           if (col < p.n_out) {
             const float g = acc[i][j][v] * r, u = acc[i][j + FN / 2][v] * r;
-            static_cast<h16*>(p.out)[(size_t)m * p.ldo + col] = (h16)(silu(g) * u);
+            if constexpr (EPI == EPI_ROPE) {
+              rope_store(p.rope, p.bias, m, col, g, u);
+            } else {
+              static_cast<h16*>(p.out)[(size_t)m * p.ldo + col] = (h16)(silu(g) * u);
+            }
           }
         }
       } else {
@@ -362,10 +366,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
           const int col = nt * NT + wn * C::WTN + j * 16 + fr;
           if (col >= p.n_out) continue;
           float y = acc[i][j][v] * r;
-          if constexpr (EPI == EPI_F32) {
-            if (p.bias) y += (float)p.bias[col];
-            static_cast<float*>(p.out)[(size_t)m * p.ldo + col] = y;
-          } else if constexpr (EPI == EPI_F16) {
+          if constexpr (EPI == EPI_F16) {
             if (p.bias) y += (float)p.bias[col];
             static_cast<h16*>(p.out)[(size_t)m * p.ldo + col] = (h16)y;
           } else {  // EPI_RESID
@@ -408,7 +409,7 @@ hipError_t launch_epi(const GemmPlan& pl, const GemmParams& gp, bool norm, hipSt
 // re-reads the activations from L2 too often); larger weight matrices use
 // 64 x 128 (3 stages) and then 128 x 128 (2 stages: two workgroups per CU).
 GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
-  const bool pair = (epi == EPI_SILU);
+  const bool pair = epi_pair(epi);
   static const int kCfg[3][3] = {{GEMM_32x64, 32, 64}, {GEMM_64x128, 64, 128}, {GEMM_128x128, 128, 128}};
   GemmPlan pl{};
   for (int c = 0; c < 3; ++c) {
@@ -441,6 +442,7 @@ hipError_t launch_gemm(const LinArgs& a, int epi, const GemmPlan& pl, void* part
   gp.A = a.A; gp.W = a.W; gp.gain = a.gain; gp.bias = a.bias; gp.out = a.out;
   gp.M = a.M; gp.K = a.K; gp.lda = a.lda; gp.ldo = a.ldo; gp.n_out = a.n_out;
   gp.eps = a.eps;
+  gp.rope = a.rope;
   gp.n_mt = pl.n_mt; gp.n_nt = pl.n_nt; gp.splits = pl.splits; gp.kc_per_split = pl.kc_per_split;
   gp.per_xcd = ceil_div(pl.n_mt * pl.n_nt * pl.splits, 8);
   gp.counters = counters;
@@ -451,10 +453,10 @@ hipError_t launch_gemm(const LinArgs& a, int epi, const GemmPlan& pl, void* part
   }
   const bool norm = a.norm != 0;
   switch (epi) {
-    case EPI_F32: return launch_epi<EPI_F32>(pl, gp, norm, s);
     case EPI_F16: return launch_epi<EPI_F16>(pl, gp, norm, s);
     case EPI_RESID: return launch_epi<EPI_RESID>(pl, gp, norm, s);
     case EPI_SILU: return launch_epi<EPI_SILU>(pl, gp, norm, s);
+    case EPI_ROPE: return launch_epi<EPI_ROPE>(pl, gp, norm, s);
     default: return hipErrorInvalidValue;
   }
 }

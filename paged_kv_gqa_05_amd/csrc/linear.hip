@@ -11,12 +11,13 @@
 // sees whole rows of the activations), and scales the accumulator by r in the
 // epilogue.  No separate norm pass and no normalised-activation buffer.
 //
-// Epilogues: F32 (QKV: + bias, fp32 out for the RoPE/append kernel), RESID
-// (h = f16(h + y) in place: the residual add of the next norm), SILU (rows
-// [gate | up]: act = f16(silu(g) * u)), F16 (logits).
+// Epilogues: ROPE (QKV rows in rotation pairs (i, i + D/2): + bias, RoPE of
+// q and k at the row's position, q out, the new token's k and v into the
+// paged cache), RESID (h = f16(h + y) in place: the residual add of the next
+// norm), SILU (rows [gate | up]: act = f16(silu(g) * u)), F16 (logits).
 //
 // This file holds the GEMV for batch < 32: a group of LPC lanes (16, 32 or
-// 64) streams one output row of W (one gate/up pair for SILU) with 16-byte
+// 64) streams one output row of W (one row pair for SILU / ROPE) with 16-byte
 // loads and v_dot2 against every batch row, then reduces across its lanes.
 // Batches of 32 and more go to the MFMA GEMM in gemm.hip.
 #include "linear.h"
@@ -42,17 +43,16 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g));
 // Writes one output element (row m, logical column col) given the accumulators.
 template <int EPI>
 __device__ __forceinline__ void epilogue(const LinArgs& a, int m, int col, float y0, float y1) {
-  if constexpr (EPI == EPI_F32) {
-    if (a.bias) y0 += (float)a.bias[col];
-    static_cast<float*>(a.out)[(size_t)m * a.ldo + col] = y0;
-  } else if constexpr (EPI == EPI_F16) {
+  if constexpr (EPI == EPI_F16) {
     if (a.bias) y0 += (float)a.bias[col];
     static_cast<h16*>(a.out)[(size_t)m * a.ldo + col] = (h16)y0;
   } else if constexpr (EPI == EPI_RESID) {
     h16* p = static_cast<h16*>(a.out) + (size_t)m * a.ldo + col;
     *p = (h16)((float)*p + y0);
-  } else {  // EPI_SILU
+  } else if constexpr (EPI == EPI_SILU) {
     static_cast<h16*>(a.out)[(size_t)m * a.ldo + col] = (h16)(silu(y0) * y1);
+  } else {  // EPI_ROPE
+    rope_store(a.rope, a.bias, m, col, y0, y1);
   }
 }
 
@@ -60,13 +60,13 @@ __device__ __forceinline__ void epilogue(const LinArgs& a, int m, int col, float
 
 template <int LPC, int MT, int EPI>
 __global__ void __launch_bounds__(256) gemv_kernel(LinArgs a) {
-  constexpr bool PAIR = (EPI == EPI_SILU);
+  constexpr bool PAIR = epi_pair(EPI);
   const int tid = threadIdx.x;
   const int lig = tid % LPC;
   const int col = blockIdx.x * (256 / LPC) + tid / LPC;
   if (col >= a.n_out) return;  // whole lane group leaves; no block-wide barrier below
-  const h16* w0 = a.W + (size_t)col * a.K;
-  const h16* w1 = PAIR ? a.W + (size_t)(col + a.n_out) * a.K : w0;
+  const h16* w0 = a.W + (size_t)(PAIR ? pair_row(EPI == EPI_ROPE, a.n_out, a.rope.d, col, 0) : col) * a.K;
+  const h16* w1 = PAIR ? a.W + (size_t)pair_row(EPI == EPI_ROPE, a.n_out, a.rope.d, col, 1) * a.K : w0;
   float acc0[MT], acc1[MT], ss[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc0[m] = acc1[m] = ss[m] = 0.f;
@@ -142,10 +142,10 @@ size_t linear_ws_bytes(int M, int n_out, int K, int epi) {
 hipError_t launch_linear(const LinArgs& a, int epi, void* part_ws, int* counters, hipStream_t s) {
   if (a.M >= kMfmaMinBatch) return launch_gemm(a, epi, gemm_plan(a.M, a.n_out, a.K, epi), part_ws, counters, s);
   switch (epi) {
-    case EPI_F32: return gemv_dispatch<EPI_F32>(a, s);
     case EPI_F16: return gemv_dispatch<EPI_F16>(a, s);
     case EPI_RESID: return gemv_dispatch<EPI_RESID>(a, s);
     case EPI_SILU: return gemv_dispatch<EPI_SILU>(a, s);
+    case EPI_ROPE: return gemv_dispatch<EPI_ROPE>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -4,12 +4,12 @@
 // Per layer (rvLLM post on discuss.pytorch.kr, section "퓨즈드 CUDA 커널" for
 // the fused ops; section "PagedAttention과 FlashAttention-3" for the paged GQA
 // attention):
-//   1. RMSNorm(h) * w_in + QKV projection + bias          (one kernel, fp32 qkv)
-//   2. RoPE of q and k + append of k, v into the cache   (one kernel)
-//   3. paged GQA attention: split + merge                (two kernels)
-//   4. O projection + residual add into h                (one kernel)
-//   5. RMSNorm(h) * w_post + gate/up projection + SiLU*mul (one kernel)
-//   6. down projection + residual add into h             (one kernel)
+//   1. RMSNorm(h) * w_in + QKV projection + bias, RoPE of q and k, q out and
+//      the new token's k and v into the cache            (one kernel)
+//   2. paged GQA attention: split + merge                (two kernels)
+//   3. O projection + residual add into h                (one kernel)
+//   4. RMSNorm(h) * w_post + gate/up projection + SiLU*mul (one kernel)
+//   5. down projection + residual add into h             (one kernel)
 // The step adds the embedding gather before the layers and RMSNorm + LM head
 // after them.  Section "CUDA 그래프 리플레이": the forward is captured once in
 // a graph and replayed on the caller's stream; sampling (argmax) stays outside.
@@ -43,7 +43,6 @@ namespace {
 
 struct StepBuffers {
   _Float16* h;    // hidden [B][H] (when the caller gives none)
-  float* qkv;     // [B][(Hq + 2 Hkv) D]
   _Float16* q;    // [B][Hq][D]
   _Float16* o;    // [B][Hq][D]
   _Float16* act;  // [B][F]
@@ -65,14 +64,13 @@ StepBuffers carve(const pkv_model* m, int batch, const AttnPlan& plan, void* bas
   };
   StepBuffers b{};
   b.h = reinterpret_cast<_Float16*>(take((size_t)batch * d.hidden * 2));
-  b.qkv = reinterpret_cast<float*>(take((size_t)batch * (d.num_q_heads + 2 * d.num_kv_heads) * d.head_dim * 4));
   b.q = reinterpret_cast<_Float16*>(take((size_t)batch * d.num_q_heads * d.head_dim * 2));
   b.o = reinterpret_cast<_Float16*>(take((size_t)batch * d.num_q_heads * d.head_dim * 2));
   b.act = reinterpret_cast<_Float16*>(take((size_t)batch * d.ffn * 2));
   b.attn_ws = take(plan.ws_bytes);
   const int qkv_n = (d.num_q_heads + 2 * d.num_kv_heads) * d.head_dim;
   size_t g = 0;
-  g = std::max(g, linear_ws_bytes(batch, qkv_n, d.hidden, EPI_F32));
+  g = std::max(g, linear_ws_bytes(batch, qkv_n / 2, d.hidden, EPI_ROPE));
   g = std::max(g, linear_ws_bytes(batch, d.hidden, d.num_q_heads * d.head_dim, EPI_RESID));
   g = std::max(g, linear_ws_bytes(batch, d.ffn, d.hidden, EPI_SILU));
   g = std::max(g, linear_ws_bytes(batch, d.hidden, d.ffn, EPI_RESID));
@@ -122,32 +120,33 @@ hipError_t run_layer(const pkv_model* m, pkv_cache* cache, int layer, _Float16* 
 
   LinArgs a{};
   a.eps = d.rms_eps;
-  // 1. RMSNorm + QKV (+ bias) -> fp32 qkv
+  // 1. RMSNorm + QKV (+ bias) + RoPE; q out, k and v of the new token into the cache
   a.A = h; a.lda = d.hidden; a.K = d.hidden; a.M = batch;
   a.W = static_cast<const _Float16*>(w.w_qkv);
   a.gain = static_cast<const _Float16*>(w.w_in); a.norm = 1;
   a.bias = static_cast<const _Float16*>(w.b_qkv);
-  a.out = sb.qkv; a.ldo = qkv_n; a.n_out = qkv_n;
-  if ((e = launch_linear(a, EPI_F32, sb.gemm_ws, sb.counters, s)) != hipSuccess) return e;
-  // 2. RoPE + KV append
-  if ((e = launch_rope_append(sb.qkv, m->rope, sb.q, kp, vp, bt, bt_stride, lens, batch, d.num_q_heads,
-                              d.num_kv_heads, d.head_dim, s)) != hipSuccess)
-    return e;
-  // 3. paged attention
+  a.n_out = qkv_n / 2;  // rotation pairs (i, i + D/2) of every head
+  a.rope.cos_sin = static_cast<const float2*>(m->rope);
+  a.rope.lens = lens; a.rope.bt = bt; a.rope.bt_stride = bt_stride;
+  a.rope.q_out = sb.q;
+  a.rope.k_pool = static_cast<_Float16*>(kp); a.rope.v_pool = static_cast<_Float16*>(vp);
+  a.rope.hq = d.num_q_heads; a.rope.hkv = d.num_kv_heads; a.rope.d = d.head_dim;
+  if ((e = launch_linear(a, EPI_ROPE, sb.gemm_ws, sb.counters, s)) != hipSuccess) return e;
+  // 2. paged attention
   AttnArgs at{};
   at.k_pool = kp; at.v_pool = vp; at.q = sb.q; at.out = sb.o; at.lse = nullptr;
   at.bt = bt; at.bt_stride = bt_stride; at.lens = lens; at.batch = batch;
   at.hq = d.num_q_heads; at.hkv = d.num_kv_heads; at.head_dim = d.head_dim; at.fp8 = false;
   at.scale = 1.0f / std::sqrt((float)d.head_dim); at.k_scale = at.v_scale = 1.f; at.ws = sb.attn_ws;
   if ((e = launch_paged_attention(at, plan, s)) != hipSuccess) return e;
-  // 4. O projection + residual add
+  // 3. O projection + residual add
   a = LinArgs{};
   a.eps = d.rms_eps;
   a.A = sb.o; a.lda = qd; a.K = qd; a.M = batch;
   a.W = static_cast<const _Float16*>(w.w_o);
   a.out = h; a.ldo = d.hidden; a.n_out = d.hidden;
   if ((e = launch_linear(a, EPI_RESID, sb.gemm_ws, sb.counters, s)) != hipSuccess) return e;
-  // 5. RMSNorm + gate/up + SiLU*mul -> act
+  // 4. RMSNorm + gate/up + SiLU*mul -> act
   a = LinArgs{};
   a.eps = d.rms_eps;
   a.A = h; a.lda = d.hidden; a.K = d.hidden; a.M = batch;
@@ -155,7 +154,7 @@ hipError_t run_layer(const pkv_model* m, pkv_cache* cache, int layer, _Float16* 
   a.gain = static_cast<const _Float16*>(w.w_post); a.norm = 1;
   a.out = sb.act; a.ldo = d.ffn; a.n_out = d.ffn;
   if ((e = launch_linear(a, EPI_SILU, sb.gemm_ws, sb.counters, s)) != hipSuccess) return e;
-  // 6. down projection + residual add
+  // 5. down projection + residual add
   a = LinArgs{};
   a.eps = d.rms_eps;
   a.A = sb.act; a.lda = d.ffn; a.K = d.ffn; a.M = batch;

@@ -6,9 +6,6 @@ namespace pkv {
 
 hipError_t launch_embed(const void* table, const int32_t* tokens, void* h, int batch, int hidden,
                         int* zero_p, int zero_n, hipStream_t s);
-hipError_t launch_rope_append(const float* qkv, const void* cos_sin, void* q_out, void* k_pool,
-                              void* v_pool, const int32_t* bt, int bt_stride, const int32_t* lens,
-                              int batch, int hq, int hkv, int d, hipStream_t s);
 hipError_t launch_argmax(const void* logits, int batch, int vocab, int32_t* tokens, hipStream_t s);
 
 }  // namespace pkv
