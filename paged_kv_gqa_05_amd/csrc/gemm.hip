@@ -380,23 +380,17 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
 }
 
 template <int MT, int NT, int NS, int EPI>
-hipError_t launch_cfg(const GemmParams& gp, bool norm, hipStream_t s) {
-  const int total = gp.n_mt * gp.n_nt * gp.splits;
-  const int grid = gp.per_xcd * 8;
-  (void)total;
-  if (norm)
-    hipLaunchKernelGGL((gemm_kernel<MT, NT, NS, EPI, true>), dim3(grid), dim3(256), 0, s, gp);
-  else
-    hipLaunchKernelGGL((gemm_kernel<MT, NT, NS, EPI, false>), dim3(grid), dim3(256), 0, s, gp);
+hipError_t launch_cfg(const GemmParams& gp, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_kernel<MT, NT, NS, EPI, epi_norm(EPI)>), dim3(gp.per_xcd * 8), dim3(256), 0, s, gp);
   return hipGetLastError();
 }
 
 template <int EPI>
-hipError_t launch_epi(const GemmPlan& pl, const GemmParams& gp, bool norm, hipStream_t s) {
+hipError_t launch_epi(const GemmPlan& pl, const GemmParams& gp, hipStream_t s) {
   switch (pl.cfg) {
-    case GEMM_32x64: return launch_cfg<32, 64, 4, EPI>(gp, norm, s);
-    case GEMM_64x128: return launch_cfg<64, 128, 3, EPI>(gp, norm, s);
-    case GEMM_128x128: return launch_cfg<128, 128, 2, EPI>(gp, norm, s);
+    case GEMM_32x64: return launch_cfg<32, 64, 4, EPI>(gp, s);
+    case GEMM_64x128: return launch_cfg<64, 128, 3, EPI>(gp, s);
+    case GEMM_128x128: return launch_cfg<128, 128, 2, EPI>(gp, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -451,12 +445,11 @@ hipError_t launch_gemm(const LinArgs& a, int epi, const GemmPlan& pl, void* part
     gp.part_ss = reinterpret_cast<float*>(static_cast<char*>(part_ws) +
                                           align_up((size_t)pl.n_mt * pl.n_nt * pl.splits * pl.mt * pl.nt * 4, 256));
   }
-  const bool norm = a.norm != 0;
   switch (epi) {
-    case EPI_F16: return launch_epi<EPI_F16>(pl, gp, norm, s);
-    case EPI_RESID: return launch_epi<EPI_RESID>(pl, gp, norm, s);
-    case EPI_SILU: return launch_epi<EPI_SILU>(pl, gp, norm, s);
-    case EPI_ROPE: return launch_epi<EPI_ROPE>(pl, gp, norm, s);
+    case EPI_F16: return launch_epi<EPI_F16>(pl, gp, s);
+    case EPI_RESID: return launch_epi<EPI_RESID>(pl, gp, s);
+    case EPI_SILU: return launch_epi<EPI_SILU>(pl, gp, s);
+    case EPI_ROPE: return launch_epi<EPI_ROPE>(pl, gp, s);
     default: return hipErrorInvalidValue;
   }
 }

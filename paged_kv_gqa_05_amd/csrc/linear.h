@@ -10,6 +10,9 @@ enum { EPI_F16 = 0, EPI_RESID = 1, EPI_SILU = 2, EPI_ROPE = 3 };
 // Epilogues that take output rows in pairs: gate/up (row j and j + n_out) and
 // the QKV projection with RoPE (rows i and i + D/2 of one head).
 __host__ __device__ constexpr bool epi_pair(int epi) { return epi == EPI_SILU || epi == EPI_ROPE; }
+// The epilogues that follow an RMSNorm (QKV, gate/up, LM head); RESID (O and
+// down projections) never does.
+__host__ __device__ constexpr bool epi_norm(int epi) { return epi != EPI_RESID; }
 
 // What the QKV epilogue needs to rotate q and k at each row's position and to
 // store the new token's k and v in the paged cache.  RoPE (rotate-half form)

@@ -16,8 +16,8 @@
 // paged cache), RESID (h = f16(h + y) in place: the residual add of the next
 // norm), SILU (rows [gate | up]: act = f16(silu(g) * u)), F16 (logits).
 //
-// This file holds the GEMV for batch < 32: a group of LPC lanes (16, 32 or
-// 64) streams one output row of W (one row pair for SILU / ROPE) with 16-byte
+// This file holds the GEMV for batch < 32: a group of 16 to 256 lanes
+// streams one output row of W (one row pair for SILU / ROPE) with 16-byte
 // loads and v_dot2 against every batch row, then reduces across its lanes.
 // Batches of 32 and more go to the MFMA GEMM in gemm.hip.
 #include "linear.h"
@@ -58,74 +58,158 @@ __device__ __forceinline__ void epilogue(const LinArgs& a, int m, int col, float
 
 // ------------------------------------------------------------------ GEMV
 
-template <int LPC, int MT, int EPI>
+// LPR lanes per output row (pair), 16 to 256: a row spans a quarter wave up
+// to the whole 4-wave workgroup.  Lane l of the row reads the chunks
+// k = 8 l + j * 8 LPR, so every step of the row covers 16 LPR contiguous
+// bytes.  LPR is sized so that a lane's whole share of the row (at most U
+// chunks) is loaded in one go: HBM latency is hidden by the bytes each lane
+// keeps in flight, not by other waves (at batch 1 a GEMV has few waves per
+// SIMD).  The gain, activation and weight loads of an iteration are issued
+// before any is used and are unconditional (past the row end they are
+// clamped to its last chunk and masked to zero afterwards; batch rows past M
+// read row M - 1 and are never stored), because a load under a branch makes
+// the compiler drain every load in flight before it.
+template <int LPR, int MT, int U, int EPI, bool NORM>
 __global__ void __launch_bounds__(256) gemv_kernel(LinArgs a) {
   constexpr bool PAIR = epi_pair(EPI);
+  constexpr int STEP = LPR * 8;
+  constexpr int NV = PAIR ? 2 * MT : MT;  // values reduced per row
   const int tid = threadIdx.x;
-  const int lig = tid % LPC;
-  const int col = blockIdx.x * (256 / LPC) + tid / LPC;
-  if (col >= a.n_out) return;  // whole lane group leaves; no block-wide barrier below
+  const int lig = tid % LPR;
+  const int col_raw = blockIdx.x * (256 / LPR) + tid / LPR;
+  const int col = min(col_raw, a.n_out - 1);  // rows past the end compute row n_out - 1, never stored
   const h16* w0 = a.W + (size_t)(PAIR ? pair_row(EPI == EPI_ROPE, a.n_out, a.rope.d, col, 0) : col) * a.K;
   const h16* w1 = PAIR ? a.W + (size_t)pair_row(EPI == EPI_ROPE, a.n_out, a.rope.d, col, 1) * a.K : w0;
+  const h16* xrow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) xrow[m] = a.A + (size_t)min(m, a.M - 1) * a.lda;
   float acc0[MT], acc1[MT], ss[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc0[m] = acc1[m] = ss[m] = 0.f;
-  const h16x8 one = h16x8{1, 1, 1, 1, 1, 1, 1, 1};
-  for (int k = lig * 8; k < a.K; k += LPC * 8) {
-    const h16x8 wv0 = *reinterpret_cast<const h16x8*>(w0 + k);
-    h16x8 wv1;
-    if (PAIR) wv1 = *reinterpret_cast<const h16x8*>(w1 + k);
-    const h16x8 g = a.gain ? *reinterpret_cast<const h16x8*>(a.gain + k) : one;
+  const h16x8 zero = h16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  const int n_iter = (a.K + U * STEP - 1) / (U * STEP);
+  for (int it = 0; it < n_iter; ++it) {
+    const int kb = lig * 8 + it * U * STEP;
+    int kk[U];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m < a.M) {
-        const h16x8 x = *reinterpret_cast<const h16x8*>(a.A + (size_t)m * a.lda + k);
-        if (a.norm) ss[m] = dot8(x, x, ss[m]);
-        const h16x8 xg = a.gain ? x * g : x;
-        acc0[m] = dot8(wv0, xg, acc0[m]);
-        if (PAIR) acc1[m] = dot8(wv1, xg, acc1[m]);
+    for (int u = 0; u < U; ++u) kk[u] = min(kb + u * STEP, a.K - 8);
+    h16x8 gv[U], xv[U][MT], wv0[U], wv1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if constexpr (NORM) gv[u] = *reinterpret_cast<const h16x8*>(a.gain + kk[u]);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) xv[u][m] = *reinterpret_cast<const h16x8*>(xrow[m] + kk[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      wv0[u] = __builtin_nontemporal_load(reinterpret_cast<const h16x8*>(w0 + kk[u]));
+      if constexpr (PAIR) wv1[u] = __builtin_nontemporal_load(reinterpret_cast<const h16x8*>(w1 + kk[u]));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool valid = kb + u * STEP < a.K;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const h16x8 x = valid ? xv[u][m] : zero;
+        if constexpr (NORM) ss[m] = dot8(x, x, ss[m]);
+        const h16x8 xg = NORM ? x * gv[u] : x;
+        acc0[m] = dot8(valid ? wv0[u] : zero, xg, acc0[m]);
+        if constexpr (PAIR) acc1[m] = dot8(valid ? wv1[u] : zero, xg, acc1[m]);
       }
     }
   }
+  // reduce over the row's lanes: within the wave, then across waves in LDS
+  constexpr int LW = LPR < 64 ? LPR : 64;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
 #pragma unroll
-    for (int o = LPC / 2; o > 0; o >>= 1) {
+    for (int o = LW / 2; o > 0; o >>= 1) {
       acc0[m] += __shfl_xor(acc0[m], o, 64);
       if (PAIR) acc1[m] += __shfl_xor(acc1[m], o, 64);
-      if (a.norm) ss[m] += __shfl_xor(ss[m], o, 64);
+      if (NORM) ss[m] += __shfl_xor(ss[m], o, 64);
     }
   }
+  if constexpr (LPR > 64) {
+    constexpr int WPR = LPR / 64;  // waves per row
+    __shared__ float red[4][NV + MT];
+    const int wave = tid >> 6, lane = tid & 63;
+    if (lane == 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        red[wave][m] = acc0[m];
+        if (PAIR) red[wave][MT + m] = acc1[m];
+        if (NORM) red[wave][NV + m] = ss[m];
+      }
+    }
+    __syncthreads();
+    if (wave % WPR) return;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      acc0[m] = acc1[m] = ss[m] = 0.f;
+#pragma unroll
+      for (int w = 0; w < WPR; ++w) {
+        acc0[m] += red[wave + w][m];
+        if (PAIR) acc1[m] += red[wave + w][MT + m];
+        if (NORM) ss[m] += red[wave + w][NV + m];
+      }
+    }
+  }
+  if (col_raw >= a.n_out) return;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    if (m < a.M && (m % LPC) == lig) {
-      const float r = a.norm ? rsqrtf(ss[m] / (float)a.K + a.eps) : 1.0f;
+    if (m < a.M && (m % LW) == lig) {
+      const float r = NORM ? rsqrtf(ss[m] / (float)a.K + a.eps) : 1.0f;
       epilogue<EPI>(a, m, col, acc0[m] * r, acc1[m] * r);
     }
   }
 }
 
-template <int LPC, int EPI>
+// Batch buckets: MT rows, U steps per iteration with MT * U <= 32 activation
+// chunks held in registers (U_MAX at MT = 1).
+template <int LPR, int EPI, bool NORM, int U_MAX>
 hipError_t gemv_dispatch_mt(const LinArgs& a, hipStream_t s) {
-  const int grid = (a.n_out + 256 / LPC - 1) / (256 / LPC);
-#define PKV_GEMV(MT_) \
-  hipLaunchKernelGGL((gemv_kernel<LPC, MT_, EPI>), dim3(grid), dim3(256), 0, s, a)
-  if (a.M <= 1) PKV_GEMV(1);
-  else if (a.M <= 2) PKV_GEMV(2);
-  else if (a.M <= 4) PKV_GEMV(4);
-  else if (a.M <= 8) PKV_GEMV(8);
-  else if (a.M <= 16) PKV_GEMV(16);
-  else PKV_GEMV(32);
+  const int grid = (a.n_out + 256 / LPR - 1) / (256 / LPR);
+#define PKV_GEMV(MT_, U_) \
+  hipLaunchKernelGGL((gemv_kernel<LPR, MT_, U_, EPI, NORM>), dim3(grid), dim3(256), 0, s, a)
+  if (a.M <= 1) PKV_GEMV(1, U_MAX);
+  else if (a.M <= 2) PKV_GEMV(2, U_MAX);
+  else if (a.M <= 4) PKV_GEMV(4, U_MAX);
+  else if (a.M <= 8) PKV_GEMV(8, (U_MAX < 4 ? U_MAX : 4));
+  else if (a.M <= 16) PKV_GEMV(16, (U_MAX < 2 ? U_MAX : 2));
+  else PKV_GEMV(32, 1);
 #undef PKV_GEMV
   return hipGetLastError();
 }
 
+template <int LPR, int EPI>
+hipError_t gemv_dispatch_lpr(const LinArgs& a, hipStream_t s) {
+  constexpr bool NORM = epi_norm(EPI);
+  // steps a lane of this row width needs, rounded up to 2, 4 or 8
+  const int steps = (a.K / 8 + LPR - 1) / LPR;
+  if (steps <= 2) return gemv_dispatch_mt<LPR, EPI, NORM, 2>(a, s);
+  if (steps <= 4) return gemv_dispatch_mt<LPR, EPI, NORM, 4>(a, s);
+  return gemv_dispatch_mt<LPR, EPI, NORM, 8>(a, s);
+}
+
+// Lanes per row: enough that a lane's share of the row is at most 8 chunks,
+// then more while the grid is under 512 workgroups.
+int gemv_lanes_per_row(int n_out, int K) {
+  const int chunks = K / 8;
+  int lpr = 16;
+  while (lpr < 256 && chunks > 8 * lpr) lpr *= 2;
+  while (lpr < 256 && (long)n_out * lpr / 256 < 512 && chunks >= 2 * lpr) lpr *= 2;
+  return lpr;
+}
+
 template <int EPI>
 hipError_t gemv_dispatch(const LinArgs& a, hipStream_t s) {
-  // fewest lanes per row that still gives >= 512 workgroups
-  if ((long)a.n_out * 16 / 256 >= 512) return gemv_dispatch_mt<16, EPI>(a, s);
-  if ((long)a.n_out * 32 / 256 >= 512) return gemv_dispatch_mt<32, EPI>(a, s);
-  return gemv_dispatch_mt<64, EPI>(a, s);
+  switch (gemv_lanes_per_row(a.n_out, a.K)) {
+    case 16: return gemv_dispatch_lpr<16, EPI>(a, s);
+    case 32: return gemv_dispatch_lpr<32, EPI>(a, s);
+    case 64: return gemv_dispatch_lpr<64, EPI>(a, s);
+    case 128: return gemv_dispatch_lpr<128, EPI>(a, s);
+    default: return gemv_dispatch_lpr<256, EPI>(a, s);
+  }
 }
 
 }  // namespace
@@ -140,6 +224,8 @@ size_t linear_ws_bytes(int M, int n_out, int K, int epi) {
 }
 
 hipError_t launch_linear(const LinArgs& a, int epi, void* part_ws, int* counters, hipStream_t s) {
+  if (epi < EPI_F16 || epi > EPI_ROPE || (a.norm != 0) != epi_norm(epi) || (a.norm && !a.gain))
+    return hipErrorInvalidValue;
   if (a.M >= kMfmaMinBatch) return launch_gemm(a, epi, gemm_plan(a.M, a.n_out, a.K, epi), part_ws, counters, s);
   switch (epi) {
     case EPI_F16: return gemv_dispatch<EPI_F16>(a, s);

@@ -11,6 +11,8 @@ from gpu_util import dev, assert_parity, weights_to_device, oracle_config, k_to_
 pytestmark = pytest.mark.gpu
 
 MID = inp.Shape(hidden=512, n_q_heads=12, n_kv_heads=2, head_dim=128, ffn=1408, vocab=1000, n_layers=2)
+# FFN wide enough that the down projection spreads a row over a whole workgroup
+WIDE = inp.Shape(hidden=512, n_q_heads=12, n_kv_heads=2, head_dim=128, ffn=4096, vocab=1000, n_layers=2)
 
 
 def _layer_case(shape, batch, seed, lo=1, hi=64):
@@ -49,6 +51,11 @@ def _oracle_layer(shape, case):
     (inp.TINY, 40, 1011, 64),      # MFMA path, ragged last M tile
     (MID, 3, 1021, 300),           # D = 128, G = 6
     (MID, 70, 1031, 200),          # MFMA path at D = 128
+    (MID, 1, 1051, 300),           # GEMV batch buckets 1, 2, 16 and 32
+    (MID, 2, 1061, 300),
+    (MID, 12, 1071, 100),
+    (MID, 31, 1081, 100),
+    (WIDE, 2, 1091, 100),          # 256 lanes per row, cross-wave reduction
 ])
 def test_decode_layer_parity(lib, shape, batch, seed, hi):
     case = _layer_case(shape, batch, seed, hi=hi)
