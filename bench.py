@@ -163,8 +163,7 @@ def time_attention(pkv, torch, w, n_pools, rounds, seed):
     out = torch.empty_like(q)
     bt_d = torch.from_numpy(bt).cuda()
     lens_d = torch.from_numpy(lens).cuda()
-    ws = torch.empty(pkv.attn_workspace_bytes(cache, w.batch, w.n_q_heads, mc), dtype=torch.uint8,
-                     device="cuda")
+    ws = pkv.attn_workspace(cache, w.batch, w.n_q_heads, mc)
     scale = 1.0 / math.sqrt(w.head_dim)
 
     def call(layer):

@@ -122,7 +122,10 @@ pkv_status pkv_kv_append(pkv_cache* cache, int layer, const void* k, const void*
 
 /* ----------------------------------------------------------------- attention */
 
-/* Scratch bytes paged_attn_decode needs for this shape (host only). */
+/* Scratch bytes paged_attn_decode needs for this shape (host only).  The
+ * workspace must be zero-filled once before its first use (e.g. hipMemset);
+ * every call leaves it in a state valid for the next call, of any shape that
+ * fits it. */
 pkv_status pkv_attn_workspace_bytes(const pkv_cache* cache, int batch, int num_q_heads,
                                     int max_context, size_t* bytes);
 
@@ -135,11 +138,13 @@ pkv_status pkv_attn_workspace_bytes(const pkv_cache* cache, int batch, int num_q
  *   layer's scales).  Accumulation is fp32; out is f16 [batch][Hq][D]; q is f16
  *   [batch][Hq][D].  lse (nullable, f32 [batch][Hq]) receives max s +
  *   ln(sum exp(s - max s)) (-inf for inactive rows).  The context is split into
- *   partitions processed in parallel and merged in a second pass (fixed
- *   order, so results are deterministic); workspace (>=
- *   pkv_attn_workspace_bytes, 256-byte aligned) holds the partial results and
- *   needs no initialisation.  bt_stride >= ceil(max_context / 16); every
- *   context_lens[b] <= max_context <= 262144 (PKV_E_UNSUPPORTED above). */
+ *   partitions processed in parallel; the last partition of a row to finish
+ *   merges them all in partition order (so results are deterministic).
+ *   workspace (>= pkv_attn_workspace_bytes, 256-byte aligned, zero-filled
+ *   before its first use) holds per-(row, KV head) arrival counters, which
+ *   every call returns to zero, and the partial results.  Two calls in flight
+ *   at once must not share a workspace.  bt_stride >= ceil(max_context / 16);
+ *   every context_lens[b] <= max_context <= 262144 (PKV_E_UNSUPPORTED above). */
 pkv_status pkv_paged_attn_decode(const pkv_cache* cache, int layer, const void* q, void* out,
                                  float* lse, const int32_t* block_tables, int bt_stride,
                                  const int32_t* context_lens, int batch, int num_q_heads,

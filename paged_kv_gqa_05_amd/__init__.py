@@ -106,6 +106,12 @@ def attn_workspace_bytes(cache, batch, num_q_heads, max_context):
     return n.value
 
 
+def attn_workspace(cache, batch, num_q_heads, max_context, device="cuda"):
+    """A zero-filled attention workspace (its arrival counters must start at zero)."""
+    return torch.zeros(attn_workspace_bytes(cache, batch, num_q_heads, max_context), dtype=torch.uint8,
+                       device=device)
+
+
 def paged_attn_decode(cache, layer, q, out, block_tables, context_lens, max_context, scale,
                       workspace, lse=None, stream=None):
     _need(q, torch.float16, "q")

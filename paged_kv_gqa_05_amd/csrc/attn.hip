@@ -1,5 +1,5 @@
-// Paged GQA decode attention for gfx950: split over the context with the merge
-// of the partitions fused into the same kernel.
+// Paged GQA decode attention for gfx950: split over the context, with the
+// merge of a row's partitions done by the last of them to finish.
 //
 // What it computes (rvLLM post on discuss.pytorch.kr, section
 // "PagedAttention과 FlashAttention-3": block-table KV cache, GQA reads each KV
@@ -30,14 +30,17 @@
 //    which cost more than the loads).  The four waves' (max, sum, O) are
 //    combined through LDS.
 //  * A row with a single partition writes its normalised f16 output directly.
-//    Otherwise each partition stores (max, sum, unnormalised O) in fp32 and a
-//    merge kernel combines them in partition order (deterministic; launched
-//    only when some row can span more than one partition).  Nothing is
-//    zero-filled.
+//    Otherwise each partition stores (max, sum, unnormalised O) in fp32 with
+//    device-coherent stores and counts its arrival on a per-(row, KV head)
+//    counter; the workgroup that arrives last merges all partitions of the
+//    row in partition order (so the result does not depend on arrival order),
+//    writes the output and resets the counter to zero.  One kernel, no merge
+//    launch; the counters are zero before and after every call.
 //  * FP8 E4M3 codes are converted to f16 in registers with the gfx950
 //    conversion instruction (exact: every E4M3 value is an f16 value); the
 //    per-tensor K scale is folded into the score scale and the V scale into
 //    the output.
+#include "coherent.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -53,9 +56,8 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLog2e = 1.44269504088896341f;
-// Partitions per (row, KV head) the merge kernel can hold (kMaxGroup x
-// kMaxParts weights in LDS).
-constexpr int kMaxParts = 512;
+// Partitions the merge reads per round trip.
+constexpr int kMergeBatch = 8;
 
 struct SplitParams {
   const unsigned char* k_pool;
@@ -65,6 +67,7 @@ struct SplitParams {
   float* lse;
   const int* bt;
   const int* lens;
+  int* counters;   // [B][Hkv] partitions arrived (zero between calls)
   float2* ws_ml;   // [B][Hq][P] (max, sum) per partition
   float* ws_o;     // [B][Hq][P][D] unnormalised O per partition
   int bt_stride;
@@ -275,91 +278,97 @@ __global__ void __launch_bounds__(kThreads) attn_kernel(SplitParams p) {
   }
   __syncthreads();
 
-  const bool single = (np == 1);
-  for (int idx = tid; idx < p.group * D; idx += kThreads) {
-    const int h = idx / D, d = idx - h * D;
-    float mw[kWaves];
+  const size_t bh0 = (size_t)b * p.hq + hbase;
+  if (np == 1) {
+    for (int idx = tid; idx < p.group * D; idx += kThreads) {
+      const int h = idx / D, d = idx - h * D;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, s_m[w][h]);
+      float L = 0.f, O = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float e = __builtin_amdgcn_exp2f(s_m[w][h] - mx);  // 0 for a wave without tokens
+        L += s_l[w][h] * e;
+        O += s_o[w][h][d] * e;
+      }
+      p.out[(bh0 + h) * D + d] = (h16)(O * p.v_scale / L);
+      if (d == 0 && p.lse) p.lse[bh0 + h] = (mx + __log2f(L)) * kLn2;
+    }
+    return;
+  }
+
+  // ---- this partition's (max, sum, O) per head, four dims per thread
+  for (int idx = tid; idx < p.group * (D / 4); idx += kThreads) {
+    const int h = idx / (D / 4), d = 4 * (idx - h * (D / 4));
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      mw[w] = s_m[w][h];
-      mx = fmaxf(mx, mw[w]);
-    }
-    float L = 0.f, O = 0.f;
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, s_m[w][h]);
+    float L = 0.f;
+    f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float e = __builtin_amdgcn_exp2f(mw[w] - mx);  // 0 for a wave without tokens
+      const float e = __builtin_amdgcn_exp2f(s_m[w][h] - mx);
       L += s_l[w][h] * e;
-      O += s_o[w][h][d] * e;
+      O += *reinterpret_cast<const f32x4*>(&s_o[w][h][d]) * e;
     }
-    const size_t bh = (size_t)b * p.hq + hbase + h;
-    if (single) {
-      p.out[bh * D + d] = (h16)(O * p.v_scale / L);
-      if (d == 0 && p.lse) p.lse[bh] = (mx + __log2f(L)) * kLn2;
-    } else {  // read by the merge kernel after this kernel has finished
-      const size_t slot = bh * p.n_parts_max + part_idx;
-      p.ws_o[slot * D + d] = O * p.v_scale;
-      if (d == 0) p.ws_ml[slot] = make_float2(mx, L);
-    }
+    const size_t slot = (bh0 + h) * p.n_parts_max + part_idx;
+    st_agent(p.ws_o + slot * D + d, O * p.v_scale);
+    if (d == 0) st_agent2(p.ws_ml + slot, make_float2(mx, L));
   }
-}
-
-// Merge of the partitions of rows with more than one: one workgroup per
-// (row, KV head); per-partition weights exp2(m_i - M) / L in LDS, then
-// O = sum_i w_i O_i in partition order with independent loads.
-template <int D>
-__global__ void __launch_bounds__(kThreads) attn_merge_kernel(SplitParams p) {
-  __shared__ float s_w[kMaxGroup][kMaxParts];
-  const int bg = blockIdx.x;
-  const int b = bg / p.hkv, g = bg - b * p.hkv;
-  const int c = p.lens[b];
-  const int np = (c + p.part - 1) / p.part;
-  if (np <= 1) return;  // written by the attention kernel (or an inactive row)
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hbase = g * p.group;
-  for (int h = wave; h < p.group; h += kWaves) {
-    const float2* ml = p.ws_ml + ((size_t)b * p.hq + hbase + h) * p.n_parts_max;
-    float mloc = -INFINITY;
-    for (int i = lane; i < np; i += 64) mloc = fmaxf(mloc, ml[i].x);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o, 64));
-    float lloc = 0.f;
-    for (int i = lane; i < np; i += 64) {
-      const float2 v = ml[i];
-      const float e = __builtin_amdgcn_exp2f(v.x - mloc);
-      s_w[h][i] = e;
-      lloc += v.y * e;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o, 64);
-    const float inv = 1.0f / lloc;
-    for (int i = lane; i < np; i += 64) s_w[h][i] *= inv;
-    if (lane == 0 && p.lse) p.lse[(size_t)b * p.hq + hbase + h] = (mloc + __log2f(lloc)) * kLn2;
-  }
+  wait_vmcnt<0>();  // this thread's partial has reached the coherent level
+  __shared__ int s_last;
   __syncthreads();
-  for (int idx = tid; idx < p.group * D; idx += kThreads) {
-    const int h = idx / D, d = idx - h * D;
-    const size_t bh = (size_t)b * p.hq + hbase + h;
-    const float* po = p.ws_o + bh * p.n_parts_max * D + d;
-    float O = 0.f;
-    int i = 0;
-    for (; i + 8 <= np; i += 8) {
-      float t[8];
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(p.counters + bg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- last partition of the row to finish: merge all np in partition order
+  if (tid == 0) __hip_atomic_store(p.counters + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int idx = tid; idx < p.group * (D / 4); idx += kThreads) {
+    const int h = idx / (D / 4), d = 4 * (idx - h * (D / 4));
+    const size_t base = (bh0 + h) * p.n_parts_max;
+    float M = -INFINITY, L = 0.f;
+    f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i0 = 0; i0 < np; i0 += kMergeBatch) {
+      // the (max, sum) and O of kMergeBatch partitions in flight together
+      float2 ml[kMergeBatch];
+      f32x4 po[kMergeBatch];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) t[u] = po[(size_t)(i + u) * D];
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const size_t slot = base + min(i0 + u, np - 1);
+        ml[u] = ld_agent2(p.ws_ml + slot);
+        po[u] = ld_agent(p.ws_o + slot * D + d);
+      }
+      float mn = M;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) O += s_w[h][i + u] * t[u];
+      for (int u = 0; u < kMergeBatch; ++u)
+        if (i0 + u < np) mn = fmaxf(mn, ml[u].x);
+      const float r = __builtin_amdgcn_exp2f(M - mn);  // 0 on the first batch (M = -inf)
+      L *= r;
+      O *= r;
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        if (i0 + u < np) {
+          const float e = __builtin_amdgcn_exp2f(ml[u].x - mn);
+          L += ml[u].y * e;
+          O += po[u] * e;
+        }
+      }
+      M = mn;
     }
-    for (; i < np; ++i) O += s_w[h][i] * po[(size_t)i * D];
-    p.out[bh * D + d] = (h16)O;
+    const float inv = 1.0f / L;
+    h16* o = p.out + (bh0 + h) * D + d;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) o[v] = (h16)(O[v] * inv);
+    if (d == 0 && p.lse) p.lse[bh0 + h] = (M + __log2f(L)) * kLn2;
   }
 }
 
 template <int D, bool FP8, int NT>
 void launch_nt(const SplitParams& sp, const AttnPlan& plan, hipStream_t s) {
   hipLaunchKernelGGL((attn_kernel<D, FP8, NT>), dim3(plan.grid), dim3(kThreads), 0, s, sp);
-  if (plan.n_parts_max > 1)
-    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(sp.batch * sp.hkv), dim3(kThreads), 0, s, sp);
 }
 
 template <int D, bool FP8>
@@ -379,20 +388,20 @@ AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int 
   // NT blocks of 16 tokens per wave, 4 waves: partitions of 64 NT tokens.
   // Eight blocks per wave (all of a wave's K and V in registers at once):
   // the loads of a whole wave are in flight together, and contexts of up to
-  // 512 tokens need no merge pass.  Fewer only when the grid would hold fewer
+  // 512 tokens need no merge.  Fewer only when the grid would hold fewer
   // workgroups than CUs.
   const int mc = max_context > 0 ? max_context : 1;
   (void)elt_bytes;
   int nt = 8;
   while (nt > 2 && (long)batch * hkv * ceil_div(mc, 64 * nt) < 256 && ceil_div(mc, 64 * nt) > 1) nt /= 2;
-  if (ceil_div(mc, 64 * nt) > kMaxParts) nt = 8;  // callers keep max_context <= 64 * 8 * kMaxParts
   p.nt = nt;
   p.part = 64 * nt;
   p.n_parts_max = ceil_div(mc, p.part);
   p.grid = batch * hkv * p.n_parts_max;
+  p.counter_bytes = align_up((size_t)batch * hkv * sizeof(int), 256);
   const size_t ml = align_up((size_t)batch * hq * p.n_parts_max * sizeof(float2), 256);
   const size_t o = align_up((size_t)batch * hq * p.n_parts_max * head_dim * sizeof(float), 256);
-  p.ws_bytes = p.n_parts_max > 1 ? ml + o : 256;
+  p.ws_bytes = p.counter_bytes + (p.n_parts_max > 1 ? ml + o : 0);
   return p;
 }
 
@@ -415,8 +424,10 @@ hipError_t launch_paged_attention(const AttnArgs& a, const AttnPlan& plan, hipSt
   sp.scale_log2 = a.scale * kLog2e * (a.fp8 ? a.k_scale : 1.0f);
   sp.v_scale = a.fp8 ? a.v_scale : 1.0f;
   const size_t ml = align_up((size_t)a.batch * a.hq * plan.n_parts_max * sizeof(float2), 256);
-  sp.ws_ml = static_cast<float2*>(a.ws);
-  sp.ws_o = reinterpret_cast<float*>(static_cast<char*>(a.ws) + ml);
+  char* ws = static_cast<char*>(a.ws);
+  sp.counters = reinterpret_cast<int*>(ws);
+  sp.ws_ml = reinterpret_cast<float2*>(ws + plan.counter_bytes);
+  sp.ws_o = reinterpret_cast<float*>(ws + plan.counter_bytes + ml);
   if (a.head_dim == 128) return a.fp8 ? launch_impl<128, true>(sp, plan, s) : launch_impl<128, false>(sp, plan, s);
   return a.fp8 ? launch_impl<64, true>(sp, plan, s) : launch_impl<64, false>(sp, plan, s);
 }

@@ -28,6 +28,7 @@
 //  * Tile order is XCD-aware: the hardware deals workgroups round-robin over
 //    the 8 XCDs; each XCD takes a contiguous range of tiles, M tiles fastest,
 //    so the M tiles that share a weight tile share one L2.
+#include "coherent.h"
 #include "linear.h"
 
 namespace pkv {
@@ -64,30 +65,6 @@ __device__ __forceinline__ void load_to_lds(const void* g, const _Float16* lds) 
 // Workgroup barrier without the memory fence of __syncthreads (which would
 // wait for every outstanding global load).
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
-
-// Split-K partials cross XCDs, whose L2 caches are not coherent with each
-// other.  They are written and read with agent-scope relaxed atomics (sc1:
-// coherent at device scope without flushing or invalidating the whole L2,
-// which a device-scope fence would do once per workgroup).
-__device__ __forceinline__ void st_agent(float* p, f32x4 v) {
-  uint64_t* q = reinterpret_cast<uint64_t*>(p);
-  __hip_atomic_store(q, __builtin_bit_cast(uint64_t, float2{v[0], v[1]}), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, __builtin_bit_cast(uint64_t, float2{v[2], v[3]}), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ f32x4 ld_agent(const float* p) {
-  uint64_t* q = const_cast<uint64_t*>(reinterpret_cast<const uint64_t*>(p));
-  const float2 a = __builtin_bit_cast(float2, __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  const float2 b = __builtin_bit_cast(float2, __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  return f32x4{a.x, a.y, b.x, b.y};
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 template <int MT, int NT, int NS, int EPI, bool NORM>
 struct Cfg {

@@ -46,9 +46,11 @@ struct StepBuffers {
   _Float16* q;    // [B][Hq][D]
   _Float16* o;    // [B][Hq][D]
   _Float16* act;  // [B][F]
-  void* attn_ws;
+  void* attn_ws;  // attention workspace; starts with its arrival counters
   void* gemm_ws;  // split-K partial tiles of the MFMA projections
-  int* counters;  // split-K arrival counters, zeroed at the start of each call
+  int* counters;  // split-K arrival counters, followed directly by the
+                  // attention counters: n_counters ints zeroed at the start
+                  // of each call
   int n_counters;
   size_t total;
 };
@@ -67,7 +69,6 @@ StepBuffers carve(const pkv_model* m, int batch, const AttnPlan& plan, void* bas
   b.q = reinterpret_cast<_Float16*>(take((size_t)batch * d.num_q_heads * d.head_dim * 2));
   b.o = reinterpret_cast<_Float16*>(take((size_t)batch * d.num_q_heads * d.head_dim * 2));
   b.act = reinterpret_cast<_Float16*>(take((size_t)batch * d.ffn * 2));
-  b.attn_ws = take(plan.ws_bytes);
   const int qkv_n = (d.num_q_heads + 2 * d.num_kv_heads) * d.head_dim;
   size_t g = 0;
   g = std::max(g, linear_ws_bytes(batch, qkv_n / 2, d.hidden, EPI_ROPE));
@@ -76,8 +77,10 @@ StepBuffers carve(const pkv_model* m, int batch, const AttnPlan& plan, void* bas
   g = std::max(g, linear_ws_bytes(batch, d.hidden, d.ffn, EPI_RESID));
   g = std::max(g, linear_ws_bytes(batch, d.vocab, d.hidden, EPI_F16));
   b.gemm_ws = take(g);
-  b.n_counters = kGemmMaxCounters;
-  b.counters = reinterpret_cast<int*>(take((size_t)b.n_counters * sizeof(int)));
+  static_assert(kGemmMaxCounters * sizeof(int) % 256 == 0, "attention counters follow the GEMM counters");
+  b.counters = reinterpret_cast<int*>(take((size_t)kGemmMaxCounters * sizeof(int)));
+  b.attn_ws = take(plan.ws_bytes);
+  b.n_counters = kGemmMaxCounters + (int)(plan.counter_bytes / sizeof(int));
   b.total = off;
   return b;
 }

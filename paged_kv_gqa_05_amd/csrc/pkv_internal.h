@@ -48,7 +48,9 @@ struct AttnPlan {
   int part;         // tokens per partition (64 nt)
   int n_parts_max;  // partitions per (row, kv head) for max_context
   int grid;         // workgroups of the attention kernel
-  size_t ws_bytes;  // workspace bytes (partials of multi-partition rows)
+  size_t counter_bytes;  // leading workspace bytes: [B][Hkv] int arrival counters,
+                         // zero before the first call, left zero by every call
+  size_t ws_bytes;  // workspace bytes (counters + partials of multi-partition rows)
 };
 AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int max_context);
 

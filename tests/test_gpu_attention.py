@@ -11,14 +11,15 @@ from gpu_util import dev, load_case_into_cache, assert_parity, k_from_lib
 pytestmark = pytest.mark.gpu
 
 
-def run_attention(pkv, case, max_context=None, cache=None, with_lse=True):
+def run_attention(pkv, case, max_context=None, cache=None, with_lse=True, ws=None):
     cache = load_case_into_cache(pkv, case, cache=cache)
     mc = max_context or case.max_context
     b, hq, d = case.q.shape
     q = dev(case.q)
     out = torch.empty_like(q)
     lse = torch.empty(b, hq, dtype=torch.float32, device="cuda") if with_lse else None
-    ws = torch.empty(pkv.attn_workspace_bytes(cache, b, hq, mc), dtype=torch.uint8, device="cuda")
+    if ws is None:
+        ws = pkv.attn_workspace(cache, b, hq, mc)
     bt = case.block_tables
     if bt.shape[1] * 16 < mc:
         bt = np.concatenate([bt, np.full((b, (mc + 15) // 16 - bt.shape[1]), -1, np.int32)], axis=1)
@@ -140,6 +141,21 @@ def test_split_plan_invariance(lib):
     a, _ = run_attention(lib, case)
     b, _ = run_attention(lib, case, max_context=32768)
     np.testing.assert_allclose(a.astype(np.float64), b.astype(np.float64), atol=1e-3, rtol=1e-3)
+
+
+def test_workspace_reused_across_calls(lib):
+    """One workspace for consecutive calls of different shapes: the arrival
+    counters at its head are back to zero after every call, and every call
+    matches the oracle."""
+    big = inp.attention_case(7, 12, 2, 128, 300, 2100, seed=18)
+    small = inp.attention_case(3, 12, 2, 128, 1, 1500, seed=19)
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")
+    for case in (big, small, big):
+        out, _ = run_attention(lib, case, ws=ws)
+        ref, _ = oracle_attention(case)
+        assert_parity(out, ref, "workspace reuse")
+        n_counter_bytes = case.q.shape[0] * 2 * 4
+        assert not ws[:n_counter_bytes].any().item()
 
 
 def test_inactive_rows(lib):
