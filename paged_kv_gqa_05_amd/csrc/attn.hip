@@ -8,12 +8,12 @@
 // with K_t, V_t gathered through the row's block table.
 //
 // Design (MI355X, not the pages' FlashAttention-3 kernels):
-//  * One workgroup (4 waves) per (row b, KV head g, partition of 64 NT tokens),
-//    blockIdx = (b * Hkv + g) * P + partition; partitions beyond a row's
-//    context exit at once.  The row's block-table entries and the query rows
-//    are loaded together with the context length, so a workgroup waits one
-//    memory round trip before its KV loads.
-//  * Wave w of a partition owns its blocks w, w + 4, ... (at most NT) and loads
+//  * One workgroup of W waves (4 or 8) per (row b, KV head g, partition of
+//    16 NT W tokens), blockIdx = (b * Hkv + g) * P + partition; partitions
+//    beyond a row's context exit at once.  The row's block-table entries and
+//    the query rows are loaded together with the context length, so a
+//    workgroup waits one memory round trip before its KV loads.
+//  * Wave w of a partition owns its blocks w, w + W, ... (at most NT) and loads
 //    all of their K and V at once.  K blocks are stored in 16-byte chunks of
 //    8 dims x 16 tokens (fp8: 16 dims), so each K load instruction of a wave
 //    reads 1 KB of contiguous memory; V blocks are dim-major [D][16].
@@ -27,7 +27,7 @@
 //  * Softmax per wave in two passes over registers: all scores first, one max
 //    per head, then P = exp2(S - max) and the PV products with no rescaling
 //    (an online softmax rescales the 32 output accumulators at every block,
-//    which cost more than the loads).  The four waves' (max, sum, O) are
+//    which cost more than the loads).  The W waves' (max, sum, O) are
 //    combined through LDS.
 //  * A row with a single partition writes its normalised f16 output directly.
 //    Otherwise each partition stores (max, sum, unnormalised O) in fp32 with
@@ -52,8 +52,6 @@ typedef h16 h16x4 __attribute__((ext_vector_type(4)));
 typedef h16 h16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLog2e = 1.44269504088896341f;
 // Partitions the merge reads per round trip.
@@ -150,8 +148,9 @@ struct Tile<D, true> {
   __device__ __forceinline__ h16x4 vfrag(int j) const { return e4m3x4_to_h16x4(v[j]); }
 };
 
-template <int D, bool FP8, int NT>
-__global__ void __launch_bounds__(kThreads) attn_kernel(SplitParams p) {
+template <int D, bool FP8, int NT, int kWaves>
+__global__ void __launch_bounds__(64 * kWaves) attn_kernel(SplitParams p) {
+  constexpr int kThreads = 64 * kWaves;
   // padded LDS row (floats) for the combine of the four waves
   constexpr int OSTR = D + 4;
   __shared__ float s_o[kWaves][kMaxGroup][OSTR];
@@ -366,17 +365,21 @@ __global__ void __launch_bounds__(kThreads) attn_kernel(SplitParams p) {
   }
 }
 
-template <int D, bool FP8, int NT>
-void launch_nt(const SplitParams& sp, const AttnPlan& plan, hipStream_t s) {
-  hipLaunchKernelGGL((attn_kernel<D, FP8, NT>), dim3(plan.grid), dim3(kThreads), 0, s, sp);
+template <int D, bool FP8, int NT, int W>
+void launch_cfg(const SplitParams& sp, const AttnPlan& plan, hipStream_t s) {
+  hipLaunchKernelGGL((attn_kernel<D, FP8, NT, W>), dim3(plan.grid), dim3(64 * W), 0, s, sp);
 }
 
 template <int D, bool FP8>
 hipError_t launch_impl(const SplitParams& sp, const AttnPlan& plan, hipStream_t s) {
-  switch (plan.nt) {
-    case 2: launch_nt<D, FP8, 2>(sp, plan, s); break;
-    case 4: launch_nt<D, FP8, 4>(sp, plan, s); break;
-    default: launch_nt<D, FP8, 8>(sp, plan, s); break;
+  if (plan.waves == 8) {
+    launch_cfg<D, FP8, 8, 8>(sp, plan, s);
+  } else {
+    switch (plan.nt) {
+      case 2: launch_cfg<D, FP8, 2, 4>(sp, plan, s); break;
+      case 4: launch_cfg<D, FP8, 4, 4>(sp, plan, s); break;
+      default: launch_cfg<D, FP8, 8, 4>(sp, plan, s); break;
+    }
   }
   return hipGetLastError();
 }
@@ -385,17 +388,30 @@ hipError_t launch_impl(const SplitParams& sp, const AttnPlan& plan, hipStream_t 
 
 AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int max_context) {
   AttnPlan p{};
-  // NT blocks of 16 tokens per wave, 4 waves: partitions of 64 NT tokens.
-  // Eight blocks per wave (all of a wave's K and V in registers at once):
-  // the loads of a whole wave are in flight together, and contexts of up to
-  // 512 tokens need no merge.  Fewer only when the grid would hold fewer
-  // workgroups than CUs.
+  // A workgroup of W waves takes one partition of 16 NT W tokens; every wave
+  // holds the K and V of its NT blocks in registers (NT = 8 at most).
+  // Partitions of one row are merged through memory (coherent stores, an
+  // arrival atomic and a re-read by the last one), which lengthens the
+  // critical path, so partitions are as large as possible while every
+  // workgroup of the call can still be resident at once: 8 waves x 8 blocks
+  // (1024 tokens; one workgroup per CU) when the partitions fit in one
+  // round of 256 workgroups and a row can exceed 512 tokens, else 4 waves x
+  // 8 blocks (512 tokens; two per CU, which keeps one loading while the other
+  // merges when the call needs several rounds).  Fewer blocks per wave only
+  // when the grid would hold fewer workgroups than CUs.  The estimate uses
+  // max_context for every row.
   const int mc = max_context > 0 ? max_context : 1;
+  const long rows = (long)batch * hkv;
   (void)elt_bytes;
-  int nt = 8;
-  while (nt > 2 && (long)batch * hkv * ceil_div(mc, 64 * nt) < 256 && ceil_div(mc, 64 * nt) > 1) nt /= 2;
+  int waves = 4, nt = 8;
+  if (mc > 512 && rows * ceil_div(mc, 1024) <= 256) {
+    waves = 8;
+  } else {
+    while (nt > 2 && rows * ceil_div(mc, 64 * nt) < 256 && ceil_div(mc, 64 * nt) > 1) nt /= 2;
+  }
+  p.waves = waves;
   p.nt = nt;
-  p.part = 64 * nt;
+  p.part = 16 * nt * waves;
   p.n_parts_max = ceil_div(mc, p.part);
   p.grid = batch * hkv * p.n_parts_max;
   p.counter_bytes = align_up((size_t)batch * hkv * sizeof(int), 256);

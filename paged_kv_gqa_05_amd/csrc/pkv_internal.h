@@ -44,8 +44,9 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ---------------------------------------------------------------- attention
 struct AttnPlan {
+  int waves;        // waves per workgroup (4 or 8)
   int nt;           // 16-token blocks per wave (2, 4 or 8)
-  int part;         // tokens per partition (64 nt)
+  int part;         // tokens per partition (16 nt waves)
   int n_parts_max;  // partitions per (row, kv head) for max_context
   int grid;         // workgroups of the attention kernel
   size_t counter_bytes;  // leading workspace bytes: [B][Hkv] int arrival counters,
