@@ -41,10 +41,13 @@
  *   [num_blocks][Hkv] tiles of 16 tokens:
  *     K tile, f16: [D/8][BS][8]   element (t, d) at ((d/8)*BS + t)*8 + d%8
  *     K tile, fp8: [D/16][BS][16] element (t, d) at ((d/16)*BS + t)*16 + d%16
- *     V tile (both): [D][BS]      element (t, d) at d*BS + t
- *   (16-byte chunks of one token's dims, so a wave reads a K tile with
- *   contiguous 1 KB loads; V dim-major).  Element size 2 bytes (f16) or 1 byte
- *   (fp8 codes).  Token t of sequence b is in block
+ *     V tile, f16: [D][BS]        element (t, d) at d*BS + t
+ *     V tile, fp8: [D/64][4][16][4][4]  element (t, d) at
+ *                  (((d/64)*4 + t/4)*16 + d%16)*16 + ((d/16)%4)*4 + t%4
+ *   (K: 16-byte chunks of one token's dims, so a wave reads a K tile with
+ *   contiguous 1 KB loads; f16 V dim-major; fp8 V in 16-byte chunks holding
+ *   4 tokens x dims d, d+16, d+32, d+48, again read in contiguous 1 KB
+ *   loads).  Element size 2 bytes (f16) or 1 byte (fp8 codes).  Token t of sequence b is in block
  *   block_tables[b * bt_stride + t / BS], slot t % BS.
  *   context_lens[b] counts the cached tokens INCLUDING the token being decoded:
  *   the new token's K/V go to position pos = context_lens[b] - 1 and attention

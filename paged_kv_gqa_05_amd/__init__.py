@@ -72,7 +72,9 @@ class KVCache:
 
     def layer(self, layer):
         """Views of one layer's pools in the library layout (include/pkv.h):
-        K [NB, Hkv, D/c, 16, c] with c = 8 (f16) or 16 (fp8), V [NB, Hkv, D, 16]."""
+        K [NB, Hkv, D/c, 16, c] with c = 8 (f16) or 16 (fp8); V [NB, Hkv, D, 16]
+        (f16) or [NB, Hkv, D/64, 4, 16, 4, 4] (fp8: dim group, token quad, dim
+        in group, dim step of 16, token in quad)."""
         k, v = C.c_void_p(), C.c_void_p()
         _check(_lib.pkv_kv_cache_layer(self.handle, layer, C.byref(k), C.byref(v)))
         tdt = torch.uint8 if self.dtype == KV_FP8_E4M3 else torch.float16
@@ -83,6 +85,8 @@ class KVCache:
         vt = self.mem[v.value - base:v.value - base + n].view(tdt)
         nb, hkv, d = self.num_blocks, self.num_kv_heads, self.head_dim
         c = 16 if self.dtype == KV_FP8_E4M3 else 8
+        if self.dtype == KV_FP8_E4M3:
+            return kt.view(nb, hkv, d // c, BLOCK_SIZE, c), vt.view(nb, hkv, d // 64, 4, 16, 4, 4)
         return kt.view(nb, hkv, d // c, BLOCK_SIZE, c), vt.view(nb, hkv, d, BLOCK_SIZE)
 
     def close(self):

@@ -31,6 +31,24 @@ def k_from_lib(k):
     return np.ascontiguousarray(k.transpose(0, 1, 3, 2, 4).reshape(nb, hkv, bs, nc * c))
 
 
+def v_to_lib(v):
+    """V pool [NB, Hkv, D, 16] (numpy) -> the library's tile layout: unchanged
+    for f16; fp8 codes [NB, Hkv, D/64, 4, 16, 4, 4] where dim d = 64 jj + 16 r + n
+    and token t = 4 q4 + tt sit at [jj, q4, n, r, tt]."""
+    if v.dtype != np.uint8:
+        return v
+    nb, hkv, d, bs = v.shape
+    return np.ascontiguousarray(v.reshape(nb, hkv, d // 64, 4, 16, 4, 4).transpose(0, 1, 2, 5, 4, 3, 6))
+
+
+def v_from_lib(v):
+    """Inverse of v_to_lib for fp8 views [NB, Hkv, D/64, 4, 16, 4, 4]."""
+    if v.ndim == 4:
+        return v
+    nb, hkv, ng = v.shape[:3]
+    return np.ascontiguousarray(v.transpose(0, 1, 2, 5, 4, 3, 6).reshape(nb, hkv, ng * 64, 16))
+
+
 def load_case_into_cache(pkv, case, num_layers=1, layer=0, cache=None):
     """A KVCache holding the case's pools at `layer` (other layers left uninitialised)."""
     fp8 = case.k_pool.dtype == np.uint8
@@ -42,7 +60,7 @@ def load_case_into_cache(pkv, case, num_layers=1, layer=0, cache=None):
         cache = pkv.KVCache(num_layers, case.num_blocks, case.k_pool.shape[1], case.k_pool.shape[3], **kw)
     k, v = cache.layer(layer)
     k.copy_(torch.from_numpy(k_to_lib(case.k_pool)))
-    v.copy_(torch.from_numpy(case.v_pool))
+    v.copy_(torch.from_numpy(v_to_lib(case.v_pool)))
     return cache
 
 
