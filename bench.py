@@ -18,6 +18,7 @@ on the host cores on a bounded sample.
     python bench.py [--gpus 1] [--steps 32] [--warmup 5]
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -191,6 +192,25 @@ def time_attention(pkv, torch, w, n_pools, rounds, seed):
             "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "rotated_pools": n_pools}
 
 
+def attention_traffic():
+    """HBM bytes per attn15 launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs (scaled by a device copy of known size), or None when the
+    attention kernel's sources have changed since the counters were taken."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    try:
+        text = open(os.path.join(here, "profiles", "paged_attention_attn15_counters.txt")).read()
+        fields = dict(l.split(": ", 1) for l in text.splitlines() if l.startswith(("traffic_", "sources_")))
+        h = hashlib.sha256()
+        for f in ("attn.hip", "coherent.h", "pkv_internal.h"):
+            with open(os.path.join(here, "paged_kv_gqa_05_amd", "csrc", f), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest() != fields["sources_sha256"].strip():
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 # ---------------------------------------------------------- CPU oracle leg
 
 def cpu_baseline(torch, weights, shape, batch_sample, ctx):
@@ -299,12 +319,13 @@ def main():
     a = attn.get("attn15")
     roofline = None
     if a:
-        roofline = {"bound": "hbm", "kernel": "paged attention (split + merge), 1.5B layer shape",
+        roofline = {"bound": "hbm", "kernel": "paged attention (split + fused merge, one kernel), "
+                                              "attn15: 1.5B layer shape, batch 64, contexts U[128, 2048]",
                     "achieved": round(a["GBs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(a["GBs"] / HBM_PEAK_GBS, 4), "traffic": None}
+                    "frac": round(a["GBs"] / HBM_PEAK_GBS, 4), "traffic": attention_traffic()}
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(torch, weights, shape, 4, args.prompt)
+        cpu = cpu_baseline(torch, weights, shape, head, args.prompt)
         log(f"cpu oracle: {cpu['value']:.3f} tok/s ({cpu['sample']})")
 
     line = {
