@@ -68,6 +68,7 @@ __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "m
 
 template <int MT, int NT, int NS, int EPI, bool NORM>
 struct Cfg {
+  static constexpr int LDS_STAGES = NS;
   static constexpr bool PAIR = epi_pair(EPI);
   static constexpr int WTM = MT / 2, WTN = NT / 2;   // wave tile
   static constexpr int FM = WTM / 16, FN = WTN / 16;  // 16 x 16 fragments per wave
@@ -79,6 +80,18 @@ struct Cfg {
   static_assert(ROWS % 32 == 0 && FM >= 1 && FN >= 1, "tile shape");
   static_assert(!PAIR || (FN % 2 == 0), "paired tiles need an even fragment count");
   static_assert(NS >= 2 && (NS - 2) * LPW < 64, "stages");
+};
+
+// LDS stores of this wave complete, then the workgroup barrier (no wait on
+// the global loads still in flight, unlike __syncthreads).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0) only
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int V>
+struct Tag {
+  static constexpr int value = V;
 };
 
 // Wait until at most `pending` stages (of LPW loads each) are still in flight;
@@ -96,9 +109,15 @@ __device__ __forceinline__ void wait_stage(int pending) {
   }
 }
 
-template <int MT, int NT, int NS, int EPI, bool NORM>
+// REG = false: stages go global -> LDS directly (global_load_lds_dwordx4), NS
+// of them in LDS.  REG = true: each lane loads the same 16-byte chunk into
+// registers (plain global_load_dwordx4, twice the L2 throughput of the
+// direct-to-LDS path on gfx950) two stages ahead and writes it to the same
+// LDS slot with ds_write_b128; NS = 2 LDS buffers.
+template <int MT, int NT, int NS, int EPI, bool NORM, bool REG>
 __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   using C = Cfg<MT, NT, NS, EPI, NORM>;
+  static_assert(!REG || NS == 2, "register staging uses two LDS buffers");
   constexpr bool PAIR = C::PAIR;
   constexpr int FM = C::FM, FN = C::FN;
   __shared__ __attribute__((aligned(1024))) h16 smem[NS * C::STAGE];
@@ -186,18 +205,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
     wrow_t[j] = MT + t + fr;
   }
 
-  // ---- main loop: NS - 1 stages in flight
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < n_iter) issue(s);
-
-  for (int it = 0; it < n_iter; ++it) {
-    const int pending = min(n_iter - 1, it + NS - 2) - it;
-    wait_stage<NS - 2, C::LPW>(pending);
-    barrier_only();
-    if (it + NS - 1 < n_iter) issue(it + NS - 1);
-
-    const h16* sb = smem + (it % NS) * C::STAGE;
+  auto compute = [&](int it) {
+    const h16* sb = smem + (it % C::LDS_STAGES) * C::STAGE;
     const int kbase = (kc0 + it) * BK;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -229,6 +238,70 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], wf[j], acc[i][j], 0, 0, 0);
     }
+  };
+
+  if constexpr (!REG) {
+    // ---- NS - 1 stages in flight, direct to LDS
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < n_iter) issue(s);
+    for (int it = 0; it < n_iter; ++it) {
+      const int pending = min(n_iter - 1, it + NS - 2) - it;
+      wait_stage<NS - 2, C::LPW>(pending);
+      barrier_only();
+      if (it + NS - 1 < n_iter) issue(it + NS - 1);
+      compute(it);
+    }
+  } else {
+    // ---- two stages in registers, two LDS buffers.  Stage s is loaded into
+    // rg[s & 1]; the loop is unrolled by two so the index is a constant.
+    h16x8 rg[2][C::LPW];
+    auto load_regs = [&](int it, h16x8* r) {
+      const int kbase = (kc0 + it) * BK;
+      const int k = min(kbase + 8 * lchunk, kmax);
+#pragma unroll
+      for (int j = 0; j < C::LPS; ++j) r[j] = *reinterpret_cast<const h16x8*>(src[j] + k);
+      if constexpr (NORM) {  // every lane loads (no branch); lanes 0-7 store
+        const int kg = min(kbase + 8 * (lane & 7), kmax);
+        r[C::LPS] = *reinterpret_cast<const h16x8*>(p.gain + kg);
+      }
+    };
+    auto write_lds = [&](int it, const h16x8* r) {
+      h16* sb = smem + (it & 1) * C::STAGE;
+#pragma unroll
+      for (int j = 0; j < C::LPS; ++j) *reinterpret_cast<h16x8*>(sb + (4 * j + wave) * 8 * BK + lane * 8) = r[j];
+      if constexpr (NORM) {
+        if (lane < 8) *reinterpret_cast<h16x8*>(sb + C::GAIN_OFF + wave * BK + lane * 8) = r[C::LPS];
+      }
+    };
+    load_regs(0, rg[0]);
+    if (n_iter > 1) {
+      load_regs(1, rg[1]);
+      wait_vmcnt<C::LPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    write_lds(0, rg[0]);
+    lds_barrier();
+    if (n_iter > 2) load_regs(2, rg[0]);
+    // iteration it: compute stage it, then move stage it + 1 from registers
+    // to LDS and start loading stage it + 3 into the registers it freed
+    auto step = [&](int it, auto par) {
+      constexpr int Q = 1 - decltype(par)::value;  // parity of stage it + 1
+      compute(it);
+      if (it + 1 < n_iter) {
+        if (it + 2 < n_iter) wait_vmcnt<C::LPW>(); else wait_vmcnt<0>();
+        write_lds(it + 1, rg[Q]);
+        lds_barrier();
+        if (it + 3 < n_iter) load_regs(it + 3, rg[Q]);
+      }
+    };
+    int it = 0;
+    for (; it + 1 < n_iter; it += 2) {
+      step(it, Tag<0>{});
+      step(it + 1, Tag<1>{});
+    }
+    if (it < n_iter) step(it, Tag<0>{});
   }
 
   // ---- sum(h^2) per activation row: reduce the four k-groups of a row
@@ -315,50 +388,111 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds column fr of each fragment, rows 4 fg + v
+  // ---- epilogue: lane holds column fr of each fragment, rows 4 fg + v.
+  // Every load the epilogue needs is issued before its first store: a load
+  // cannot be moved above a store to a possibly aliasing pointer, so an
+  // interleaved load-modify-store costs one memory round trip per element.
+  int mrow[FM][4];
+  bool mok[FM][4];
+  float rs[FM][4];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int ml = wm * C::WTM + i * 16 + 4 * fg + v;
-      const int m = m0 + ml;
-      if (m >= p.M) continue;
-      const float r = NORM ? s_ss[ml] : 1.0f;
-      if constexpr (PAIR) {
+      mok[i][v] = m0 + ml < p.M;
+      mrow[i][v] = min(m0 + ml, p.M - 1);
+      rs[i][v] = NORM ? s_ss[ml] : 1.0f;
+    }
+  if constexpr (EPI == EPI_ROPE) {
+    constexpr int FP = FN / 2;  // pair fragments
+    int pc[FP];
+    bool pok[FP];
+#pragma unroll
+    for (int j = 0; j < FP; ++j) {
+      const int col = nt * (NT / 2) + wn * (NT / 4) + j * 16 + fr;
+      pok[j] = col < p.n_out;
+      pc[j] = min(col, p.n_out - 1);
+    }
+    RopeRow rr[FM][4];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) rr[i][v] = rope_row_len(p.rope, mrow[i][v]);
+    float2 bias[FP];
+#pragma unroll
+    for (int j = 0; j < FP; ++j) bias[j] = rope_bias(p.rope, p.bias, pc[j]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) rope_row_blk(p.rope, mrow[i][v], rr[i][v]);
+    float2 cs[FM][4][FP];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int j = 0; j < FP; ++j) cs[i][v][j] = rope_cs(p.rope, rr[i][v], pc[j]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int j = 0; j < FP; ++j)
+          if (mok[i][v] && pok[j])
+            rope_put(p.rope, rr[i][v], mrow[i][v], pc[j], acc[i][j][v] * rs[i][v] + bias[j].x,
+                     acc[i][j + FP][v] * rs[i][v] + bias[j].y, cs[i][v][j]);
+  } else if constexpr (EPI == EPI_SILU) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int j = 0; j < FN / 2; ++j) {
           const int col = nt * (NT / 2) + wn * (NT / 4) + j * 16 + fr;
-          if (col < p.n_out) {
-            const float g = acc[i][j][v] * r, u = acc[i][j + FN / 2][v] * r;
-            if constexpr (EPI == EPI_ROPE) {
-              rope_store(p.rope, p.bias, m, col, g, u);
-            } else {
-              static_cast<h16*>(p.out)[(size_t)m * p.ldo + col] = (h16)(silu(g) * u);
-            }
+          if (mok[i][v] && col < p.n_out) {
+            const float g = acc[i][j][v] * rs[i][v], u = acc[i][j + FN / 2][v] * rs[i][v];
+            static_cast<h16*>(p.out)[(size_t)mrow[i][v] * p.ldo + col] = (h16)(silu(g) * u);
           }
         }
-      } else {
+  } else {
+    int cc[FN];
+    bool cok[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = nt * NT + wn * C::WTN + j * 16 + fr;
+      cok[j] = col < p.n_out;
+      cc[j] = min(col, p.n_out - 1);
+    }
+    // EPI_F16: the bias of each column; EPI_RESID: the residual h itself
+    float add[FM][4][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const int col = nt * NT + wn * C::WTN + j * 16 + fr;
-          if (col >= p.n_out) continue;
-          float y = acc[i][j][v] * r;
-          if constexpr (EPI == EPI_F16) {
-            if (p.bias) y += (float)p.bias[col];
-            static_cast<h16*>(p.out)[(size_t)m * p.ldo + col] = (h16)y;
-          } else {  // EPI_RESID
-            h16* o = static_cast<h16*>(p.out) + (size_t)m * p.ldo + col;
-            *o = (h16)((float)*o + y);
-          }
+          if constexpr (EPI == EPI_F16)
+            add[i][v][j] = p.bias ? (float)p.bias[cc[j]] : 0.f;
+          else
+            add[i][v][j] = (float)static_cast<const h16*>(p.out)[(size_t)mrow[i][v] * p.ldo + cc[j]];
         }
-      }
-    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if (mok[i][v] && cok[j])
+            static_cast<h16*>(p.out)[(size_t)mrow[i][v] * p.ldo + cc[j]] =
+                (h16)(acc[i][j][v] * rs[i][v] + add[i][v][j]);
   }
 }
 
-template <int MT, int NT, int NS, int EPI>
+template <int MT, int NT, int NS, int EPI, bool REG = false>
 hipError_t launch_cfg(const GemmParams& gp, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<MT, NT, NS, EPI, epi_norm(EPI)>), dim3(gp.per_xcd * 8), dim3(256), 0, s, gp);
+  hipLaunchKernelGGL((gemm_kernel<MT, NT, NS, EPI, epi_norm(EPI), REG>), dim3(gp.per_xcd * 8), dim3(256), 0, s,
+                     gp);
   return hipGetLastError();
 }
 

@@ -41,38 +41,69 @@ __device__ __forceinline__ int pair_row(int epi_rope, int n_out, int head_dim, i
   return p + (second ? n_out : 0);
 }
 
-// QKV epilogue for pair p of batch row m: y0, y1 are rows i and i + D/2 of a
-// head (norm applied, bias not yet added).
-__device__ __forceinline__ void rope_store(const RopeArgs& ra, const _Float16* bias, int m, int p, float y0,
-                                           float y1) {
+// The QKV epilogue in three steps, so that a kernel can issue every load of
+// its tile before the first store (a load cannot be moved above a store to a
+// possibly aliasing pointer, and each such pair would cost a memory round
+// trip): the row's context length, then its position's block id and the
+// (cos, sin) of each pair, then stores only.
+struct RopeRow {
+  int c, pos, blk;
+};
+__device__ __forceinline__ RopeRow rope_row_len(const RopeArgs& ra, int m) {
+  RopeRow r;
+  r.c = ra.lens[m];
+  r.pos = r.c > 0 ? r.c - 1 : 0;
+  r.blk = 0;
+  return r;
+}
+__device__ __forceinline__ void rope_row_blk(const RopeArgs& ra, int m, RopeRow& r) {
+  r.blk = r.c > 0 ? ra.bt[(size_t)m * ra.bt_stride + r.pos / 16] : 0;
+}
+__device__ __forceinline__ float2 rope_cs(const RopeArgs& ra, const RopeRow& r, int p) {
+  const int half = ra.d >> 1;
+  return ra.cos_sin[(size_t)r.pos * half + p % half];
+}
+// Pair p of batch row m: y0, y1 are rows i and i + D/2 of a head with the
+// norm and the bias applied.  Rotates q and k heads at the row's position,
+// writes q, and stores the new token's k and v in the paged cache.
+__device__ __forceinline__ void rope_put(const RopeArgs& ra, const RopeRow& r, int m, int p, float y0, float y1,
+                                         float2 cs) {
   const int half = ra.d >> 1;
   const int head = p / half, i = p - head * half;
-  if (bias) {
-    y0 += (float)bias[head * ra.d + i];
-    y1 += (float)bias[head * ra.d + half + i];
-  }
-  const int c = ra.lens[m];
-  const int pos = c > 0 ? c - 1 : 0;
   if (head < ra.hq + ra.hkv) {
-    const float2 cs = ra.cos_sin[(size_t)pos * half + i];
     const float o0 = y0 * cs.x - y1 * cs.y;
     const float o1 = y1 * cs.x + y0 * cs.y;
     if (head < ra.hq) {
       _Float16* q = ra.q_out + ((size_t)m * ra.hq + head) * ra.d;
       q[i] = (_Float16)o0;
       q[half + i] = (_Float16)o1;
-    } else if (c > 0) {  // K tile [D/8][16][8]
-      const int blk = ra.bt[(size_t)m * ra.bt_stride + pos / 16];
-      _Float16* kp = ra.k_pool + ((size_t)blk * ra.hkv + (head - ra.hq)) * 16 * ra.d + (pos % 16) * 8;
+    } else if (r.c > 0) {  // K tile [D/8][16][8]
+      _Float16* kp = ra.k_pool + ((size_t)r.blk * ra.hkv + (head - ra.hq)) * 16 * ra.d + (r.pos % 16) * 8;
       kp[(i >> 3) * 128 + (i & 7)] = (_Float16)o0;
       kp[((half + i) >> 3) * 128 + ((half + i) & 7)] = (_Float16)o1;
     }
-  } else if (c > 0) {  // V tile [D][16]
-    const int blk = ra.bt[(size_t)m * ra.bt_stride + pos / 16];
-    _Float16* vp = ra.v_pool + ((size_t)blk * ra.hkv + (head - ra.hq - ra.hkv)) * ra.d * 16 + (pos % 16);
+  } else if (r.c > 0) {  // V tile [D][16]
+    _Float16* vp = ra.v_pool + ((size_t)r.blk * ra.hkv + (head - ra.hq - ra.hkv)) * ra.d * 16 + (r.pos % 16);
     vp[i * 16] = (_Float16)y0;
     vp[(half + i) * 16] = (_Float16)y1;
   }
+}
+// The pair's two bias values (0 without bias).
+__device__ __forceinline__ float2 rope_bias(const RopeArgs& ra, const _Float16* bias, int p) {
+  if (!bias) return make_float2(0.f, 0.f);
+  const int half = ra.d >> 1;
+  const int head = p / half, i = p - head * half;
+  return make_float2((float)bias[head * ra.d + i], (float)bias[head * ra.d + half + i]);
+}
+
+// All three steps for one pair (y0, y1 with the norm applied, bias not yet).
+__device__ __forceinline__ void rope_store(const RopeArgs& ra, const _Float16* bias, int m, int p, float y0,
+                                           float y1) {
+  RopeRow r = rope_row_len(ra, m);
+  rope_row_blk(ra, m, r);
+  const float2 cs = rope_cs(ra, r, p);
+  const float2 b = rope_bias(ra, bias, p);
+  rope_put(ra, r, m, p, y0 + b.x, y1 + b.y, cs);
 }
 
 // Batches at or above this size use the MFMA GEMM; smaller ones the GEMV.
