@@ -68,7 +68,6 @@ __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "m
 
 template <int MT, int NT, int NS, int EPI, bool NORM>
 struct Cfg {
-  static constexpr int LDS_STAGES = NS;
   static constexpr bool PAIR = epi_pair(EPI);
   static constexpr int WTM = MT / 2, WTN = NT / 2;   // wave tile
   static constexpr int FM = WTM / 16, FN = WTN / 16;  // 16 x 16 fragments per wave
@@ -80,18 +79,6 @@ struct Cfg {
   static_assert(ROWS % 32 == 0 && FM >= 1 && FN >= 1, "tile shape");
   static_assert(!PAIR || (FN % 2 == 0), "paired tiles need an even fragment count");
   static_assert(NS >= 2 && (NS - 2) * LPW < 64, "stages");
-};
-
-// LDS stores of this wave complete, then the workgroup barrier (no wait on
-// the global loads still in flight, unlike __syncthreads).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0) only
-  asm volatile("s_barrier" ::: "memory");
-}
-
-template <int V>
-struct Tag {
-  static constexpr int value = V;
 };
 
 // Wait until at most `pending` stages (of LPW loads each) are still in flight;
@@ -109,15 +96,9 @@ __device__ __forceinline__ void wait_stage(int pending) {
   }
 }
 
-// REG = false: stages go global -> LDS directly (global_load_lds_dwordx4), NS
-// of them in LDS.  REG = true: each lane loads the same 16-byte chunk into
-// registers (plain global_load_dwordx4, twice the L2 throughput of the
-// direct-to-LDS path on gfx950) two stages ahead and writes it to the same
-// LDS slot with ds_write_b128; NS = 2 LDS buffers.
-template <int MT, int NT, int NS, int EPI, bool NORM, bool REG>
+template <int MT, int NT, int NS, int EPI, bool NORM>
 __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   using C = Cfg<MT, NT, NS, EPI, NORM>;
-  static_assert(!REG || NS == 2, "register staging uses two LDS buffers");
   constexpr bool PAIR = C::PAIR;
   constexpr int FM = C::FM, FN = C::FN;
   __shared__ __attribute__((aligned(1024))) h16 smem[NS * C::STAGE];
@@ -206,7 +187,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   }
 
   auto compute = [&](int it) {
-    const h16* sb = smem + (it % C::LDS_STAGES) * C::STAGE;
+    const h16* sb = smem + (it % NS) * C::STAGE;
     const int kbase = (kc0 + it) * BK;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -240,68 +221,16 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
     }
   };
 
-  if constexpr (!REG) {
-    // ---- NS - 1 stages in flight, direct to LDS
+  // ---- main loop: NS - 1 stages in flight
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-      if (s < n_iter) issue(s);
-    for (int it = 0; it < n_iter; ++it) {
-      const int pending = min(n_iter - 1, it + NS - 2) - it;
-      wait_stage<NS - 2, C::LPW>(pending);
-      barrier_only();
-      if (it + NS - 1 < n_iter) issue(it + NS - 1);
-      compute(it);
-    }
-  } else {
-    // ---- two stages in registers, two LDS buffers.  Stage s is loaded into
-    // rg[s & 1]; the loop is unrolled by two so the index is a constant.
-    h16x8 rg[2][C::LPW];
-    auto load_regs = [&](int it, h16x8* r) {
-      const int kbase = (kc0 + it) * BK;
-      const int k = min(kbase + 8 * lchunk, kmax);
-#pragma unroll
-      for (int j = 0; j < C::LPS; ++j) r[j] = *reinterpret_cast<const h16x8*>(src[j] + k);
-      if constexpr (NORM) {  // every lane loads (no branch); lanes 0-7 store
-        const int kg = min(kbase + 8 * (lane & 7), kmax);
-        r[C::LPS] = *reinterpret_cast<const h16x8*>(p.gain + kg);
-      }
-    };
-    auto write_lds = [&](int it, const h16x8* r) {
-      h16* sb = smem + (it & 1) * C::STAGE;
-#pragma unroll
-      for (int j = 0; j < C::LPS; ++j) *reinterpret_cast<h16x8*>(sb + (4 * j + wave) * 8 * BK + lane * 8) = r[j];
-      if constexpr (NORM) {
-        if (lane < 8) *reinterpret_cast<h16x8*>(sb + C::GAIN_OFF + wave * BK + lane * 8) = r[C::LPS];
-      }
-    };
-    load_regs(0, rg[0]);
-    if (n_iter > 1) {
-      load_regs(1, rg[1]);
-      wait_vmcnt<C::LPW>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    write_lds(0, rg[0]);
-    lds_barrier();
-    if (n_iter > 2) load_regs(2, rg[0]);
-    // iteration it: compute stage it, then move stage it + 1 from registers
-    // to LDS and start loading stage it + 3 into the registers it freed
-    auto step = [&](int it, auto par) {
-      constexpr int Q = 1 - decltype(par)::value;  // parity of stage it + 1
-      compute(it);
-      if (it + 1 < n_iter) {
-        if (it + 2 < n_iter) wait_vmcnt<C::LPW>(); else wait_vmcnt<0>();
-        write_lds(it + 1, rg[Q]);
-        lds_barrier();
-        if (it + 3 < n_iter) load_regs(it + 3, rg[Q]);
-      }
-    };
-    int it = 0;
-    for (; it + 1 < n_iter; it += 2) {
-      step(it, Tag<0>{});
-      step(it + 1, Tag<1>{});
-    }
-    if (it < n_iter) step(it, Tag<0>{});
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < n_iter) issue(s);
+  for (int it = 0; it < n_iter; ++it) {
+    const int pending = min(n_iter - 1, it + NS - 2) - it;
+    wait_stage<NS - 2, C::LPW>(pending);
+    barrier_only();
+    if (it + NS - 1 < n_iter) issue(it + NS - 1);
+    compute(it);
   }
 
   // ---- sum(h^2) per activation row: reduce the four k-groups of a row
@@ -489,10 +418,9 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   }
 }
 
-template <int MT, int NT, int NS, int EPI, bool REG = false>
+template <int MT, int NT, int NS, int EPI>
 hipError_t launch_cfg(const GemmParams& gp, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<MT, NT, NS, EPI, epi_norm(EPI), REG>), dim3(gp.per_xcd * 8), dim3(256), 0, s,
-                     gp);
+  hipLaunchKernelGGL((gemm_kernel<MT, NT, NS, EPI, epi_norm(EPI)>), dim3(gp.per_xcd * 8), dim3(256), 0, s, gp);
   return hipGetLastError();
 }
 
