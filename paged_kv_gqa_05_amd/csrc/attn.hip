@@ -158,8 +158,16 @@ struct Tile<D, true> {
   }
 };
 
+// Waves per SIMD each configuration is compiled for (register budget
+// 512 / n): 4 waves x NT <= 4 keeps three workgroups per CU resident, which
+// the plan's residency estimate relies on; the others hold one.
+template <int NT, int W>
+constexpr int attn_min_waves() {
+  return (W == 4 && NT <= 4) ? 3 : 1;
+}
+
 template <int D, bool FP8, int NT, int kWaves>
-__global__ void __launch_bounds__(64 * kWaves) attn_kernel(SplitParams p) {
+__global__ void __launch_bounds__(64 * kWaves, (attn_min_waves<NT, kWaves>())) attn_kernel(SplitParams p) {
   constexpr int kThreads = 64 * kWaves;
   // padded LDS row (floats) for the combine of the four waves
   constexpr int OSTR = D + 4;
@@ -403,21 +411,26 @@ AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int 
   // Partitions of one row are merged through memory (coherent stores, an
   // arrival atomic and a re-read by the last one), which lengthens the
   // critical path, so partitions are as large as possible while every
-  // workgroup of the call can still be resident at once: 8 waves x 8 blocks
-  // (1024 tokens; one workgroup per CU) when the partitions fit in one
-  // round of 256 workgroups and a row can exceed 512 tokens, else 4 waves x
-  // 8 blocks (512 tokens; two per CU, which keeps one loading while the other
-  // merges when the call needs several rounds).  Fewer blocks per wave only
-  // when the grid would hold fewer workgroups than CUs.  The estimate uses
-  // max_context for every row.
+  // workgroup of the call can still be resident at once:
+  //  * 8 waves x 8 blocks (1024 tokens, one workgroup per CU) when a row can
+  //    exceed 512 tokens and the partitions fit in 256 workgroups;
+  //  * else 4 waves x 8 blocks (512 tokens, one per CU: 296 registers at f16);
+  //  * else, when those exceed 256 workgroups, 4 waves x 4 blocks (256
+  //    tokens, three per CU) if that fits in 768;
+  //  * calls that need several rounds anyway keep 4 x 8 (measured best on the
+  //    long fp8 workload).
+  // Fewer blocks per wave also when the grid would hold fewer workgroups than
+  // CUs.  The estimate uses max_context for every row.
   const int mc = max_context > 0 ? max_context : 1;
   const long rows = (long)batch * hkv;
+  auto wgs = [&](int w, int nt) { return rows * ceil_div(mc, 16 * nt * w); };
   (void)elt_bytes;
   int waves = 4, nt = 8;
-  if (mc > 512 && rows * ceil_div(mc, 1024) <= 256) {
+  if (mc > 512 && wgs(8, 8) <= 256) {
     waves = 8;
   } else {
-    while (nt > 2 && rows * ceil_div(mc, 64 * nt) < 256 && ceil_div(mc, 64 * nt) > 1) nt /= 2;
+    if (wgs(4, 8) > 256 && wgs(4, 4) <= 768) nt = 4;
+    while (nt > 2 && wgs(4, nt) < 256 && ceil_div(mc, 64 * nt) > 1) nt /= 2;
   }
   p.waves = waves;
   p.nt = nt;
