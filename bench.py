@@ -44,14 +44,19 @@ def log(*a):
 class DecodeRun:
     """One batch size: cache, allocator, staging ring, captured graph."""
 
-    def __init__(self, pkv, torch, model, shape, batch, prompt_len, total_steps, seed):
+    def __init__(self, pkv, torch, model, shape, batch, prompt_len, total_steps, seed, kv_dtype="f16"):
         self.pkv, self.torch, self.model, self.shape, self.batch = pkv, torch, model, shape, batch
         self.prompt_len = prompt_len
         self.max_context = total_steps + 1  # total_steps counts the prompt steps too
         self.stride = math.ceil(self.max_context / 16)
         need = batch * self.stride
         self.num_blocks = int(math.ceil(1.25 * need))
-        self.cache = pkv.KVCache(shape.n_layers, self.num_blocks, shape.n_kv_heads, shape.head_dim)
+        if kv_dtype == "fp8":  # per-layer scales sized for |k|, |v| up to ~9
+            self.cache = pkv.KVCache(shape.n_layers, self.num_blocks, shape.n_kv_heads, shape.head_dim,
+                                     dtype=pkv.KV_FP8_E4M3, k_scales=[0.02] * shape.n_layers,
+                                     v_scales=[0.02] * shape.n_layers)
+        else:
+            self.cache = pkv.KVCache(shape.n_layers, self.num_blocks, shape.n_kv_heads, shape.head_dim)
         self.alloc = pkv.BlockAllocator(self.num_blocks, seed=seed)
         rng = np.random.default_rng(seed)
         self.prompts = rng.integers(0, shape.vocab, size=(batch, prompt_len)).astype(np.int32)
@@ -101,8 +106,8 @@ class DecodeRun:
         self.cache.close()
 
 
-def time_decode(pkv, torch, model, shape, batch, prompt_len, warmup, steps, seed):
-    run = DecodeRun(pkv, torch, model, shape, batch, prompt_len, prompt_len + warmup + steps, seed)
+def time_decode(pkv, torch, model, shape, batch, prompt_len, warmup, steps, seed, kv_dtype="f16"):
+    run = DecodeRun(pkv, torch, model, shape, batch, prompt_len, prompt_len + warmup + steps, seed, kv_dtype)
     run.prefill()
     for _ in range(warmup):
         run.step()
@@ -122,14 +127,15 @@ def time_decode(pkv, torch, model, shape, batch, prompt_len, warmup, steps, seed
             "wall_s": wall, "mean_context": ctx_mean}
 
 
-def step_bytes(shape, batch, mean_ctx):
+def step_bytes(shape, batch, mean_ctx, kv_elt=2):
     """Algorithmic HBM bytes of one decode step: weights once, the KV read for
-    every row's context, the new KV written, embedding rows read, logits written."""
+    every row's context, the new KV written, embedding rows read, logits written
+    (kv_elt: bytes per cached K/V element, 2 for f16, 1 for E4M3)."""
     h, d, f, v = shape.hidden, shape.head_dim, shape.ffn, shape.vocab
     qkv = (shape.n_q_heads + 2 * shape.n_kv_heads) * d
     per_layer_w = 2 * (h + qkv * h + qkv + h * shape.n_q_heads * d + h + 2 * f * h + h * f)
     weights = shape.n_layers * per_layer_w + 2 * (h + v * h)
-    kv_tok = shape.n_layers * shape.n_kv_heads * d * 2 * 2
+    kv_tok = shape.n_layers * shape.n_kv_heads * d * 2 * kv_elt
     return weights + batch * mean_ctx * kv_tok + batch * kv_tok + batch * h * 2 + batch * v * 2
 
 
@@ -262,6 +268,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--batches", default="1,64,128,256")
     ap.add_argument("--prompt", type=int, default=128)
+    ap.add_argument("--fp8-batches", default="256",
+                    help="batches also timed with an E4M3 KV cache (reported beside the f16 line)")
     ap.add_argument("--attn-rounds", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-attn", action="store_true")
@@ -309,6 +317,17 @@ def main():
         log(f"batch {n}: {r['ms_per_step']:.3f} ms/step, {r['tok_s']:.0f} tok/s, "
             f"{100 * r['frac_of_roofline']:.1f}% of the HBM roofline")
 
+    per_batch_fp8 = {}
+    for n in ([int(x) for x in args.fp8_batches.split(",") if x.strip()] if batches else []):
+        r = time_decode(pkv, torch, model, shape, n, args.prompt, args.warmup, args.steps, seed=2003 + n,
+                        kv_dtype="fp8")
+        nbytes = step_bytes(shape, n, r["mean_context"], kv_elt=1)
+        r["bytes_per_step"] = nbytes
+        r["roofline_ms"] = nbytes / (HBM_PEAK_GBS * 1e9) * 1e3
+        r["frac_of_roofline"] = r["roofline_ms"] / r["ms_per_step"]
+        per_batch_fp8[n] = r
+        log(f"batch {n}, E4M3 KV cache: {r['ms_per_step']:.3f} ms/step, {r['tok_s']:.0f} tok/s")
+
     attn = {}
     if not args.no_attn:
         attn["attn15"] = time_attention(pkv, torch, inp.ATTN15, 28, args.attn_rounds, seed=11)
@@ -350,6 +369,8 @@ def main():
                    "global_batch": head, "seq_len": args.prompt + args.warmup + args.steps},
         "decode": {str(n): {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                    for n, r in per_batch.items()},
+        "decode_fp8_kv": {str(n): {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+                          for n, r in per_batch_fp8.items()},
         "attention": attn,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -117,8 +117,12 @@ pkv_status pkv_kv_cache_layer(const pkv_cache* cache, int layer, void** k_pool, 
 
 /* Append one token per row: k and v are f16 [batch][Hkv][D]; row b is stored
  * at pos = context_lens[b] - 1 of layer `layer` (skipped when the length is 0).
- * A pure copy: the stored bytes equal the input bytes.  f16 caches only
- * (PKV_E_UNSUPPORTED for fp8).  block_tables: [batch][bt_stride] int32. */
+ * f16 caches store the input bytes unchanged.  fp8 caches store the E4M3 code
+ * of x / s for each f16 input x, with s the layer's k or v scale: the quotient
+ * is formed in float32 (IEEE division), then rounded to the nearest E4M3
+ * value with ties to the even code; magnitudes at or above 448 saturate to
+ * +-448 and NaN maps to a NaN code (a reading: the rvLLM post names an E4M3
+ * cache without a rounding rule).  block_tables: [batch][bt_stride] int32. */
 pkv_status pkv_kv_append(pkv_cache* cache, int layer, const void* k, const void* v,
                          const int32_t* block_tables, int bt_stride,
                          const int32_t* context_lens, int batch, pkv_stream_t stream);
@@ -207,8 +211,9 @@ pkv_status pkv_step_workspace_bytes(const pkv_model* model, const pkv_cache* cac
  *   append k, v at pos = context_lens[b] - 1; o = paged attention(q)
  *   h1 = h + W_o o;  m = RMSNorm(h1) * w_post;  g,u = split(W_gate_up m)
  *   h  = h1 + W_down (silu(g) * u)
- * hidden: f16 [batch][H], updated in place.  The cache must be f16 with the
- * model's Hkv and head_dim and at least layer+1 layers. */
+ * hidden: f16 [batch][H], updated in place.  The cache (f16, or fp8 with the
+ * appended k and v quantised as pkv_kv_append does, from their f16 values)
+ * must have the model's Hkv and head_dim and at least layer+1 layers. */
 pkv_status pkv_decode_layer(const pkv_model* model, pkv_cache* cache, int layer, void* hidden,
                             const int32_t* block_tables, int bt_stride,
                             const int32_t* context_lens, int batch, int max_context,
@@ -218,7 +223,8 @@ pkv_status pkv_decode_layer(const pkv_model* model, pkv_cache* cache, int layer,
  * logits = W_lm RMSNorm(h) * w_final_norm.  token_ids int32 [batch];
  * logits f16 [batch][V]; hidden_out (nullable) f16 [batch][H] gets the final
  * pre-norm hidden state.  Appends each row's token to the cache at
- * pos = context_lens[b] - 1 in every layer. */
+ * pos = context_lens[b] - 1 in every layer (f16 or fp8 caches, as
+ * pkv_decode_layer). */
 pkv_status pkv_decode_step(const pkv_model* model, pkv_cache* cache, const int32_t* token_ids,
                            const int32_t* block_tables, int bt_stride,
                            const int32_t* context_lens, int batch, int max_context,

@@ -43,7 +43,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .fp8 import e4m3_decode
+from .fp8 import e4m3_decode, e4m3_quantize
 
 F16 = np.float16
 
@@ -200,9 +200,17 @@ def paged_attention_batch(q, k_pool, v_pool, block_tables, ctx_lens, scale, *,
     return out, lse
 
 
-def kv_append(k_pool, v_pool, k_new, v_new, block_tables, ctx_lens):
-    """Store each active row's new K/V (f16 [B, Hkv, D]) at pos = ctx_len - 1."""
+def kv_append(k_pool, v_pool, k_new, v_new, block_tables, ctx_lens, k_scale=None, v_scale=None):
+    """Store each active row's new K/V (f16 [B, Hkv, D]) at pos = ctx_len - 1.
+
+    E4M3 pools (uint8) store the codes of the f16 values under the layer's
+    per-tensor scales (e4m3_quantize: float32 quotient, nearest-even,
+    saturating), the reading taken for the quantised cache of the rvLLM post
+    (section "PagedAttention과 FlashAttention-3")."""
     bs = k_pool.shape[2]
+    if k_pool.dtype == np.uint8:
+        k_new = e4m3_quantize(k_new, k_scale)
+        v_new = e4m3_quantize(v_new, v_scale)
     for b in range(k_new.shape[0]):
         c = int(ctx_lens[b])
         if c == 0:
@@ -223,11 +231,13 @@ def _linear(x, w, acc, bias=None):
     return y
 
 
-def decode_layer(cfg, lw, h, k_pool, v_pool, block_tables, ctx_lens, acc=np.float64):
+def decode_layer(cfg, lw, h, k_pool, v_pool, block_tables, ctx_lens, acc=np.float64, k_scale=None,
+                 v_scale=None):
     """One decoder layer for a batch of single-token rows.
 
     h: [B, H] f16 hidden state; the pools are this layer's and are updated in
-    place by the append.  Returns the new hidden state [B, H] f16.
+    place by the append (E4M3 pools with this layer's k_scale / v_scale).
+    Returns the new hidden state [B, H] f16.
     """
     hq, hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     b_n = h.shape[0]
@@ -242,10 +252,13 @@ def decode_layer(cfg, lw, h, k_pool, v_pool, block_tables, ctx_lens, acc=np.floa
     q = rope(q, pos, cfg.rope_theta, acc).astype(F16)
     k = rope(k, pos, cfg.rope_theta, acc).astype(F16)
     v = v.astype(F16)
-    kv_append(k_pool, v_pool, k, v, block_tables, lens)
+    kv_append(k_pool, v_pool, k, v, block_tables, lens, k_scale, v_scale)
 
-    o, _ = paged_attention_batch(q, k_pool, v_pool, block_tables, lens,
-                                 1.0 / np.sqrt(d), acc=acc)
+    if k_pool.dtype == np.uint8:
+        o, _ = paged_attention_batch(q, k_pool, v_pool, block_tables, lens, 1.0 / np.sqrt(d),
+                                     k_scale=k_scale, v_scale=v_scale, acc=acc)
+    else:
+        o, _ = paged_attention_batch(q, k_pool, v_pool, block_tables, lens, 1.0 / np.sqrt(d), acc=acc)
     h1 = (np.asarray(h, dtype=acc) + _linear(o.reshape(b_n, hq * d), lw["w_o"], acc)).astype(F16)
 
     m = rmsnorm(h1, lw["w_post"], cfg.rms_eps, acc)
@@ -256,16 +269,19 @@ def decode_layer(cfg, lw, h, k_pool, v_pool, block_tables, ctx_lens, acc=np.floa
 
 
 def decode_step(cfg, weights, k_pools, v_pools, tokens, block_tables, ctx_lens,
-                acc=np.float64):
+                acc=np.float64, k_scales=None, v_scales=None):
     """Embedding -> every layer -> final RMSNorm -> LM head.
 
     weights: {"embed" [V,H], "layers": [layer dicts], "w_final_norm" [H],
     "w_lm_head" [V,H]} (f16).  k_pools / v_pools: per-layer pools, updated in
-    place.  Returns (logits [B, V] f16, final hidden [B, H] f16).
+    place (E4M3 pools take per-layer k_scales / v_scales).  Returns
+    (logits [B, V] f16, final hidden [B, H] f16).
     """
     h = np.asarray(weights["embed"])[np.asarray(tokens, dtype=np.int64)].astype(F16)
     for li, lw in enumerate(weights["layers"]):
-        h = decode_layer(cfg, lw, h, k_pools[li], v_pools[li], block_tables, ctx_lens, acc)
+        ks = None if k_scales is None else k_scales[li]
+        vs = None if v_scales is None else v_scales[li]
+        h = decode_layer(cfg, lw, h, k_pools[li], v_pools[li], block_tables, ctx_lens, acc, ks, vs)
     n = rmsnorm(h, weights["w_final_norm"], cfg.rms_eps, acc)
     logits = _linear(n, weights["w_lm_head"], acc).astype(F16)
     return logits, h

@@ -125,9 +125,10 @@ pkv_status pkv_kv_append(pkv_cache* cache, int layer, const void* k, const void*
   pkv_status st = check_meta_args(cache, layer, block_tables, bt_stride, context_lens, batch, 1);
   if (st != PKV_OK) return st;
   if (!k || !v) return fail(PKV_E_ARG, "k / v is NULL");
-  if (cache->desc.dtype != PKV_KV_F16) return fail(PKV_E_UNSUPPORTED, "kv_append supports f16 caches only");
+  const bool fp8 = cache->desc.dtype == PKV_KV_FP8_E4M3;
   PKV_HIP(launch_kv_append(cache->k_pool(layer), cache->v_pool(layer), k, v, block_tables, bt_stride,
-                           context_lens, batch, cache->desc.num_kv_heads, cache->desc.head_dim,
+                           context_lens, batch, cache->desc.num_kv_heads, cache->desc.head_dim, fp8,
+                           fp8 ? cache->k_scales[layer] : 1.f, fp8 ? cache->v_scales[layer] : 1.f,
                            static_cast<hipStream_t>(stream)));
   return PKV_OK;
 }

@@ -1,16 +1,20 @@
-// KV append into the block-table paged cache (a plain copy into the slot of
-// position context_lens[b] - 1; aitrends.kr glossary: the KV cache keeps the
-// keys and values of earlier tokens; rvLLM post, section
-// "PagedAttention과 FlashAttention-3": the cache is paged through block tables).
+// KV append into the block-table paged cache: each active row's new k and v
+// go to the slot of position context_lens[b] - 1, as f16 or as E4M3 codes
+// under the layer's scales (aitrends.kr glossary: the KV cache keeps the keys
+// and values of earlier tokens; rvLLM post, section
+// "PagedAttention과 FlashAttention-3": the cache is paged through block
+// tables, optionally FP8 E4M3).
+#include "kvstore.h"
 #include "pkv_internal.h"
 
 namespace pkv {
 namespace {
 
-__global__ void kv_append_kernel(uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
-                                 const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+__global__ void kv_append_kernel(void* __restrict__ kpool, void* __restrict__ vpool,
+                                 const _Float16* __restrict__ k, const _Float16* __restrict__ v,
                                  const int32_t* __restrict__ bt, int bt_stride,
-                                 const int32_t* __restrict__ lens, int hkv, int head_dim) {
+                                 const int32_t* __restrict__ lens, int hkv, int head_dim, int fp8,
+                                 float k_scale, float v_scale) {
   const int b = blockIdx.x;
   const int c = lens[b];
   if (c <= 0) return;
@@ -19,10 +23,9 @@ __global__ void kv_append_kernel(uint16_t* __restrict__ kpool, uint16_t* __restr
   const int slot = pos % kBlock;
   for (int idx = threadIdx.x; idx < hkv * head_dim; idx += blockDim.x) {
     const int g = idx / head_dim, d = idx - g * head_dim;
-    const size_t bg = (size_t)blk * hkv + g;
-    // K tile [D/8][16][8]: 8-dim chunk, token, dim within the chunk
-    kpool[bg * kBlock * head_dim + (d >> 3) * (kBlock * 8) + slot * 8 + (d & 7)] = k[(size_t)b * hkv * head_dim + idx];
-    vpool[(bg * head_dim + d) * kBlock + slot] = v[(size_t)b * hkv * head_dim + idx];
+    const size_t tile = ((size_t)blk * hkv + g) * kBlock * head_dim;
+    kv_store(kpool, tile + k_tile_off(fp8, slot, d), fp8, k_scale, (float)k[(size_t)b * hkv * head_dim + idx]);
+    kv_store(vpool, tile + v_tile_off(fp8, slot, d), fp8, v_scale, (float)v[(size_t)b * hkv * head_dim + idx]);
   }
 }
 
@@ -30,11 +33,10 @@ __global__ void kv_append_kernel(uint16_t* __restrict__ kpool, uint16_t* __restr
 
 hipError_t launch_kv_append(void* k_pool, void* v_pool, const void* k, const void* v,
                             const int32_t* bt, int bt_stride, const int32_t* lens, int batch,
-                            int hkv, int head_dim, hipStream_t s) {
-  hipLaunchKernelGGL(kv_append_kernel, dim3(batch), dim3(256), 0, s,
-                     static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool),
-                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), bt,
-                     bt_stride, lens, hkv, head_dim);
+                            int hkv, int head_dim, bool fp8, float k_scale, float v_scale, hipStream_t s) {
+  hipLaunchKernelGGL(kv_append_kernel, dim3(batch), dim3(256), 0, s, k_pool, v_pool,
+                     static_cast<const _Float16*>(k), static_cast<const _Float16*>(v), bt, bt_stride, lens,
+                     hkv, head_dim, fp8 ? 1 : 0, k_scale, v_scale);
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // Fused projection launchers shared by the decode layer and the LM head.
 #pragma once
 
+#include "kvstore.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -26,9 +27,11 @@ struct RopeArgs {
   const int32_t* bt;      // [M][bt_stride] block tables
   int bt_stride;
   _Float16* q_out;        // [M][Hq][D] rotated queries
-  _Float16* k_pool;       // this layer's K pool (tiles [D/8][16][8])
-  _Float16* v_pool;       // this layer's V pool (tiles [D][16])
+  void* k_pool;           // this layer's K pool (f16 or E4M3 tiles, include/pkv.h)
+  void* v_pool;           // this layer's V pool
   int hq, hkv, d;
+  int fp8;                // E4M3 cache: store codes of f16(x) / scale
+  float k_scale, v_scale;
 };
 
 // Weight rows of output pair p.
@@ -77,15 +80,17 @@ __device__ __forceinline__ void rope_put(const RopeArgs& ra, const RopeRow& r, i
       _Float16* q = ra.q_out + ((size_t)m * ra.hq + head) * ra.d;
       q[i] = (_Float16)o0;
       q[half + i] = (_Float16)o1;
-    } else if (r.c > 0) {  // K tile [D/8][16][8]
-      _Float16* kp = ra.k_pool + ((size_t)r.blk * ra.hkv + (head - ra.hq)) * 16 * ra.d + (r.pos % 16) * 8;
-      kp[(i >> 3) * 128 + (i & 7)] = (_Float16)o0;
-      kp[((half + i) >> 3) * 128 + ((half + i) & 7)] = (_Float16)o1;
+    } else if (r.c > 0) {
+      const size_t tile = ((size_t)r.blk * ra.hkv + (head - ra.hq)) * 16 * ra.d;
+      const int t = r.pos % 16;
+      kv_store(ra.k_pool, tile + k_tile_off(ra.fp8, t, i), ra.fp8, ra.k_scale, o0);
+      kv_store(ra.k_pool, tile + k_tile_off(ra.fp8, t, half + i), ra.fp8, ra.k_scale, o1);
     }
-  } else if (r.c > 0) {  // V tile [D][16]
-    _Float16* vp = ra.v_pool + ((size_t)r.blk * ra.hkv + (head - ra.hq - ra.hkv)) * ra.d * 16 + (r.pos % 16);
-    vp[i * 16] = (_Float16)y0;
-    vp[(half + i) * 16] = (_Float16)y1;
+  } else if (r.c > 0) {
+    const size_t tile = ((size_t)r.blk * ra.hkv + (head - ra.hq - ra.hkv)) * 16 * ra.d;
+    const int t = r.pos % 16;
+    kv_store(ra.v_pool, tile + v_tile_off(ra.fp8, t, i), ra.fp8, ra.v_scale, y0);
+    kv_store(ra.v_pool, tile + v_tile_off(ra.fp8, t, half + i), ra.fp8, ra.v_scale, y1);
   }
 }
 // The pair's two bias values (0 without bias).

@@ -92,7 +92,6 @@ pkv_status check_step(const pkv_model* m, const pkv_cache* cache, const int32_t*
                       StepBuffers* bufs, AttnPlan* plan) {
   if (!m || !cache) return fail(PKV_E_ARG, "model / cache is NULL");
   const pkv_cache_desc& cd = cache->desc;
-  if (cd.dtype != PKV_KV_F16) return fail(PKV_E_UNSUPPORTED, "the decode step supports f16 KV caches");
   if (cd.num_kv_heads != m->d.num_kv_heads || cd.head_dim != m->d.head_dim)
     return fail(PKV_E_ARG, "cache heads / head_dim differ from the model's");
   if (!bt || !lens) return fail(PKV_E_ARG, "block_tables / context_lens is NULL");
@@ -132,15 +131,18 @@ hipError_t run_layer(const pkv_model* m, pkv_cache* cache, int layer, _Float16* 
   a.rope.cos_sin = static_cast<const float2*>(m->rope);
   a.rope.lens = lens; a.rope.bt = bt; a.rope.bt_stride = bt_stride;
   a.rope.q_out = sb.q;
-  a.rope.k_pool = static_cast<_Float16*>(kp); a.rope.v_pool = static_cast<_Float16*>(vp);
+  const bool fp8 = cache->desc.dtype == PKV_KV_FP8_E4M3;
+  const float ks = fp8 ? cache->k_scales[layer] : 1.f, vs = fp8 ? cache->v_scales[layer] : 1.f;
+  a.rope.k_pool = kp; a.rope.v_pool = vp;
   a.rope.hq = d.num_q_heads; a.rope.hkv = d.num_kv_heads; a.rope.d = d.head_dim;
+  a.rope.fp8 = fp8; a.rope.k_scale = ks; a.rope.v_scale = vs;
   if ((e = launch_linear(a, EPI_ROPE, sb.gemm_ws, sb.counters, s)) != hipSuccess) return e;
   // 2. paged attention
   AttnArgs at{};
   at.k_pool = kp; at.v_pool = vp; at.q = sb.q; at.out = sb.o; at.lse = nullptr;
   at.bt = bt; at.bt_stride = bt_stride; at.lens = lens; at.batch = batch;
-  at.hq = d.num_q_heads; at.hkv = d.num_kv_heads; at.head_dim = d.head_dim; at.fp8 = false;
-  at.scale = 1.0f / std::sqrt((float)d.head_dim); at.k_scale = at.v_scale = 1.f; at.ws = sb.attn_ws;
+  at.hq = d.num_q_heads; at.hkv = d.num_kv_heads; at.head_dim = d.head_dim; at.fp8 = fp8;
+  at.scale = 1.0f / std::sqrt((float)d.head_dim); at.k_scale = ks; at.v_scale = vs; at.ws = sb.attn_ws;
   if ((e = launch_paged_attention(at, plan, s)) != hipSuccess) return e;
   // 3. O projection + residual add
   a = LinArgs{};

@@ -75,6 +75,6 @@ hipError_t launch_paged_attention(const AttnArgs& a, const AttnPlan& p, hipStrea
 // ------------------------------------------------------------------ KV ops
 hipError_t launch_kv_append(void* k_pool, void* v_pool, const void* k, const void* v,
                             const int32_t* bt, int bt_stride, const int32_t* lens, int batch,
-                            int hkv, int head_dim, hipStream_t s);
+                            int hkv, int head_dim, bool fp8, float k_scale, float v_scale, hipStream_t s);
 
 }  // namespace pkv

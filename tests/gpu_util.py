@@ -92,3 +92,26 @@ def oracle_config(shape, n_layers=None):
     return oracle.ModelConfig(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn,
                               shape.vocab, shape.n_layers if n_layers is None else n_layers,
                               shape.rms_eps, shape.rope_theta)
+
+
+def tie_aware_agree(gpu_tok, ref_logits):
+    """Per row: the GPU's greedy token is the oracle's, or its oracle logit is
+    within the parity bar of the oracle's maximum (a tie at the bar)."""
+    ref = ref_logits.astype(np.float64)
+    best = ref.max(-1)
+    got = ref[np.arange(len(gpu_tok)), gpu_tok]
+    return got >= best - (ATOL + RTOL * np.abs(best))
+
+
+def calibrated(gpu, ref, ref_pert, what):
+    """GPU within the per-element bar, or within twice the oracle's own change
+    under a 1-ulp perturbation of its input (ref_pert)."""
+    g, r, rp = (np.asarray(a, np.float64) for a in (gpu, ref, ref_pert))
+    assert np.all(np.isfinite(g)), what
+    err = np.abs(g - r)
+    bar = ATOL + RTOL * np.abs(r)
+    sens = np.abs(rp - r).max()
+    inside = np.mean(err <= bar)
+    print(f"{what}: max abs err {err.max():.4f}, {100 * inside:.4f} % inside the bar, "
+          f"oracle 1-ulp sensitivity {sens:.4f}")
+    assert np.all(err <= np.maximum(bar, 2 * sens)), (what, err.max(), sens)

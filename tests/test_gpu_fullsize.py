@@ -27,7 +27,7 @@ import torch
 
 import oracle
 import pkv_inputs as inp
-from gpu_util import dev, assert_parity, oracle_config, ATOL, RTOL, k_to_lib
+from gpu_util import dev, assert_parity, calibrated, oracle_config, k_to_lib, tie_aware_agree
 from test_gpu_model import _run_layer_gpu, _oracle_layer
 
 pytestmark = pytest.mark.gpu
@@ -58,13 +58,6 @@ def _host(w):
     return {"embed": w["embed"].cpu().numpy(), "w_final_norm": w["w_final_norm"].cpu().numpy(),
             "w_lm_head": w["w_lm_head"].cpu().numpy(),
             "layers": [{k: (None if t is None else t.cpu().numpy()) for k, t in lw.items()} for lw in w["layers"]]}
-
-
-def _tie_aware_agree(gpu_tok, ref_logits):
-    ref = ref_logits.astype(np.float64)
-    best = ref.max(-1)
-    got = ref[np.arange(len(gpu_tok)), gpu_tok]
-    return got >= best - (ATOL + RTOL * np.abs(best))
 
 
 class FullStep:
@@ -119,19 +112,6 @@ class FullStep:
                                   self.lens[rows], acc=np.float32)
 
 
-def _calibrated(gpu, ref, ref_pert, what):
-    """GPU within the per-element bar, or within twice the oracle's own 1-ulp sensitivity."""
-    g, r, rp = (np.asarray(a, np.float64) for a in (gpu, ref, ref_pert))
-    assert np.all(np.isfinite(g)), what
-    err = np.abs(g - r)
-    bar = ATOL + RTOL * np.abs(r)
-    sens = np.abs(rp - r).max()
-    inside = np.mean(err <= bar)
-    print(f"{what}: max abs err {err.max():.4f}, {100 * inside:.4f} % inside the bar, "
-          f"oracle 1-ulp sensitivity {sens:.4f}")
-    assert np.all(err <= np.maximum(bar, 2 * sens)), (what, err.max(), sens)
-
-
 @pytest.mark.parametrize("batch", [64, 256])
 def test_lm_head_full_vocabulary(lib, batch):
     rig = FullStep(lib, inp.QWEN15, 1, batch, 1, 40, seed=5100 + batch)
@@ -140,7 +120,7 @@ def test_lm_head_full_vocabulary(lib, batch):
     rl, rh = rig.oracle_rows(rows)
     assert_parity(hidden, rh, "hidden")
     assert_parity(logits, rl, f"logits, batch {batch}")
-    assert np.all(_tie_aware_agree(tok, rl))
+    assert np.all(tie_aware_agree(tok, rl))
     assert np.mean(tok == oracle.greedy_argmax(rl)) >= 0.99
 
 
@@ -152,6 +132,6 @@ def test_full_model_step_sampled_rows(lib, name, batch, lo, hi, n_rows):
     rows = np.sort(np.random.default_rng(5300).choice(batch, size=n_rows, replace=False))
     rl, rh = rig.oracle_rows(rows)
     rlp, rhp = rig.oracle_rows(rows, perturb=True)
-    _calibrated(logits[rows], rl, rlp, f"{name} logits")
-    _calibrated(hidden[rows], rh, rhp, f"{name} final hidden")
-    assert np.all(_tie_aware_agree(tok[rows], rl))
+    calibrated(logits[rows], rl, rlp, f"{name} logits")
+    calibrated(hidden[rows], rh, rhp, f"{name} final hidden")
+    assert np.all(tie_aware_agree(tok[rows], rl))
