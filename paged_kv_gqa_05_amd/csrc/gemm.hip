@@ -66,17 +66,18 @@ __device__ __forceinline__ void load_to_lds(const void* g, const _Float16* lds) 
 // wait for every outstanding global load).
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int MT, int NT, int NS, int EPI, bool NORM>
+template <int MT, int NT, int NS, int EPI, bool NORM, int WM, int WN>
 struct Cfg {
   static constexpr bool PAIR = epi_pair(EPI);
-  static constexpr int WTM = MT / 2, WTN = NT / 2;   // wave tile
+  static constexpr int WV = WM * WN;                  // waves per workgroup
+  static constexpr int WTM = MT / WM, WTN = NT / WN;  // wave tile
   static constexpr int FM = WTM / 16, FN = WTN / 16;  // 16 x 16 fragments per wave
   static constexpr int ROWS = MT + NT;
-  static constexpr int LPS = ROWS / 32;               // row loads per wave per stage
+  static constexpr int LPS = ROWS / (8 * WV);         // 8-row loads per wave per stage
   static constexpr int LPW = LPS + (NORM ? 1 : 0);    // + the gain row
-  static constexpr int GAIN_OFF = ROWS * BK;          // f16 offset of the 4 gain rows
-  static constexpr int STAGE = ROWS * BK + (NORM ? 4 * BK : 0);  // f16 per stage
-  static_assert(ROWS % 32 == 0 && FM >= 1 && FN >= 1, "tile shape");
+  static constexpr int GAIN_OFF = ROWS * BK;          // f16 offset of the per-wave gain rows
+  static constexpr int STAGE = ROWS * BK + (NORM ? WV * BK : 0);  // f16 per stage
+  static_assert(ROWS % (8 * WV) == 0 && FM >= 1 && FN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "tile shape");
   static_assert(!PAIR || (FN % 2 == 0), "paired tiles need an even fragment count");
   static_assert(NS >= 2 && (NS - 2) * LPW < 64, "stages");
 };
@@ -96,9 +97,10 @@ __device__ __forceinline__ void wait_stage(int pending) {
   }
 }
 
-template <int MT, int NT, int NS, int EPI, bool NORM>
-__global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
-  using C = Cfg<MT, NT, NS, EPI, NORM>;
+template <int MT, int NT, int NS, int EPI, bool NORM, int WM, int WN>
+__global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmParams p) {
+  using C = Cfg<MT, NT, NS, EPI, NORM, WM, WN>;
+  constexpr int WV = C::WV;
   constexpr bool PAIR = C::PAIR;
   constexpr int FM = C::FM, FN = C::FN;
   __shared__ __attribute__((aligned(1024))) h16 smem[NS * C::STAGE];
@@ -120,16 +122,16 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
 
   // ---- per-lane sources of this wave's direct-to-LDS row loads
-  // load j of wave w covers stage rows 8 * (4 j + w) .. + 8
+  // load j of wave w covers stage rows 8 * (WV j + w) .. + 8
   const int lrow = lane >> 3;                  // row within the 8-row group
   const int lchunk = (lane & 7) ^ lrow;        // 16-byte chunk this lane fetches
   const h16* src[C::LPS];
 #pragma unroll
   for (int j = 0; j < C::LPS; ++j) {
-    const int r = 8 * (4 * j + wave) + lrow;   // stage row
+    const int r = 8 * (WV * j + wave) + lrow;  // stage row
     if (r < MT) {
       src[j] = p.A + (size_t)min(m0 + r, p.M - 1) * p.lda;
     } else {
@@ -152,7 +154,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
     const int k = min(kbase + 8 * lchunk, kmax);
     h16* sb = smem + buf * C::STAGE;
 #pragma unroll
-    for (int j = 0; j < C::LPS; ++j) load_to_lds(src[j] + k, sb + (4 * j + wave) * 8 * BK);
+    for (int j = 0; j < C::LPS; ++j) load_to_lds(src[j] + k, sb + (WV * j + wave) * 8 * BK);
     if constexpr (NORM) {
       if (lane < 8) {  // this wave's copy of the 64 gain values of the stage
         const int kg = min(kbase + 8 * lane, kmax);
@@ -179,7 +181,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   for (int j = 0; j < FN; ++j) {
     int t;
     if (PAIR) {
-      t = (j < FN / 2) ? wn * (NT / 4) + j * 16 : NT / 2 + wn * (NT / 4) + (j - FN / 2) * 16;
+      t = (j < FN / 2) ? wn * (NT / (2 * WN)) + j * 16 : NT / 2 + wn * (NT / (2 * WN)) + (j - FN / 2) * 16;
     } else {
       t = wn * C::WTN + j * 16;
     }
@@ -339,7 +341,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
     bool pok[FP];
 #pragma unroll
     for (int j = 0; j < FP; ++j) {
-      const int col = nt * (NT / 2) + wn * (NT / 4) + j * 16 + fr;
+      const int col = nt * (NT / 2) + wn * (NT / (2 * WN)) + j * 16 + fr;
       pok[j] = col < p.n_out;
       pc[j] = min(col, p.n_out - 1);
     }
@@ -378,7 +380,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
       for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int j = 0; j < FN / 2; ++j) {
-          const int col = nt * (NT / 2) + wn * (NT / 4) + j * 16 + fr;
+          const int col = nt * (NT / 2) + wn * (NT / (2 * WN)) + j * 16 + fr;
           if (mok[i][v] && col < p.n_out) {
             const float g = acc[i][j][v] * rs[i][v], u = acc[i][j + FN / 2][v] * rs[i][v];
             static_cast<h16*>(p.out)[(size_t)mrow[i][v] * p.ldo + col] = (h16)(silu(g) * u);
@@ -418,9 +420,10 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   }
 }
 
-template <int MT, int NT, int NS, int EPI>
+template <int MT, int NT, int NS, int EPI, int WM = 2, int WN = 2>
 hipError_t launch_cfg(const GemmParams& gp, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<MT, NT, NS, EPI, epi_norm(EPI)>), dim3(gp.per_xcd * 8), dim3(256), 0, s, gp);
+  hipLaunchKernelGGL((gemm_kernel<MT, NT, NS, EPI, epi_norm(EPI), WM, WN>), dim3(gp.per_xcd * 8),
+                     dim3(64 * WM * WN), 0, s, gp);
   return hipGetLastError();
 }
 
@@ -429,7 +432,7 @@ hipError_t launch_epi(const GemmPlan& pl, const GemmParams& gp, hipStream_t s) {
   switch (pl.cfg) {
     case GEMM_32x64: return launch_cfg<32, 64, 4, EPI>(gp, s);
     case GEMM_64x128: return launch_cfg<64, 128, 3, EPI>(gp, s);
-    case GEMM_128x128: return launch_cfg<128, 128, 2, EPI>(gp, s);
+    case GEMM_128x128: return launch_cfg<128, 128, 2, EPI, 4, 2>(gp, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -437,23 +440,30 @@ hipError_t launch_epi(const GemmPlan& pl, const GemmParams& gp, hipStream_t s) {
 }  // namespace
 
 // Tile shape and K split for an M x rows x K projection (host only).
-// Tile table (measured at the 1.5B decode shapes, batch 64 and 256): small
-// 32 x 64 tiles with 4 stages win until they exceed ~1024 tiles (the grid then
-// re-reads the activations from L2 too often); larger weight matrices use
-// 64 x 128 (3 stages) and then 128 x 128 (2 stages: two workgroups per CU).
+// Tile table, measured at the 1.5B decode shapes (batch 64, 128, 256, weights
+// rotated so the Infinity Cache cannot hold them): 32 x 64 tiles with 4 stages
+// (2 x 2 waves), 64 x 128 with 3 stages (2 x 2), 128 x 128 with 2 stages (4 x 2
+// waves: two workgroups per CU).  Small tiles win until they exceed ~1024
+// tiles (the grid then re-reads the activations from L2 too often).  Long
+// reductions (K >= 4096, split over K) start at 64 x 128 from batch 128 up:
+// fewer partial tiles to merge (down projection, batch 256: 23 us vs 32 us).
+// When 64 x 128 would already need 512 tiles or more, 128 x 128 (gate/up at
+// batch 256: 37 us vs 41 us; LM head).  No tile is taller than the batch
+// rounded up to 32.
 GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
   const bool pair = epi_pair(epi);
   static const int kCfg[3][3] = {{GEMM_32x64, 32, 64}, {GEMM_64x128, 64, 128}, {GEMM_128x128, 128, 128}};
+  auto tiles_of = [&](int c) { return ceil_div(M, kCfg[c][1]) * ceil_div(n_out, pair ? kCfg[c][2] / 2 : kCfg[c][2]); };
+  const int m_cap = ceil_div(M, 32) * 32;
+  int c = 0;
+  if (K >= 4096 && M >= 128) c = 1;
+  while (c < 2 && kCfg[c + 1][1] <= m_cap && tiles_of(c) >= (c == 1 ? 512 : 1024)) ++c;
   GemmPlan pl{};
-  for (int c = 0; c < 3; ++c) {
-    if (c > 0 && kCfg[c][1] > ceil_div(M, 32) * 32) break;  // no tile taller than the batch
-    pl.cfg = kCfg[c][0];
-    pl.mt = kCfg[c][1];
-    pl.nt = kCfg[c][2];
-    pl.n_mt = ceil_div(M, pl.mt);
-    pl.n_nt = ceil_div(n_out, pair ? pl.nt / 2 : pl.nt);
-    if (pl.n_mt * pl.n_nt < 1024) break;
-  }
+  pl.cfg = kCfg[c][0];
+  pl.mt = kCfg[c][1];
+  pl.nt = kCfg[c][2];
+  pl.n_mt = ceil_div(M, pl.mt);
+  pl.n_nt = ceil_div(n_out, pair ? pl.nt / 2 : pl.nt);
   const int n_kc = ceil_div(K, 64);
   const int tiles = pl.n_mt * pl.n_nt;
   // split K while the grid holds fewer than ~one workgroup per CU and every
