@@ -232,9 +232,11 @@ pkv_status pkv_decode_step(const pkv_model* model, pkv_cache* cache, const int32
                            size_t workspace_bytes, pkv_stream_t stream);
 
 /* Greedy token per row: the lowest index of the largest f16 logit
- * (zingnex.cn article, section 支持的参数: temperature 0 decodes greedily).
- * logits f16 [batch][vocab]; tokens int32 [batch]. */
-pkv_status pkv_argmax(const void* logits, int batch, int vocab, int32_t* tokens,
+ * (zingnex.cn article, section 支持的参数: temperature 0 decodes greedily);
+ * NaN logits never win.  logits f16 [batch][vocab]; tokens int32 [batch].
+ * context_lens (nullable, int32 [batch]): a row whose length is 0 is inactive
+ * and gets token -1. */
+pkv_status pkv_argmax(const void* logits, int batch, int vocab, int32_t* tokens, const int32_t* context_lens,
                       pkv_stream_t stream);
 
 /* ------------------------------------------------------------- graph replay */
@@ -254,6 +256,28 @@ pkv_status pkv_graph_capture(const pkv_model* model, pkv_cache* cache, const int
 /* Launch the captured step on the caller's stream. */
 pkv_status pkv_graph_replay(pkv_graph* graph, pkv_stream_t stream);
 void pkv_graph_destroy(pkv_graph* graph);
+
+/* Batch-size buckets (rvLLM post, section "CUDA 그래프 리플레이": graphs are
+ * captured for a set of batch sizes and a step runs the smallest one that
+ * holds its rows).  Captures one pkv_decode_step per bucket (host array,
+ * strictly ascending, 1 to 64 entries) over the same buffers, each sized for
+ * the largest bucket; workspace_bytes must cover pkv_step_workspace_bytes of
+ * every bucket.  token_ids and context_lens are written by the library on
+ * replay, so they are not const. */
+typedef struct pkv_graph_set pkv_graph_set;
+pkv_status pkv_graph_set_capture(const pkv_model* model, pkv_cache* cache, const int32_t* buckets,
+                                 int n_buckets, int32_t* token_ids, const int32_t* block_tables, int bt_stride,
+                                 int32_t* context_lens, int max_context, void* logits, void* hidden_out,
+                                 void* workspace, size_t workspace_bytes, pkv_stream_t capture_stream,
+                                 pkv_graph_set** out);
+/* Runs the step for rows [0, batch): replays the smallest bucket >= batch on
+ * `stream`, first setting context_lens and token_ids of the padding rows
+ * [batch, bucket) to 0 on that stream (inactive rows: no append, attention
+ * output 0, pkv_argmax with context_lens gives -1).  *bucket_out (host,
+ * nullable) receives the bucket used.  PKV_E_ARG if batch exceeds the largest
+ * bucket. */
+pkv_status pkv_graph_set_replay(pkv_graph_set* set, int batch, pkv_stream_t stream, int* bucket_out);
+void pkv_graph_set_destroy(pkv_graph_set* set);
 
 /* ----------------------------------------------------- host block allocator */
 

@@ -182,10 +182,14 @@ def decode_step(model, cache, token_ids, block_tables, context_lens, max_context
                                 _stream(stream)))
 
 
-def argmax(logits, tokens, stream=None):
+def argmax(logits, tokens, context_lens=None, stream=None):
+    """Greedy tokens; rows whose context length is 0 (when given) get -1."""
     _need(logits, torch.float16, "logits")
     _need(tokens, torch.int32, "tokens")
-    _check(_lib.pkv_argmax(_p(logits), logits.shape[0], logits.shape[1], _p(tokens), _stream(stream)))
+    if context_lens is not None:
+        _need(context_lens, torch.int32, "context_lens")
+    _check(_lib.pkv_argmax(_p(logits), logits.shape[0], logits.shape[1], _p(tokens), _p(context_lens),
+                           _stream(stream)))
 
 
 class Graph:
@@ -207,6 +211,35 @@ class Graph:
 
     def close(self):
         _destroy("pkv_graph_destroy", self)
+
+    __del__ = close
+
+
+class GraphSet:
+    """One captured decode step per batch-size bucket over shared buffers sized
+    for the largest bucket; replay(n) runs rows [0, n) in the smallest bucket
+    >= n with the padding rows made inactive, and returns that bucket."""
+
+    def __init__(self, model, cache, buckets, token_ids, block_tables, context_lens, max_context, logits,
+                 workspace, hidden_out=None, capture_stream=None):
+        self.keep = (model, cache, token_ids, block_tables, context_lens, logits, workspace, hidden_out)
+        self.buckets = sorted(int(b) for b in buckets)
+        cs = capture_stream if capture_stream is not None else torch.cuda.Stream()
+        arr = (C.c_int32 * len(self.buckets))(*self.buckets)
+        h = C.c_void_p()
+        _check(_lib.pkv_graph_set_capture(model.handle, cache.handle, arr, len(self.buckets), _p(token_ids),
+                                          _p(block_tables), block_tables.shape[1], _p(context_lens), max_context,
+                                          _p(logits), _p(hidden_out), _p(workspace), workspace.numel(),
+                                          C.c_void_p(cs.cuda_stream), C.byref(h)))
+        self.handle = h
+
+    def replay(self, batch, stream=None):
+        bk = C.c_int(0)
+        _check(_lib.pkv_graph_set_replay(self.handle, int(batch), _stream(stream), C.byref(bk)))
+        return bk.value
+
+    def close(self):
+        _destroy("pkv_graph_set_destroy", self)
 
     __del__ = close
 

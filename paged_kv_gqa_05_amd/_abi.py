@@ -48,11 +48,15 @@ SIGNATURES = {
                                     vp, size_t, vp]),
     "pkv_decode_step": (c_status, [vp, vp, i32p, i32p, C.c_int, i32p, C.c_int, C.c_int, vp, vp,
                                    vp, size_t, vp]),
-    "pkv_argmax": (c_status, [vp, C.c_int, C.c_int, i32p, vp]),
+    "pkv_argmax": (c_status, [vp, C.c_int, C.c_int, i32p, i32p, vp]),
     "pkv_graph_capture": (c_status, [vp, vp, i32p, i32p, C.c_int, i32p, C.c_int, C.c_int, vp, vp,
                                      vp, size_t, vp, C.POINTER(vp)]),
     "pkv_graph_replay": (c_status, [vp, vp]),
     "pkv_graph_destroy": (None, [vp]),
+    "pkv_graph_set_capture": (c_status, [vp, vp, i32p, C.c_int, i32p, i32p, C.c_int, i32p, C.c_int, vp, vp,
+                                         vp, size_t, vp, C.POINTER(vp)]),
+    "pkv_graph_set_replay": (c_status, [vp, C.c_int, vp, C.POINTER(C.c_int)]),
+    "pkv_graph_set_destroy": (None, [vp]),
     "pkv_alloc_create": (c_status, [C.c_int, C.c_uint64, C.POINTER(vp)]),
     "pkv_alloc_grow": (c_status, [vp, C.POINTER(C.c_int32), C.c_int, C.c_int, C.c_int]),
     "pkv_alloc_release": (c_status, [vp, C.POINTER(C.c_int32), C.c_int]),

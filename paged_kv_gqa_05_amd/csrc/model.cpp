@@ -39,6 +39,14 @@ struct pkv_graph {
   hipGraphExec_t exec = nullptr;
 };
 
+// One captured step per batch-size bucket over the same caller buffers.
+struct pkv_graph_set {
+  std::vector<int> buckets;  // strictly ascending
+  std::vector<pkv_graph*> graphs;
+  int32_t* tokens = nullptr;
+  int32_t* lens = nullptr;
+};
+
 namespace {
 
 struct StepBuffers {
@@ -298,10 +306,11 @@ pkv_status pkv_decode_step(const pkv_model* m, pkv_cache* cache, const int32_t* 
                       ws_bytes, static_cast<hipStream_t>(stream));
 }
 
-pkv_status pkv_argmax(const void* logits, int batch, int vocab, int32_t* tokens, pkv_stream_t stream) {
+pkv_status pkv_argmax(const void* logits, int batch, int vocab, int32_t* tokens, const int32_t* context_lens,
+                      pkv_stream_t stream) {
   if (!logits || !tokens) return fail(PKV_E_ARG, "NULL argument");
   if (batch < 1 || vocab < 1) return fail(PKV_E_ARG, "batch and vocab must be >= 1");
-  PKV_HIP(launch_argmax(logits, batch, vocab, tokens, static_cast<hipStream_t>(stream)));
+  PKV_HIP(launch_argmax(logits, batch, vocab, tokens, context_lens, static_cast<hipStream_t>(stream)));
   return PKV_OK;
 }
 
@@ -359,6 +368,65 @@ void pkv_graph_destroy(pkv_graph* g) {
   if (g->exec) (void)hipGraphExecDestroy(g->exec);
   if (g->graph) (void)hipGraphDestroy(g->graph);
   delete g;
+}
+
+void pkv_graph_set_destroy(pkv_graph_set* set) {
+  if (!set) return;
+  for (pkv_graph* g : set->graphs) pkv_graph_destroy(g);
+  delete set;
+}
+
+pkv_status pkv_graph_set_capture(const pkv_model* m, pkv_cache* cache, const int32_t* buckets, int n_buckets,
+                                 int32_t* tokens, const int32_t* bt, int bt_stride, int32_t* lens,
+                                 int max_context, void* logits, void* hidden_out, void* ws, size_t ws_bytes,
+                                 pkv_stream_t capture_stream, pkv_graph_set** out) {
+  if (!out) return fail(PKV_E_ARG, "out is NULL");
+  *out = nullptr;
+  if (!buckets || n_buckets < 1 || n_buckets > 64) return fail(PKV_E_ARG, "1 to 64 buckets required");
+  for (int i = 0; i < n_buckets; ++i)
+    if (buckets[i] < 1 || (i > 0 && buckets[i] <= buckets[i - 1]))
+      return fail(PKV_E_ARG, "buckets must be positive and strictly ascending");
+  for (int i = 0; i < n_buckets; ++i) {  // the workspace must serve every bucket
+    size_t need = 0;
+    pkv_status st = pkv_step_workspace_bytes(m, cache, buckets[i], max_context, &need);
+    if (st != PKV_OK) return st;
+    if (ws_bytes < need)
+      return fail(PKV_E_ARG, "workspace too small for bucket " + std::to_string(buckets[i]) + ": need " +
+                                 std::to_string(need) + " bytes");
+  }
+  pkv_graph_set* set = new (std::nothrow) pkv_graph_set();
+  if (!set) return fail(PKV_E_NOMEM, "host allocation failed");
+  set->buckets.assign(buckets, buckets + n_buckets);
+  set->tokens = tokens;
+  set->lens = lens;
+  for (int i = 0; i < n_buckets; ++i) {
+    pkv_graph* g = nullptr;
+    pkv_status st = pkv_graph_capture(m, cache, tokens, bt, bt_stride, lens, buckets[i], max_context, logits,
+                                      hidden_out, ws, ws_bytes, capture_stream, &g);
+    if (st != PKV_OK) {
+      pkv_graph_set_destroy(set);
+      return st;
+    }
+    set->graphs.push_back(g);
+  }
+  *out = set;
+  return PKV_OK;
+}
+
+pkv_status pkv_graph_set_replay(pkv_graph_set* set, int batch, pkv_stream_t stream, int* bucket_out) {
+  if (!set || set->graphs.empty()) return fail(PKV_E_STATE, "graph set is not captured");
+  if (batch < 1 || batch > set->buckets.back()) return fail(PKV_E_ARG, "batch outside the captured buckets");
+  size_t i = 0;
+  while (set->buckets[i] < batch) ++i;
+  const int bk = set->buckets[i];
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (bk > batch) {  // padding rows: inactive (length 0), token 0
+    PKV_HIP(launch_zero_i32(set->tokens + batch, bk - batch, s));
+    PKV_HIP(launch_zero_i32(set->lens + batch, bk - batch, s));
+  }
+  PKV_HIP(hipGraphLaunch(set->graphs[i]->exec, s));
+  if (bucket_out) *bucket_out = bk;
+  return PKV_OK;
 }
 
 }  // extern "C"

@@ -17,7 +17,8 @@ __global__ void embed_kernel(const h16* __restrict__ table, const int32_t* __res
     *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(src + i);
 }
 
-// Lowest index of the largest value per row; NaN logits never win.  One
+// Lowest index of the largest value per row (-1 for a row whose context
+// length is 0 when lengths are given); NaN logits never win.  One
 // workgroup of 1024 threads per row; when every row is 16-byte aligned (vec:
 // vocab % 8 == 0 and an aligned base) rows are read with 16-byte loads, four
 // in flight per thread.
@@ -29,8 +30,13 @@ __device__ __forceinline__ void argmax_take(float v, int i, float& best, int& id
 }
 
 __global__ void __launch_bounds__(1024) argmax_kernel(const h16* __restrict__ logits, int vocab,
-                                                      int32_t* __restrict__ out, int vec) {
+                                                      int32_t* __restrict__ out, int vec,
+                                                      const int32_t* __restrict__ lens) {
   const int b = blockIdx.x;
+  if (lens && lens[b] == 0) {  // inactive row
+    if (threadIdx.x == 0) out[b] = -1;
+    return;
+  }
   const h16* row = logits + (size_t)b * vocab;
   float best = -INFINITY;
   int idx = 0x7fffffff;
@@ -84,10 +90,11 @@ hipError_t launch_embed(const void* table, const int32_t* tokens, void* h, int b
   return hipGetLastError();
 }
 
-hipError_t launch_argmax(const void* logits, int batch, int vocab, int32_t* tokens, hipStream_t s) {
+hipError_t launch_argmax(const void* logits, int batch, int vocab, int32_t* tokens, const int32_t* lens,
+                         hipStream_t s) {
   const int vec = (vocab % 8 == 0) && (reinterpret_cast<uintptr_t>(logits) % 16 == 0);
   hipLaunchKernelGGL(argmax_kernel, dim3(batch), dim3(1024), 0, s, static_cast<const h16*>(logits), vocab,
-                     tokens, vec);
+                     tokens, vec, lens);
   return hipGetLastError();
 }
 

@@ -123,3 +123,16 @@ def test_validate_metadata():
         pkv.validate_metadata(bt, np.array([20, 49], np.int32), 4, 48)
     with pytest.raises(pkv.PkvError, match="bt_stride"):
         pkv.validate_metadata(bt, lens, 4, 49)
+
+
+def test_graph_set_argument_errors():
+    lib = pkv.lib()
+    out = C.c_void_p()
+    for buckets in ([4, 2], [0, 4], [3, 3]):
+        arr = (C.c_int32 * len(buckets))(*buckets)
+        assert lib.pkv_graph_set_capture(None, None, arr, len(buckets), None, None, 1, None, 16, None, None, None, 0,
+                                         None, C.byref(out)) == 1
+        assert b"ascending" in lib.pkv_last_error()
+    assert lib.pkv_graph_set_capture(None, None, None, 0, None, None, 1, None, 16, None, None, None, 0, None,
+                                     C.byref(out)) == 1
+    assert lib.pkv_graph_set_replay(None, 1, None, None) == 6

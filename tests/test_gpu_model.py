@@ -171,3 +171,56 @@ def test_graph_replay_matches_eager_and_sees_new_metadata(lib):
         el, _ = eager.gpu_step(eager.prompts[:, t])
         assert np.array_equal(gl.view(np.uint16), el.view(np.uint16)), t
     g.close()
+
+
+def test_graph_set_buckets_with_inactive_rows(lib):
+    """Buckets 1/4/8 over shared buffers: 3 active rows run in bucket 4, then 6
+    in bucket 8 (rows 3-5 join); active rows match the oracle, padding rows get
+    token -1 and never touch the cache."""
+    shape, mc, buckets = MID, 64, [1, 4, 8]
+    w = inp.model_weights(shape, 4001, bias=True, norm_jitter=True, std=0.05)
+    model = lib.Model(shape, weights_to_device(w), max_positions=mc)
+    stride = (mc + 15) // 16
+    nb = 8 * stride + 7
+    cache = lib.KVCache(shape.n_layers, nb, shape.n_kv_heads, shape.head_dim)
+    for layer in range(shape.n_layers):
+        for t_ in cache.layer(layer):
+            t_.zero_()
+    rng = np.random.default_rng(4002)
+    bt = rng.permutation(nb).astype(np.int32)[: 8 * stride].reshape(8, stride)
+    prompts = rng.integers(0, shape.vocab, size=(8, 12)).astype(np.int32)
+    lens = np.zeros(8, np.int32)
+    tok_d = torch.zeros(8, dtype=torch.int32, device="cuda")
+    lens_d = torch.zeros(8, dtype=torch.int32, device="cuda")
+    logits = torch.empty(8, shape.vocab, dtype=torch.float16, device="cuda")
+    ws = torch.empty(max(lib.step_workspace_bytes(model, cache, b, mc) for b in buckets), dtype=torch.uint8,
+                     device="cuda")
+    gs = lib.GraphSet(model, cache, buckets, tok_d, dev(bt), lens_d, mc, logits, ws)
+    kp = [np.full((nb, shape.n_kv_heads, 16, shape.head_dim), np.nan, np.float16) for _ in range(shape.n_layers)]
+    vp = [np.full((nb, shape.n_kv_heads, shape.head_dim, 16), np.nan, np.float16) for _ in range(shape.n_layers)]
+    cfg = oracle_config(shape)
+    out = torch.empty(8, dtype=torch.int32, device="cuda")
+    for phase, n in ((0, 3), (1, 6)):
+        for t in range(6):
+            lens[:n] += 1
+            tok = prompts[:n, 6 * phase + t]
+            host_tok = np.zeros(8, np.int32)
+            host_tok[:n] = tok
+            tok_d.copy_(torch.from_numpy(host_tok))
+            lens_d.copy_(torch.from_numpy(lens))
+            bk = gs.replay(n)
+            assert bk == (4 if n == 3 else 8)
+            lib.argmax(logits[:bk], out[:bk], context_lens=lens_d[:bk])
+            torch.cuda.synchronize()
+            rl, _ = oracle.decode_step(cfg, w, kp, vp, tok, bt[:n], lens[:n])
+            assert_parity(logits[:n].cpu().numpy(), rl, f"bucket {bk}, step {t}")
+            got = out[:bk].cpu().numpy()
+            assert np.all(got[n:] == -1)
+            assert lens_d[n:bk].cpu().numpy().tolist() == [0] * (bk - n)
+    # rows 6 and 7 were never active: their blocks are still zero
+    for layer in range(shape.n_layers):
+        k, v = cache.layer(layer)
+        k, v = k.cpu().numpy(), v.cpu().numpy()
+        for b in (6, 7):
+            assert not k[bt[b]].any() and not v[bt[b]].any()
+    gs.close()
