@@ -36,10 +36,12 @@ def candidates(logits, temperature, top_k, top_p):
     if top_p < 1.0:
         total = w.sum()
         vals = np.sort(w[keep])[::-1]
-        # mass carried by w >= vals[i]: every value equal to vals[i] included
-        uniq = np.unique(vals)[::-1]
-        mass = np.array([w[keep & (w >= t)].sum() for t in uniq])
-        tau = uniq[np.nonzero(mass >= top_p * total)[0][0]]
+        cum = np.cumsum(vals)
+        # The first position whose running mass reaches top_p * Z holds tau:
+        # every larger value ends its run of ties earlier, below the target,
+        # and the mass of w >= tau (its ties included) is at least cum there.
+        i = np.nonzero(cum >= top_p * total)[0]
+        tau = vals[i[0] if i.size else -1]
         keep &= w >= tau
     ids = np.nonzero(keep)[0]
     return ids, w[ids]

@@ -81,3 +81,18 @@ def test_draw_walks_kept_tokens_in_index_order():
     ids, w = candidates(lg, 1.0, 2, 1.0)                 # keeps 1 and 3 (tied at 2.0)
     assert ids.tolist() == [1, 3]
     assert sample_row(lg, 1.0, 2, 1.0, 0.49) == 1 and sample_row(lg, 1.0, 2, 1.0, 0.51) == 3
+
+
+def test_top_p_matches_enumeration_with_many_ties():
+    """Logits on a coarse grid (long runs of equal weights): the kept set is the
+    one found by trying every distinct weight from the top down."""
+    rng = np.random.default_rng(5)
+    lg = rng.integers(-4, 5, 300).astype(np.float16)
+    z = lg.astype(np.float64) / 0.9
+    w = np.exp(z - z.max())
+    for top_p in (0.0, 0.1, 0.35, 0.6, 0.95):
+        for t in np.unique(w)[::-1]:
+            if w[w >= t].sum() >= top_p * w.sum():
+                break
+        want = np.nonzero(w >= t)[0]
+        assert candidates(lg, 0.9, -1, top_p)[0].tolist() == want.tolist(), top_p
