@@ -239,6 +239,26 @@ pkv_status pkv_decode_step(const pkv_model* model, pkv_cache* cache, const int32
 pkv_status pkv_argmax(const void* logits, int batch, int vocab, int32_t* tokens, const int32_t* context_lens,
                       pkv_stream_t stream);
 
+/* Sampled token per row, after the forward pass (zingnex.cn article, section
+ * 支持的参数: temperature (0 = greedy), top_p, top_k (-1 = disabled)).  All
+ * per-row arrays are device memory, [batch]: temperature f32, top_k int32,
+ * top_p f32, uniform f32 in [0, 1) (the caller's random numbers; values
+ * outside are clamped).  For row b with T = temperature[b]:
+ *   T <= 0 (or NaN): the greedy token, as pkv_argmax;
+ *   z = logit / T; top_k > 0 keeps every token with z at or above the k-th
+ *   largest z (ties at the boundary kept); w = exp(z - max z);
+ *   top_p < 1 keeps every token with w at or above tau, the largest weight
+ *   whose kept mass reaches top_p * sum(w) (ties kept; top_p <= 0 keeps the
+ *   largest weight and its ties);
+ *   the result is the first kept token, in index order, whose running sum of
+ *   w exceeds uniform[b] * (kept mass).
+ * Non-finite logits are never kept.  context_lens (nullable): rows of length
+ * 0 get -1.  Sums are float32; a draw within rounding of a boundary of the
+ * cumulative mass may fall on either neighbour. */
+pkv_status pkv_sample(const void* logits, int batch, int vocab, const float* temperature, const int32_t* top_k,
+                      const float* top_p, const float* uniform, int32_t* tokens, const int32_t* context_lens,
+                      pkv_stream_t stream);
+
 /* ------------------------------------------------------------- graph replay */
 
 /* Capture one pkv_decode_step (same arguments) into a hipGraph on

@@ -215,6 +215,21 @@ class Graph:
     __del__ = close
 
 
+def sample(logits, temperature, top_k, top_p, uniform, tokens, context_lens=None, stream=None):
+    """Sampled tokens (temperature / top-k / top-p, inverse CDF with the given
+    uniforms); per-row parameter tensors on the device, [batch]."""
+    _need(logits, torch.float16, "logits")
+    _need(temperature, torch.float32, "temperature")
+    _need(top_k, torch.int32, "top_k")
+    _need(top_p, torch.float32, "top_p")
+    _need(uniform, torch.float32, "uniform")
+    _need(tokens, torch.int32, "tokens")
+    if context_lens is not None:
+        _need(context_lens, torch.int32, "context_lens")
+    _check(_lib.pkv_sample(_p(logits), logits.shape[0], logits.shape[1], _p(temperature), _p(top_k), _p(top_p),
+                           _p(uniform), _p(tokens), _p(context_lens), _stream(stream)))
+
+
 class GraphSet:
     """One captured decode step per batch-size bucket over shared buffers sized
     for the largest bucket; replay(n) runs rows [0, n) in the smallest bucket

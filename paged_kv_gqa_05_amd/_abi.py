@@ -49,6 +49,7 @@ SIGNATURES = {
     "pkv_decode_step": (c_status, [vp, vp, i32p, i32p, C.c_int, i32p, C.c_int, C.c_int, vp, vp,
                                    vp, size_t, vp]),
     "pkv_argmax": (c_status, [vp, C.c_int, C.c_int, i32p, i32p, vp]),
+    "pkv_sample": (c_status, [vp, C.c_int, C.c_int, vp, i32p, vp, vp, i32p, i32p, vp]),
     "pkv_graph_capture": (c_status, [vp, vp, i32p, i32p, C.c_int, i32p, C.c_int, C.c_int, vp, vp,
                                      vp, size_t, vp, C.POINTER(vp)]),
     "pkv_graph_replay": (c_status, [vp, vp]),

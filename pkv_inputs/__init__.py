@@ -281,3 +281,36 @@ def random_pools_torch(seed, num_blocks, n_kv_heads, head_dim, valid, device="cu
     k.masked_fill_(inval[:, None, :, None], float("nan"))
     v.masked_fill_(inval[:, None, None, :], float("nan"))
     return k, v
+
+
+class SamplingCase:
+    def __init__(self, logits, temperature, top_k, top_p, uniform, lens):
+        self.logits, self.temperature, self.top_k, self.top_p = logits, temperature, top_k, top_p
+        self.uniform, self.lens = uniform, lens
+
+
+def sampling_case(batch, vocab, seed, masked_rows=True):
+    """Logits shaped like a language model's: N(0, 2^2) background plus 20
+    peaked tokens (+U(4, 12)); every fourth row bans ~10% of the vocabulary
+    with -inf and every eighth holds one NaN.  Per-row parameters cycle through
+    temperature {0, 0.3, 0.7, 1, 1.5}, top_k {-1, 1, 5, 50, 1000, 0},
+    top_p {1, 0.9, 0.5, 0, 0.99, 0.2}; uniforms U[0, 1); every ninth row is
+    inactive (length 0)."""
+    rng = np.random.default_rng(seed)
+    lg = rng.normal(0.0, 2.0, (batch, vocab))
+    for b in range(batch):
+        peaks = rng.choice(vocab, size=min(20, vocab), replace=False)
+        lg[b, peaks] += rng.uniform(4.0, 12.0, peaks.size)
+        if masked_rows and b % 4 == 3:
+            banned = rng.random(vocab) < 0.1
+            banned[np.argmax(lg[b])] = False
+            lg[b, banned] = -np.inf
+        if masked_rows and b % 8 == 5:
+            lg[b, rng.integers(vocab)] = np.nan
+    temps = np.array([0.0, 0.3, 0.7, 1.0, 1.5], np.float32)
+    ks = np.array([-1, 1, 5, 50, 1000, 0], np.int32)
+    ps = np.array([1.0, 0.9, 0.5, 0.0, 0.99, 0.2], np.float32)
+    idx = np.arange(batch)
+    lens = np.where(idx % 9 == 8, 0, 1 + idx).astype(np.int32)
+    return SamplingCase(lg.astype(F16), temps[idx % 5], ks[(idx // 2) % 6], ps[(idx // 3) % 6],
+                        rng.random(batch).astype(np.float32), lens)
