@@ -252,8 +252,8 @@ pkv_status pkv_argmax(const void* logits, int batch, int vocab, int32_t* tokens,
  *   largest weight and its ties);
  *   the result is the first kept token, in index order, whose running sum of
  *   w exceeds uniform[b] * (kept mass).
- * Non-finite logits are never kept.  context_lens (nullable): rows of length
- * 0 get -1.  Sums are float32; a draw within rounding of a boundary of the
+ * Non-finite logits are never kept; a row with none finite gets 0.
+ * context_lens (nullable): rows of length 0 get -1.  vocab <= 2^24.  Sums are float32; a draw within rounding of a boundary of the
  * cumulative mass may fall on either neighbour. */
 pkv_status pkv_sample(const void* logits, int batch, int vocab, const float* temperature, const int32_t* top_k,
                       const float* top_p, const float* uniform, int32_t* tokens, const int32_t* context_lens,

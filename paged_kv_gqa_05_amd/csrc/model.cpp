@@ -318,6 +318,7 @@ pkv_status pkv_sample(const void* logits, int batch, int vocab, const float* tem
                       const float* top_p, const float* uniform, int32_t* tokens, const int32_t* context_lens,
                       pkv_stream_t stream) {
   if (batch < 1 || vocab < 1) return fail(PKV_E_ARG, "batch and vocab must be >= 1");
+  if (vocab > (1 << 24)) return fail(PKV_E_ARG, "vocab must be <= 2^24");
   if (!logits || !temperature || !top_k || !top_p || !uniform || !tokens) return fail(PKV_E_ARG, "NULL argument");
   PKV_HIP(launch_sample(logits, batch, vocab, temperature, top_k, top_p, uniform, context_lens, tokens,
                         static_cast<hipStream_t>(stream)));

@@ -4,18 +4,22 @@
 // greedy, top_p, top_k with -1 = disabled; rvLLM post, section "CUDA 그래프
 // 리플레이": sampling stays outside the graph).
 //
-// Per row (one workgroup of 1024 threads):
+// Per row (one workgroup of 1024 threads), for T > 0:
 //   z = logit / T; top-k keeps every token with z at or above the k-th
 //   largest (ties kept); w = exp(z - max z); top-p keeps every token with w at
 //   or above tau, the largest weight whose kept mass reaches top_p * sum w
 //   (ties kept); the draw takes the first kept token in index order whose
 //   running sum of w exceeds u * (kept mass).
-// Both thresholds are found by radix descent over order-preserving 32-bit
-// keys, 8 bits per pass over the row (the k-th largest by counts; tau by the
-// mass carried per bin), so nothing is sorted.  Non-finite logits are never
-// kept.  Sums are reduced in a fixed order (per-thread strides, then a fixed
-// tree), so a row's result does not vary from run to run except through the
-// top-p mass bins, which add in arrival order.
+// z and w are increasing functions of the f16 logit, so both thresholds are
+// found as a logit: radix descent over the logit's 16-bit order-preserving
+// key, an 11-bit digit then a 5-bit one, counting tokens (top-k) or summing
+// their w (top-p) per bin.  Masses are summed in 64-bit fixed point (w times
+// 2^40, w <= 1), so every sum is exact and order-free and a row's result is
+// the same on every run.  The kept sets, ties included, are then exactly
+// the ones the definitions give.  Passes over the row: max and count (fused
+// into the first top-k pass), two for top-k, two for top-p (the first also
+// gives sum w), one to sum w per wave segment and per 64-unit step of it;
+// then one wave loads the step where the draw lands.  Non-finite logits are never kept.
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -24,253 +28,361 @@ namespace {
 typedef _Float16 h16;
 constexpr int kST = 1024;
 constexpr int kSW = kST / 64;
+constexpr int kBins = 2048;
+constexpr int kMaxSteps = 64;                         // step sums kept per wave segment                           // the first digit: key bits 15..5
+constexpr uint32_t kKeyNegInf = 0x03ffu, kKeyPosInf = 0xfc00u;
 
-// Larger float -> larger key (negative floats reversed); -0 and +0 share a key.
-__device__ __forceinline__ uint32_t fkey(float f) {
-  const uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+// Larger logit -> larger key; -0 and +0 share a key; NaNs fall outside
+// [key(-inf), key(+inf)].
+__device__ __forceinline__ uint32_t hkey(uint32_t u) {
+  if ((u & 0x7fffu) == 0) u = 0;
+  return (u & 0x8000u) ? (~u & 0xffffu) : (u | 0x8000u);
 }
+__device__ __forceinline__ bool key_finite(uint32_t k) { return k > kKeyNegInf && k < kKeyPosInf; }
+__device__ __forceinline__ float key_value(uint32_t k) {
+  const uint32_t u = (k & 0x8000u) ? (k & 0x7fffu) : (~k & 0xffffu);
+  return (float)__builtin_bit_cast(h16, (uint16_t)u);
+}
+__device__ __forceinline__ float logit_of(uint32_t u) { return (float)__builtin_bit_cast(h16, (uint16_t)u); }
 
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  float t = 0.f;
-  for (int w = 0; w < kSW; ++w) t += red[w];
-  return t;
-}
-__device__ __forceinline__ float block_max(float v, float* red) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  float t = -INFINITY;
-  for (int w = 0; w < kSW; ++w) t = fmaxf(t, red[w]);
-  return t;
-}
+// A unit is eight logits (one 16-byte load) when VEC, else one logit.
+template <bool VEC>
+struct Row {
+  static constexpr int kElems = VEC ? 8 : 1;
+  const uint16_t* p;
+  int vocab;
+  __device__ int units() const { return VEC ? vocab >> 3 : vocab; }
+  __device__ uint4 load(int unit) const {
+    if (VEC) return reinterpret_cast<const uint4*>(p)[unit];
+    return make_uint4(p[unit], 0u, 0u, 0u);
+  }
+  __device__ static uint32_t elem(const uint4& q, int j) {
+    const uint32_t w = j < 2 ? q.x : (j < 4 ? q.y : (j < 6 ? q.z : q.w));
+    return (j & 1) ? (w >> 16) : (w & 0xffffu);
+  }
+};
 
-// f(i, logit) for the tokens [i0, i1) of a row.  With vec set, the row is
-// 16-byte aligned and i0, i1 are multiples of 8 (or i1 = vocab, itself one),
-// so eight logits come per 16-byte load.
-template <class F>
-__device__ __forceinline__ void for_range(const h16* row, int i0, int i1, int step, bool vec, F&& f) {
-  if (vec) {
-    const uint4* rv = reinterpret_cast<const uint4*>(row);
-    for (int v = (i0 >> 3); v < (i1 >> 3); v += step) {
-      const uint4 q = rv[v];
-      const h16* h = reinterpret_cast<const h16*>(&q);
+// f(index, f16 bits) for every token, token unit v by thread v % kST; four
+// units in flight per thread.
+template <bool VEC, class F>
+__device__ __forceinline__ void for_row(const Row<VEC>& r, F&& f) {
+  const int n = r.units();
+  for (int v0 = threadIdx.x; v0 < n; v0 += 4 * kST) {
+    uint4 q[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) f(v * 8 + j, (float)h[j]);
+    for (int u = 0; u < 4; ++u) q[u] = r.load(min(v0 + u * kST, n - 1));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + u * kST;
+      if (v < n) {
+#pragma unroll
+        for (int j = 0; j < Row<VEC>::kElems; ++j) f(v * Row<VEC>::kElems + j, Row<VEC>::elem(q[u], j));
+      }
     }
-  } else {
-    for (int i = i0; i < i1; i += step) f(i, (float)row[i]);
   }
 }
-// The whole row, token i visited by thread (i / 8) % kST (vec) or i % kST.
-template <class F>
-__device__ __forceinline__ void for_row(const h16* row, int vocab, bool vec, F&& f) {
-  for_range(row, vec ? threadIdx.x * 8 : threadIdx.x, vocab, kST, vec, f);
+
+typedef unsigned long long u64;
+
+// w in [0, 1] as a 2^-40 fixed-point integer (sums of up to 2^24 stay below 2^64)
+__device__ __forceinline__ u64 wfix(float w) { return (u64)(w * 0x1p40f); }
+
+struct Smem {
+  union {
+    uint32_t i[2 * kBins];
+    u64 l[kBins];
+  } hist;
+  u64 wl[kSW];
+  float steps[kSW * kMaxSteps];
+  float wf[kSW];
+  int wi[kSW];
+  int bin;
+  u64 before, total, target;
+  int tok;
+};
+
+// Descending selection over the kBins bins (32-bit counts, or 64-bit masses
+// when kWide): the first bin, from the top, at which above + (all higher
+// bins) + (the bin itself) reaches target_abs + ceil(frac * (sum of all
+// bins)); bin 0 if none does.  Leaves the bin, the amount above it (above
+// included), the bins' sum and the target in sm.  Only non-empty bins are
+// taken, so a target of 0 gives the highest non-empty bin.
+template <bool kWide>
+__device__ void select_bin(Smem& sm, u64 above, u64 target_abs, float frac) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b0 = kBins - 1 - 2 * tid;
+  const u64 a = kWide ? sm.hist.l[b0] : sm.hist.i[b0];
+  const u64 c = kWide ? sm.hist.l[b0 - 1] : sm.hist.i[b0 - 1];
+  const u64 loc = a + c;
+  u64 incl = loc;
+  for (int o = 1; o < 64; o <<= 1) {
+    const u64 t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) sm.wl[wave] = incl;
+  __syncthreads();
+  u64 off = above, tot = 0;
+  for (int w = 0; w < kSW; ++w) {
+    const u64 x = sm.wl[w];
+    if (w < wave) off += x;
+    tot += x;
+  }
+  const u64 target = target_abs + (frac > 0.f ? (u64)ceil((double)frac * (double)tot) : 0ull);
+  const u64 before = off + incl - loc;
+  int cand = 2 * kBins;
+  // a bin is taken only if it holds something: with target 0 the first
+  // non-empty bin, otherwise the crossing bin (never empty anyway)
+  if (a > 0 && before + a >= target)
+    cand = 2 * tid;
+  else if (c > 0 && before + loc >= target)
+    cand = 2 * tid + 1;
+  for (int o = 32; o > 0; o >>= 1) cand = min(cand, __shfl_xor(cand, o, 64));
+  if (lane == 0) sm.wi[wave] = cand;
+  __syncthreads();
+  int j = 2 * kBins;
+  for (int w = 0; w < kSW; ++w) j = min(j, sm.wi[w]);
+  if (j == 2 * kBins) j = kBins - 1;
+  if (tid == (j >> 1)) {
+    sm.bin = kBins - 1 - j;
+    sm.before = (j & 1) ? before + a : before;
+  }
+  if (tid == 0) sm.total = tot, sm.target = target;
+  __syncthreads();
 }
 
-__global__ void __launch_bounds__(kST) sample_kernel(const h16* __restrict__ logits, int vocab, int vec,
+__device__ __forceinline__ void clear_hist(Smem& sm) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sm.hist.i[threadIdx.x + j * kST] = 0;
+  __syncthreads();
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(kST) sample_kernel(const uint16_t* __restrict__ logits, int vocab,
                                                      const float* __restrict__ temperature,
                                                      const int32_t* __restrict__ top_k,
                                                      const float* __restrict__ top_p,
                                                      const float* __restrict__ uniform,
                                                      const int32_t* __restrict__ lens, int32_t* __restrict__ out) {
-  __shared__ float red[kSW];
-  __shared__ int hist[256];
-  __shared__ float mass[256];
-  __shared__ int bc_i[2];
-  __shared__ float bc_f[2];
-  __shared__ int s_tok;
-  const int b = blockIdx.x, tid = threadIdx.x;
+  __shared__ Smem sm;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (lens && lens[b] == 0) {  // inactive row
     if (tid == 0) out[b] = -1;
     return;
   }
-  const h16* row = logits + (size_t)b * vocab;
+  const Row<VEC> row{logits + (size_t)b * vocab, vocab};
   const float T = temperature[b];
 
-  if (!(T > 0.f)) {  // greedy: lowest index of the largest logit
-    float best = -INFINITY;
-    int idx = 0x7fffffff;
-    for_row(row, vocab, vec, [&](int i, float v) {
-      if (v > best || (v == best && i < idx)) best = v, idx = i;
+  if (!(T > 0.f)) {  // greedy: lowest index of the largest non-NaN logit
+    unsigned long long best = 0;
+    for_row(row, [&](int i, uint32_t u) {
+      const uint32_t k = hkey(u);
+      const unsigned long long c = ((unsigned long long)k << 32) | (0xffffffffu - (uint32_t)i);
+      if (k >= kKeyNegInf && k <= kKeyPosInf && c > best) best = c;
     });
+    uint32_t hi = (uint32_t)(best >> 32), lo = (uint32_t)best;
     for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(best, o, 64);
-      const int oi = __shfl_xor(idx, o, 64);
-      if (ov > best || (ov == best && oi < idx)) best = ov, idx = oi;
+      const uint32_t oh = __shfl_xor(hi, o, 64), ol = __shfl_xor(lo, o, 64);
+      if (oh > hi || (oh == hi && ol > lo)) hi = oh, lo = ol;
     }
-    if ((tid & 63) == 0) red[tid >> 6] = best, hist[tid >> 6] = idx;
+    if (lane == 0) sm.hist.i[2 * wave] = hi, sm.hist.i[2 * wave + 1] = lo;
     __syncthreads();
     if (tid == 0) {
-      for (int w = 1; w < kSW; ++w)
-        if (red[w] > best || (red[w] == best && hist[w] < idx)) best = red[w], idx = hist[w];
-      out[b] = idx == 0x7fffffff ? 0 : idx;
+      for (int w = 0; w < kSW; ++w) {
+        const uint32_t oh = (uint32_t)sm.hist.i[2 * w], ol = (uint32_t)sm.hist.i[2 * w + 1];
+        if (oh > hi || (oh == hi && ol > lo)) hi = oh, lo = ol;
+      }
+      out[b] = hi == 0 ? 0 : (int)(0xffffffffu - lo);
     }
     return;
   }
-  // z = logit / T; a non-finite z is never kept
+  const float inv_t = 1.f / T;
 
-  // ---- max z and the count of finite z
-  float m = -INFINITY, cnt = 0.f;
-  for_row(row, vocab, vec, [&](int, float x) {
-    const float z = x / T;
-    if (isfinite(z)) m = fmaxf(m, z), cnt += 1.f;
-  });
-  m = block_max(m, red);
-  const int n_finite = (int)block_sum(cnt, red);
-
-  // ---- top-k: key of the k-th largest finite z (radix select by counts)
+  // ---- pass 1: largest finite key; with top-k also the first-digit counts
   const int k = top_k[b];
-  const bool use_k = k > 0 && k < n_finite;
-  uint32_t kkey = 0;
-  if (use_k) {
-    uint32_t prefix = 0, mask = 0;
-    int need = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += kST) hist[i] = 0;
+  if (k > 0) clear_hist(sm);
+  uint32_t kmax = 0;
+  for_row(row, [&](int, uint32_t u) {
+    const uint32_t key = hkey(u);
+    if (!key_finite(key)) return;
+    kmax = max(kmax, key);
+    if (k > 0) atomicAdd(&sm.hist.i[key >> 5], 1u);
+  });
+  for (int o = 32; o > 0; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  if (lane == 0) sm.wi[wave] = (int)kmax;
+  __syncthreads();
+  for (int w = 0; w < kSW; ++w) kmax = max(kmax, (uint32_t)sm.wi[w]);
+  const float mx = key_value(kmax);  // unused when no logit is finite
+  __syncthreads();
+
+  // ---- top-k: the k-th largest key (counts, ties at it all kept)
+  uint32_t thr = kKeyNegInf + 1;  // smallest finite key
+  if (k > 0) {
+    select_bin<false>(sm, 0, (u64)k, 0.f);
+    if ((u64)k < sm.total) {  // else every finite logit is kept
+      const uint32_t hb = sm.bin;
+      const u64 need = (u64)k - sm.before;
       __syncthreads();
-      for_row(row, vocab, vec, [&](int, float x) {
-        const float z = x / T;
-        if (!isfinite(z)) return;
-        const uint32_t key = fkey(z);
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+      clear_hist(sm);
+      for_row(row, [&](int, uint32_t u) {
+        const uint32_t key = hkey(u);
+        if (key_finite(key) && (key >> 5) == hb) atomicAdd(&sm.hist.i[key & 31], 1u);
       });
       __syncthreads();
-      if (tid == 0) {
-        int cum = 0, d = 255;
-        for (; d > 0; --d) {
-          if (cum + hist[d] >= need) break;
-          cum += hist[d];
-        }
-        bc_i[0] = d;
-        bc_i[1] = need - cum;
-      }
-      __syncthreads();
-      prefix |= (uint32_t)bc_i[0] << shift;
-      mask |= 255u << shift;
-      need = bc_i[1];
-      __syncthreads();
+      select_bin<false>(sm, 0, need, 0.f);
+      thr = (hb << 5) | sm.bin;
     }
-    kkey = prefix;
+    __syncthreads();
   }
-  auto kept_k = [&](float z) { return isfinite(z) && (!use_k || fkey(z) >= kkey); };
+  auto kept = [&](uint32_t key) { return key_finite(key) && key >= thr; };
+  // w = exp((x - max) / T) on the hardware's base-2 exponential
+  const float c2 = inv_t * 1.44269504088896341f;
+  auto weight_of = [&](float x) { return __builtin_amdgcn_exp2f((x - mx) * c2); };
+  auto weight = [&](uint32_t u) { return weight_of(logit_of(u)); };
 
-  // ---- total weight of the top-k set
-  float zs = 0.f;
-  for_row(row, vocab, vec, [&](int, float x) {
-    const float z = x / T;
-    if (kept_k(z)) zs += expf(z - m);
-  });
-  const float Z = block_sum(zs, red);
-
-  // ---- top-p: tau, the largest weight whose kept mass reaches top_p * Z
-  float p = top_p[b];
-  const bool use_p = p < 1.f;  // NaN: disabled
-  if (use_p && !(p > 0.f)) p = 1e-30f;  // keep only the largest weight (and its ties)
-  uint32_t pkey = 0;
-  if (use_p) {
-    const float target = p * Z;
-    uint32_t prefix = 0, mask = 0;
-    float above = 0.f;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += kST) mass[i] = 0.f;
-      __syncthreads();
-      for_row(row, vocab, vec, [&](int, float x) {
-        const float z = x / T;
-        if (!kept_k(z)) return;
-        const float w = expf(z - m);
-        const uint32_t key = fkey(w);
-        if ((key & mask) == prefix) atomicAdd(&mass[(key >> shift) & 255], w);
-      });
-      __syncthreads();
-      if (tid == 0) {
-        float cum = above;
-        int d = 255;
-        for (; d > 0; --d) {
-          if (cum + mass[d] >= target) break;
-          cum += mass[d];
-        }
-        bc_i[0] = d;
-        bc_f[0] = cum;
-      }
-      __syncthreads();
-      prefix |= (uint32_t)bc_i[0] << shift;
-      mask |= 255u << shift;
-      above = bc_f[0];
-      __syncthreads();
-    }
-    pkey = prefix;
-  }
-  auto weight = [&](float x) {  // w if the token is kept, else 0
-    const float z = x / T;
-    if (!kept_k(z)) return 0.f;
-    const float w = expf(z - m);
-    return (!use_p || fkey(w) >= pkey) ? w : 0.f;
-  };
-
-  // ---- the draw: contiguous chunks per thread, prefix over chunks
-  const int chunk = vec ? 8 * ((vocab + 8 * kST - 1) / (8 * kST)) : (vocab + kST - 1) / kST;
-  const int i0 = min(tid * chunk, vocab), i1 = min(i0 + chunk, vocab);
-  float cs = 0.f;
-  int last = -1;
-  for_range(row, i0, i1, 1, vec, [&](int i, float x) {
-    const float w = weight(x);
-    if (w > 0.f) cs += w, last = i;
-  });
-  // inclusive scan of the chunk sums in thread order
-  float incl = cs;
-  for (int o = 1; o < 64; o <<= 1) {
-    const float t = __shfl_up(incl, o, 64);
-    if ((tid & 63) >= o) incl += t;
-  }
-  __syncthreads();  // every read of red by the reductions above is done
-  if ((tid & 63) == 63) red[tid >> 6] = incl;
-  __syncthreads();
-  float wave_off = 0.f;
-  for (int w = 0; w < (tid >> 6); ++w) wave_off += red[w];
-  float total = 0.f;
-  for (int w = 0; w < kSW; ++w) total += red[w];
-  const float excl = wave_off + incl - cs;
-  float u = uniform[b];
-  u = u < 0.f ? 0.f : (u >= 1.f ? 0.99999994f : u);
-  const float target = u * total;
-  // the first thread whose running total passes the target walks its chunk;
-  // with no such thread (rounding), the last kept token of the row
-  int first = (cs > 0.f && excl + cs > target) ? tid : kST;
-  int lk = last;
-  for (int o = 32; o > 0; o >>= 1) {
-    first = min(first, __shfl_xor(first, o, 64));
-    lk = max(lk, __shfl_xor(lk, o, 64));
-  }
-  if ((tid & 63) == 0) {
-    hist[tid >> 6] = first;
-    hist[kSW + (tid >> 6)] = lk;
-  }
-  __syncthreads();
-  int f = kST, l = -1;
-  for (int w = 0; w < kSW; ++w) f = min(f, hist[w]), l = max(l, hist[kSW + w]);
-  if (tid == 0 && f == kST) s_tok = l < 0 ? 0 : l;
-  if (tid == f) {
-    float run = excl;
-    int tok = -1;
-    for_range(row, i0, i1, 1, vec, [&](int i, float x) {
-      const float w = weight(x);
-      if (tok < 0 && w > 0.f) {
-        run += w;
-        if (run > target) tok = i;
-      }
+  // ---- top-p: the key of tau (mass per bin; the first pass also gives sum w)
+  const float p = top_p[b];
+  if (p < 1.f) {  // NaN: off
+    const float frac = p > 0.f ? p : 0.f;  // 0 keeps the largest weight and its ties
+    clear_hist(sm);
+    for_row(row, [&](int, uint32_t u) {
+      const uint32_t key = hkey(u);
+      if (kept(key)) atomicAdd(&sm.hist.l[key >> 5], wfix(weight(u)));
     });
-    s_tok = tok < 0 ? last : tok;
+    __syncthreads();
+    select_bin<true>(sm, 0, 0, frac);
+    const uint32_t hb = sm.bin;
+    const u64 above = sm.before, target = sm.target;
+    __syncthreads();
+    clear_hist(sm);
+    // the second digit completes the key, so a bin's mass is its count times
+    // the weight of that one logit value: the same integers as summing per token
+    for_row(row, [&](int, uint32_t u) {
+      const uint32_t key = hkey(u);
+      if (kept(key) && (key >> 5) == hb) atomicAdd(&sm.hist.i[key & 31], 1u);
+    });
+    __syncthreads();
+    const uint32_t cnt = tid < 32 ? sm.hist.i[tid] : 0u;
+    __syncthreads();
+    if (tid < 32) sm.hist.l[tid] = cnt ? (u64)cnt * wfix(weight_of(key_value((hb << 5) | tid))) : 0ull;
+    __syncthreads();
+    select_bin<true>(sm, above, target, 0.f);
+    thr = max(thr, (hb << 5) | sm.bin);
+    __syncthreads();
+  }
+
+  // ---- the draw: each wave sums w over its contiguous segment of units, 64
+  // units per step, keeping the step sums (up to kMaxSteps) for the walk
+  const int n = row.units();
+  const int seg = (n + kSW - 1) / kSW;
+  const int s0 = min(wave * seg, n), s1 = min(s0 + seg, n);
+  const int nsteps = (s1 - s0 + 63) >> 6;
+  float ws = 0.f;
+  int lastk = -1;
+  for (int st0 = 0; st0 < nsteps; st0 += 4) {
+    uint4 q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) q[u] = row.load(min(s0 + (st0 + u) * 64 + lane, s1 - 1));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int st = st0 + u, v = s0 + st * 64 + lane;
+      if (st >= nsteps) break;
+      float uw = 0.f;
+      if (v < s1) {
+#pragma unroll
+        for (int j = 0; j < Row<VEC>::kElems; ++j) {
+          const uint32_t e = Row<VEC>::elem(q[u], j);
+          if (kept(hkey(e))) uw += weight(e), lastk = v * Row<VEC>::kElems + j;
+        }
+      }
+      // butterfly: every lane ends with the same bits (each add is commutative)
+      for (int o = 32; o > 0; o >>= 1) uw += __shfl_xor(uw, o, 64);
+      if (lane == 0 && st < kMaxSteps) sm.steps[wave * kMaxSteps + st] = uw;
+      ws += uw;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) lastk = max(lastk, __shfl_xor(lastk, o, 64));
+  if (lane == 0) sm.wf[wave] = ws, sm.wi[wave] = lastk;
+  __syncthreads();
+  float total = 0.f;
+  for (int w = 0; w < kSW; ++w) total += sm.wf[w];
+  float uu = uniform[b];
+  uu = uu < 0.f ? 0.f : (uu >= 1.f ? 0.99999994f : uu);
+  const float target = uu * total;
+  // the first segment whose running total passes the target; none (rounding,
+  // or nothing kept): the last kept token of the row
+  int hit = -1;
+  float run = 0.f;
+  int last_all = -1;
+  for (int w = 0; w < kSW; ++w) {
+    last_all = max(last_all, sm.wi[w]);
+    if (hit < 0 && sm.wf[w] > 0.f && run + sm.wf[w] > target) hit = w;
+    if (hit < 0) run += sm.wf[w];
+  }
+  if (tid == 0) sm.tok = last_all < 0 ? 0 : last_all;
+  __syncthreads();
+  if (wave == hit) {
+    // the step where the draw lands (from the kept step sums), else every step
+    int stb = 0, ste = nsteps;
+    if (nsteps <= kMaxSteps) {
+      int st = 0;
+      for (; st < nsteps; ++st) {
+        const float t = sm.steps[wave * kMaxSteps + st];
+        if (t > 0.f && run + t > target) break;
+        run += t;
+      }
+      stb = st;
+      ste = st < nsteps ? st + 1 : st;
+    }
+    int tok = -1, seen = -1;
+    for (int st = stb; st < ste && tok < 0; ++st) {
+      const int v = s0 + st * 64 + lane;
+      const uint4 q = row.load(min(v, s1 - 1));
+      float uw = 0.f;
+      int ul = -1;
+      if (v < s1) {
+#pragma unroll
+        for (int j = 0; j < Row<VEC>::kElems; ++j) {
+          const uint32_t e = Row<VEC>::elem(q, j);
+          if (kept(hkey(e))) uw += weight(e), ul = v * Row<VEC>::kElems + j;
+        }
+      }
+      seen = max(seen, ul);
+      float incl = uw;
+      for (int o = 1; o < 64; o <<= 1) {
+        const float t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      const unsigned long long m = __ballot(uw > 0.f && run + incl > target);
+      if (m) {
+        const int f = __ffsll((long long)m) - 1;
+        if (lane == f) {
+          float r = run + incl - uw;
+          tok = ul;  // rounding: the unit's last kept token
+#pragma unroll
+          for (int j = 0; j < Row<VEC>::kElems; ++j) {
+            const uint32_t e = Row<VEC>::elem(q, j);
+            if (kept(hkey(e))) {
+              r += weight(e);
+              if (r > target) {
+                tok = v * Row<VEC>::kElems + j;
+                break;
+              }
+            }
+          }
+          sm.tok = tok;
+        }
+        tok = __shfl(tok, f, 64);
+      } else {
+        run += __shfl(incl, 63, 64);
+      }
+    }
+    // rounding left the draw past every walked token: the last kept one seen,
+    // else the segment's last kept token
+    for (int o = 32; o > 0; o >>= 1) seen = max(seen, __shfl_xor(seen, o, 64));
+    if (tok < 0 && lane == 0) sm.tok = seen >= 0 ? seen : sm.wi[wave];
   }
   __syncthreads();
-  if (tid == 0) out[b] = s_tok;
+  if (tid == 0) out[b] = sm.tok;
 }
 
 }  // namespace
@@ -278,9 +390,13 @@ __global__ void __launch_bounds__(kST) sample_kernel(const h16* __restrict__ log
 hipError_t launch_sample(const void* logits, int batch, int vocab, const float* temperature, const int32_t* top_k,
                          const float* top_p, const float* uniform, const int32_t* lens, int32_t* tokens,
                          hipStream_t s) {
-  const int vec = (vocab % 8 == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0) ? 1 : 0;
-  hipLaunchKernelGGL(sample_kernel, dim3(batch), dim3(kST), 0, s, static_cast<const h16*>(logits), vocab, vec,
-                     temperature, top_k, top_p, uniform, lens, tokens);
+  const auto* l = static_cast<const uint16_t*>(logits);
+  if (vocab % 8 == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0)
+    hipLaunchKernelGGL(sample_kernel<true>, dim3(batch), dim3(kST), 0, s, l, vocab, temperature, top_k, top_p,
+                       uniform, lens, tokens);
+  else
+    hipLaunchKernelGGL(sample_kernel<false>, dim3(batch), dim3(kST), 0, s, l, vocab, temperature, top_k, top_p,
+                       uniform, lens, tokens);
   return hipGetLastError();
 }
 

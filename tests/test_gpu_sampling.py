@@ -83,6 +83,7 @@ def check_rows(case, got):
     (45, 1000, 2),       # small vocabulary, 16-byte row loads
     (36, 997, 3),        # odd vocabulary: element loads, ragged per-thread chunks
     (10, 37, 4),         # fewer tokens than threads
+    (12, 70001, 8),      # element loads, wave segments longer than the kept step sums
 ])
 def test_sample_parity(lib, batch, vocab, seed):
     case = inp.sampling_case(batch, vocab, seed)
