@@ -49,10 +49,11 @@ from .decoder import (
     decode_step,
     greedy_argmax,
     causal_forward,
+    prefill,
 )
 
 __all__ = [
     "e4m3_decode", "e4m3_encode", "e4m3_quantize", "e4m3_table", "candidates", "sample", "sample_row", "ModelConfig", "rmsnorm", "silu", "rope",
     "rope_angles", "paged_attention", "paged_attention_batch", "kv_append",
-    "decode_layer", "decode_step", "greedy_argmax", "causal_forward",
+    "decode_layer", "decode_step", "greedy_argmax", "causal_forward", "prefill",
 ]

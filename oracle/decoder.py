@@ -287,6 +287,38 @@ def decode_step(cfg, weights, k_pools, v_pools, tokens, block_tables, ctx_lens,
     return logits, h
 
 
+def prefill(cfg, weights, k_pools, v_pools, tokens, seq_starts, prior_lens, block_tables,
+            acc=np.float64, k_scales=None, v_scales=None):
+    """Batched, chunked prefill over the paged cache.
+
+    Sequence s brings the new tokens tokens[seq_starts[s]:seq_starts[s+1]] at
+    positions prior_lens[s], prior_lens[s] + 1, ... (prior_lens[s] tokens are
+    already cached).  Reading of the multi-token causal step (the post's
+    "PagedAttention과 FlashAttention-3" section names causal multi-token
+    attention over the same cache): in every layer the k and v of all new
+    tokens are appended first, and new token j of sequence s then attends over
+    positions [0, prior_lens[s] + j] of its own sequence.  That is the decode
+    layer applied to each new token as a row of its own, with context length
+    prior_lens[s] + j + 1 and its sequence's block-table row.  Returns (logits
+    [S, V] f16 of each sequence's last new token, hidden [T, H] f16 of every
+    new token).  The pools are updated in place.
+    """
+    starts = np.asarray(seq_starts, dtype=np.int64)
+    n_seq = starts.shape[0] - 1
+    seq_of = np.repeat(np.arange(n_seq), np.diff(starts))
+    j = np.arange(starts[-1]) - starts[seq_of]
+    lens = (np.asarray(prior_lens, dtype=np.int64)[seq_of] + j + 1).astype(np.int32)
+    rows_bt = np.asarray(block_tables)[seq_of]
+    h = np.asarray(weights["embed"])[np.asarray(tokens, dtype=np.int64)].astype(F16)
+    for li, lw in enumerate(weights["layers"]):
+        ks = None if k_scales is None else k_scales[li]
+        vs = None if v_scales is None else v_scales[li]
+        h = decode_layer(cfg, lw, h, k_pools[li], v_pools[li], rows_bt, lens, acc, ks, vs)
+    n = rmsnorm(h[starts[1:] - 1], weights["w_final_norm"], cfg.rms_eps, acc)
+    logits = _linear(n, weights["w_lm_head"], acc).astype(F16)
+    return logits, h
+
+
 def greedy_argmax(logits):
     """Greedy token: index of the largest f16 logit, lowest index on ties."""
     return np.argmax(np.asarray(logits), axis=-1).astype(np.int32)

@@ -7,7 +7,10 @@
   a complex-number RoPE;
 * rows are independent (batch composition does not change a row);
 * the append writes exactly the slot at pos = ctx - 1 and nothing else;
-* greedy argmax takes the lowest index on ties.
+* greedy argmax takes the lowest index on ties;
+* prefill of several prompts at once == the textbook causal forward of each
+  prompt (last logits and every cached K and V), and prefill in two chunks ==
+  prefill in one == token-by-token decode.
 The end-to-end logits of a random-weight model are otherwise parity unpinned
 (the pages print no logits or tokens).
 """
@@ -15,7 +18,7 @@ import numpy as np
 import torch
 import torch.nn.functional as F
 
-from oracle import ModelConfig, decode_step, causal_forward, decode_layer, greedy_argmax
+from oracle import ModelConfig, decode_step, causal_forward, decode_layer, greedy_argmax, prefill
 import pkv_inputs as inp
 
 SHAPE = inp.Shape(hidden=128, n_q_heads=4, n_kv_heads=2, head_dim=32, ffn=160, vocab=300, n_layers=2)
@@ -135,3 +138,71 @@ def test_layer_append_touches_only_its_slot():
 def test_argmax_lowest_index_on_ties():
     lg = np.array([[0.5, 2.0, 2.0, -1.0], [3.0, 3.0, 3.0, 3.0], [-5, -4, -4.5, -4]], np.float16)
     assert greedy_argmax(lg).tolist() == [1, 0, 1]
+
+
+def _empty_pools(nb):
+    kp = [np.full((nb, CFG.n_kv_heads, BS, CFG.head_dim), np.nan, np.float16) for _ in range(CFG.n_layers)]
+    vp = [np.full((nb, CFG.n_kv_heads, CFG.head_dim, BS), np.nan, np.float16) for _ in range(CFG.n_layers)]
+    return kp, vp
+
+
+def test_prefill_equals_causal_forward():
+    """Three prompts of different lengths in one prefill from an empty cache:
+    each sequence's last logits and every cached K and V equal the textbook
+    causal forward of that prompt alone."""
+    w = _weights(61)
+    rng = np.random.default_rng(62)
+    lens = [23, 1, 37]
+    prompts = [rng.integers(0, SHAPE.vocab, size=n).astype(np.int32) for n in lens]
+    need = [(n + BS - 1) // BS for n in lens]
+    nb = sum(need) + 2
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.full((3, max(need)), -1, np.int32)
+    off = 0
+    for s, k in enumerate(need):
+        bt[s, :k] = perm[off:off + k]
+        off += k
+    kp, vp = _empty_pools(nb)
+    starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    logits, h = prefill(CFG, w, kp, vp, np.concatenate(prompts), starts, [0, 0, 0], bt)
+    assert logits.shape == (3, SHAPE.vocab) and h.shape == (sum(lens), SHAPE.hidden)
+    for s, toks in enumerate(prompts):
+        full, ks, vs = causal_forward(CFG, w, toks)
+        np.testing.assert_allclose(logits[s].astype(np.float64), full[-1].astype(np.float64),
+                                   atol=4e-3, rtol=4e-3)
+        t = np.arange(lens[s])
+        for li in range(CFG.n_layers):
+            np.testing.assert_allclose(kp[li][bt[s][t // BS], :, t % BS, :].astype(np.float64),
+                                       ks[li].astype(np.float64), atol=2e-3, rtol=2e-3)
+            np.testing.assert_allclose(vp[li][bt[s][t // BS], :, :, t % BS].astype(np.float64),
+                                       vs[li].astype(np.float64), atol=2e-3, rtol=2e-3)
+
+
+def test_prefill_in_chunks_equals_one_chunk_and_decode():
+    """The same prompts prefilled whole, in two chunks (the second continuing
+    from a cached prefix), and token by token through the decode step give the
+    same last logits and the same cache."""
+    w = _weights(63)
+    rng = np.random.default_rng(64)
+    toks = rng.integers(0, SHAPE.vocab, size=(2, 29)).astype(np.int32)
+    nb = 2 * 2 + 1
+    bt = rng.permutation(nb)[:4].reshape(2, 2).astype(np.int32)
+    kp1, vp1 = _empty_pools(nb)
+    whole, _ = prefill(CFG, w, kp1, vp1, toks.reshape(-1), [0, 29, 58], [0, 0], bt)
+    kp2, vp2 = _empty_pools(nb)
+    cut = [11, 20]
+    first = np.concatenate([toks[0, :cut[0]], toks[1, :cut[1]]])
+    prefill(CFG, w, kp2, vp2, first, [0, cut[0], cut[0] + cut[1]], [0, 0], bt)
+    rest = np.concatenate([toks[0, cut[0]:], toks[1, cut[1]:]])
+    second, _ = prefill(CFG, w, kp2, vp2, rest, [0, 29 - cut[0], 58 - cut[0] - cut[1]], cut, bt)
+    np.testing.assert_allclose(second.astype(np.float64), whole.astype(np.float64), atol=2e-3, rtol=2e-3)
+    inc, kp3, vp3, bt3 = _run_incremental(w, toks, np.random.default_rng(65))
+    np.testing.assert_allclose(inc[:, -1].astype(np.float64), whole.astype(np.float64), atol=4e-3, rtol=4e-3)
+    t = np.arange(29)
+    for li in range(CFG.n_layers):
+        for b in range(2):
+            a = kp1[li][bt[b][t // BS], :, t % BS, :].astype(np.float64)
+            np.testing.assert_allclose(kp2[li][bt[b][t // BS], :, t % BS, :].astype(np.float64), a,
+                                       atol=2e-3, rtol=2e-3)
+            np.testing.assert_allclose(kp3[li][bt3[b][t // BS], :, t % BS, :].astype(np.float64), a,
+                                       atol=2e-3, rtol=2e-3)
