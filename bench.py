@@ -198,6 +198,36 @@ def time_attention(pkv, torch, w, n_pools, rounds, seed):
             "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "rotated_pools": n_pools}
 
 
+def time_sampling(pkv, torch, inp, batch, vocab, rounds, seed, mode):
+    """Sampling after the LM head: one call over [batch, vocab] f16 logits
+    shaped like a language model's (peaked rows), every row active.
+    mode "mixed": temperatures 0.3-1.5 with top-k {off, 1, 5, 50, 1000} and
+    top-p {1, 0.9, 0.5, 0, 0.99, 0.2} cycling over rows; "top_p": T = 0.7,
+    top-p 0.9 on every row; "temperature": T = 0.7 only."""
+    c = inp.sampling_case(batch, vocab, seed, masked_rows=False)
+    c.lens[:] = 1
+    c.temperature[c.temperature == 0] = 0.7
+    if mode != "mixed":
+        c.temperature[:] = 0.7
+        c.top_k[:] = -1
+        c.top_p[:] = 0.9 if mode == "top_p" else 1.0
+    dev = lambda a: torch.from_numpy(a).cuda()
+    args = [dev(x) for x in (c.logits, c.temperature, c.top_k, c.top_p, c.uniform)]
+    tok = torch.empty(batch, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        pkv.sample(*args, tok)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(rounds):
+        pkv.sample(*args, tok)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / rounds * 1e3
+    return {"batch": batch, "vocab": vocab, "mode": mode, "us_per_call": us,
+            "logit_bytes": batch * vocab * 2}
+
+
 def attention_traffic():
     """HBM bytes per attn15 launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE runs (scaled by a device copy of known size), or None when the
@@ -273,6 +303,7 @@ def main():
     ap.add_argument("--attn-rounds", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-attn", action="store_true")
+    ap.add_argument("--no-sample", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "kernel for scaling rocprof FETCH_SIZE / WRITE_SIZE)")
@@ -335,6 +366,13 @@ def main():
         attn["fp8long"] = time_attention(pkv, torch, inp.FP8LONG, 8, args.attn_rounds, seed=12)
         log(f"fp8long: {attn['fp8long']['us_per_call']:.2f} us/call, {attn['fp8long']['GBs']:.0f} GB/s")
 
+    sampling = {}
+    if not args.no_sample:
+        for mode in ("mixed", "top_p", "temperature"):
+            r = time_sampling(pkv, torch, inp, 256, shape.vocab, 20, 13, mode)
+            sampling[mode] = r
+            log(f"sampling b256 {mode}: {r['us_per_call']:.1f} us/call")
+
     if head is None:  # profiling runs: attention only
         print(json.dumps({"attention": attn}))
         return
@@ -372,6 +410,7 @@ def main():
         "decode_fp8_kv": {str(n): {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                           for n, r in per_batch_fp8.items()},
         "attention": attn,
+        "sampling": sampling,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -231,6 +231,30 @@ pkv_status pkv_decode_step(const pkv_model* model, pkv_cache* cache, const int32
                            void* logits, void* hidden_out, void* workspace,
                            size_t workspace_bytes, pkv_stream_t stream);
 
+/* Batched, chunked prefill (the step before decode; rvLLM post, section
+ * "PagedAttention과 FlashAttention-3": causal multi-token attention over the
+ * paged cache).  Sequence s brings the new tokens
+ * token_ids[seq_starts[s] .. seq_starts[s+1]) at positions prior_lens[s],
+ * prior_lens[s] + 1, ... (prior_lens[s] tokens already cached, 0 for a whole
+ * prompt).  In every layer the k and v of all new tokens are appended, then
+ * new token j of sequence s attends over positions [0, prior_lens[s] + j] of
+ * its sequence: the layer of pkv_decode_layer with each new token as a row of
+ * its own.  Device arrays: token_ids int32 [n_tokens]; seq_starts int32
+ * [n_seqs + 1], ascending from 0 to n_tokens, every sequence with at least
+ * one new token; prior_lens int32 [n_seqs]; block_tables int32
+ * [n_seqs][bt_stride] covering each sequence's first prior + new tokens;
+ * logits f16 [n_seqs][V] gets the logits of each sequence's last new token.
+ * max_context bounds prior_lens[s] + (new tokens of s); a token beyond it is
+ * not appended and attends to nothing (its row is inactive).  f16 or fp8
+ * caches as pkv_decode_layer.  workspace: pkv_prefill_workspace_bytes, 256-byte
+ * aligned, contents irrelevant (the arrival counters are zeroed on entry). */
+pkv_status pkv_prefill_workspace_bytes(const pkv_model* model, const pkv_cache* cache, int n_tokens, int n_seqs,
+                                       int max_context, size_t* bytes);
+pkv_status pkv_prefill(const pkv_model* model, pkv_cache* cache, const int32_t* token_ids,
+                       const int32_t* seq_starts, const int32_t* prior_lens, int n_seqs, int n_tokens,
+                       const int32_t* block_tables, int bt_stride, int max_context, void* logits,
+                       void* workspace, size_t workspace_bytes, pkv_stream_t stream);
+
 /* Greedy token per row: the lowest index of the largest f16 logit
  * (zingnex.cn article, section 支持的参数: temperature 0 decodes greedily);
  * NaN logits never win.  logits f16 [batch][vocab]; tokens int32 [batch].

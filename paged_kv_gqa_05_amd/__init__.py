@@ -182,6 +182,30 @@ def decode_step(model, cache, token_ids, block_tables, context_lens, max_context
                                 _stream(stream)))
 
 
+def prefill_workspace_bytes(model, cache, n_tokens, n_seqs, max_context):
+    n = C.c_size_t()
+    _check(_lib.pkv_prefill_workspace_bytes(model.handle, cache.handle, n_tokens, n_seqs, max_context,
+                                            C.byref(n)))
+    return n.value
+
+
+def prefill(model, cache, token_ids, seq_starts, prior_lens, block_tables, max_context, logits, workspace,
+            stream=None):
+    """Prefill the new tokens of every sequence (concatenated in token_ids,
+    sequence s = token_ids[seq_starts[s]:seq_starts[s+1]], continuing after
+    prior_lens[s] cached tokens); logits [S, V] of each last new token."""
+    for t, n in ((token_ids, "token_ids"), (seq_starts, "seq_starts"), (prior_lens, "prior_lens"),
+                 (block_tables, "block_tables")):
+        _need(t, torch.int32, n)
+    _need(logits, torch.float16, "logits")
+    n_seqs = prior_lens.shape[0]
+    if seq_starts.shape[0] != n_seqs + 1 or logits.shape[0] != n_seqs or block_tables.shape[0] != n_seqs:
+        raise ValueError("seq_starts must hold n_seqs + 1 offsets; logits and block_tables n_seqs rows")
+    _check(_lib.pkv_prefill(model.handle, cache.handle, _p(token_ids), _p(seq_starts), _p(prior_lens), n_seqs,
+                            token_ids.shape[0], _p(block_tables), block_tables.shape[1], max_context, _p(logits),
+                            _p(workspace), workspace.numel(), _stream(stream)))
+
+
 def argmax(logits, tokens, context_lens=None, stream=None):
     """Greedy tokens; rows whose context length is 0 (when given) get -1."""
     _need(logits, torch.float16, "logits")

@@ -95,6 +95,42 @@ StepBuffers carve(const pkv_model* m, int batch, const AttnPlan& plan, void* bas
 
 int cache_elt(const pkv_cache_desc& cd) { return cd.dtype == PKV_KV_FP8_E4M3 ? 1 : 2; }
 
+// A prefill runs the decode layers over its n_tokens new tokens as rows of
+// their own; after the step buffers for that many rows come the per-token
+// rows (context length, block-table copy), the last row of every sequence,
+// their hidden states and the LM head's split-K scratch for n_seqs rows.
+struct PrefillBuffers {
+  StepBuffers sb;
+  int stride_tok;
+  int32_t* lens_tok;
+  int32_t* bt_tok;
+  int32_t* last_idx;
+  _Float16* h_last;
+  void* lm_ws;
+  size_t total;
+};
+
+PrefillBuffers carve_prefill(const pkv_model* m, int n_tokens, int n_seqs, int max_context, const AttnPlan& plan,
+                             void* base) {
+  PrefillBuffers pb{};
+  pb.sb = carve(m, n_tokens, plan, base);
+  char* p = static_cast<char*>(base);
+  size_t off = pb.sb.total;
+  auto take = [&](size_t bytes) {
+    char* r = p ? p + off : nullptr;
+    off += align_up(bytes, 256);
+    return r;
+  };
+  pb.stride_tok = ceil_div(max_context, kBlock);
+  pb.lens_tok = reinterpret_cast<int32_t*>(take((size_t)n_tokens * 4));
+  pb.bt_tok = reinterpret_cast<int32_t*>(take((size_t)n_tokens * pb.stride_tok * 4));
+  pb.last_idx = reinterpret_cast<int32_t*>(take((size_t)n_seqs * 4));
+  pb.h_last = reinterpret_cast<_Float16*>(take((size_t)n_seqs * m->d.hidden * 2));
+  pb.lm_ws = take(linear_ws_bytes(n_seqs, m->d.vocab, m->d.hidden, EPI_F16));
+  pb.total = off;
+  return pb;
+}
+
 pkv_status check_step(const pkv_model* m, const pkv_cache* cache, const int32_t* bt, int bt_stride,
                       const int32_t* lens, int batch, int max_context, void* ws, size_t ws_bytes,
                       StepBuffers* bufs, AttnPlan* plan) {
@@ -304,6 +340,58 @@ pkv_status pkv_decode_step(const pkv_model* m, pkv_cache* cache, const int32_t* 
                            void* hidden_out, void* ws, size_t ws_bytes, pkv_stream_t stream) {
   return enqueue_step(m, cache, tokens, bt, bt_stride, lens, batch, max_context, logits, hidden_out, ws,
                       ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+pkv_status pkv_prefill_workspace_bytes(const pkv_model* m, const pkv_cache* cache, int n_tokens, int n_seqs,
+                                       int max_context, size_t* bytes) {
+  if (!m || !cache || !bytes) return fail(PKV_E_ARG, "NULL argument");
+  if (n_tokens < 1 || n_seqs < 1 || max_context < 1)
+    return fail(PKV_E_ARG, "n_tokens, n_seqs and max_context must be >= 1");
+  const AttnPlan plan =
+      attn_plan(n_tokens, m->d.num_q_heads, m->d.num_kv_heads, m->d.head_dim, cache_elt(cache->desc), max_context);
+  *bytes = carve_prefill(m, n_tokens, n_seqs, max_context, plan, nullptr).total;
+  return PKV_OK;
+}
+
+pkv_status pkv_prefill(const pkv_model* m, pkv_cache* cache, const int32_t* tokens, const int32_t* seq_starts,
+                       const int32_t* prior_lens, int n_seqs, int n_tokens, const int32_t* bt, int bt_stride,
+                       int max_context, void* logits, void* ws, size_t ws_bytes, pkv_stream_t stream) {
+  if (!m || !cache) return fail(PKV_E_ARG, "model / cache is NULL");
+  const pkv_cache_desc& cd = cache->desc;
+  if (cd.num_kv_heads != m->d.num_kv_heads || cd.head_dim != m->d.head_dim)
+    return fail(PKV_E_ARG, "cache heads / head_dim differ from the model's");
+  if (cd.num_layers < m->d.num_layers) return fail(PKV_E_ARG, "cache has fewer layers than the model");
+  if (!tokens || !seq_starts || !prior_lens || !bt || !logits)
+    return fail(PKV_E_ARG, "token_ids / seq_starts / prior_lens / block_tables / logits is NULL");
+  if (n_tokens < 1 || n_seqs < 1) return fail(PKV_E_ARG, "n_tokens and n_seqs must be >= 1");
+  if (max_context < 1 || max_context > m->d.max_positions)
+    return fail(PKV_E_ARG, "max_context must be in [1, max_positions]");
+  if (max_context > kAttnMaxContext) return fail(PKV_E_UNSUPPORTED, "max_context above 262144");
+  if (bt_stride < ceil_div(max_context, kBlock)) return fail(PKV_E_ARG, "bt_stride < ceil(max_context / 16)");
+  const AttnPlan plan =
+      attn_plan(n_tokens, m->d.num_q_heads, m->d.num_kv_heads, m->d.head_dim, cache_elt(cd), max_context);
+  const size_t need = carve_prefill(m, n_tokens, n_seqs, max_context, plan, nullptr).total;
+  if (!ws || ws_bytes < need) return fail(PKV_E_ARG, "workspace too small: need " + std::to_string(need) + " bytes");
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(PKV_E_ARG, "workspace must be 256-byte aligned");
+  const PrefillBuffers pb = carve_prefill(m, n_tokens, n_seqs, max_context, plan, ws);
+  const StepBuffers& sb = pb.sb;
+  const pkv_model_desc& d = m->d;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  PKV_HIP(launch_prefill_rows(seq_starts, prior_lens, bt, bt_stride, n_seqs, n_tokens, pb.stride_tok, max_context,
+                              pb.lens_tok, pb.bt_tok, pb.last_idx, s));
+  PKV_HIP(launch_embed(m->embed, tokens, sb.h, n_tokens, d.hidden, sb.counters, sb.n_counters, s));
+  for (int l = 0; l < d.num_layers; ++l)
+    PKV_HIP(run_layer(m, cache, l, sb.h, pb.bt_tok, pb.stride_tok, pb.lens_tok, n_tokens, sb, plan, s));
+  // the last new token of every sequence -> final RMSNorm -> LM head
+  PKV_HIP(launch_embed(sb.h, pb.last_idx, pb.h_last, n_seqs, d.hidden, sb.counters, sb.n_counters, s));
+  LinArgs a{};
+  a.eps = d.rms_eps;
+  a.A = pb.h_last; a.lda = d.hidden; a.K = d.hidden; a.M = n_seqs;
+  a.W = static_cast<const _Float16*>(m->w_lm);
+  a.gain = static_cast<const _Float16*>(m->w_final); a.norm = 1;
+  a.out = logits; a.ldo = d.vocab; a.n_out = d.vocab;
+  PKV_HIP(launch_linear(a, EPI_F16, pb.lm_ws, sb.counters, s));
+  return PKV_OK;
 }
 
 pkv_status pkv_argmax(const void* logits, int batch, int vocab, int32_t* tokens, const int32_t* context_lens,

@@ -1,4 +1,5 @@
-// Small per-step kernels: embedding gather and greedy argmax.
+// Small per-step kernels: embedding gather, greedy argmax and the per-token
+// rows of a prefill.
 #include "ops.h"
 
 namespace pkv {
@@ -81,7 +82,41 @@ __global__ void __launch_bounds__(1024) argmax_kernel(const h16* __restrict__ lo
   }
 }
 
+// Per-token rows of a prefill: new token j of sequence s (tokens
+// [seq_starts[s], seq_starts[s+1])) gets context length prior_lens[s] + j + 1
+// (0, an inactive row, if that is outside [1, max_context]) and a copy of the
+// first stride_tok entries of its sequence's block-table row; last_idx[s] is
+// the row of the sequence's last new token.  Offsets are clamped to [0, T], so
+// malformed offsets cannot reach outside the buffers.
+__global__ void prefill_rows_kernel(const int32_t* __restrict__ seq_starts, const int32_t* __restrict__ prior_lens,
+                                    const int32_t* __restrict__ bt, int bt_stride, int n_tokens, int stride_tok,
+                                    int max_context, int32_t* __restrict__ lens_tok, int32_t* __restrict__ bt_tok,
+                                    int32_t* __restrict__ last_idx) {
+  const int s = blockIdx.x;
+  const int t0 = min(max(seq_starts[s], 0), n_tokens);
+  const int t1 = min(max(seq_starts[s + 1], t0), n_tokens);
+  const int n = t1 - t0, prior = prior_lens[s];
+  for (int j = threadIdx.x; j < n; j += blockDim.x) {
+    const long long pos1 = (long long)prior + j + 1;
+    lens_tok[t0 + j] = (pos1 >= 1 && pos1 <= max_context) ? (int)pos1 : 0;
+  }
+  const int32_t* src = bt + (size_t)s * bt_stride;
+  for (int i = threadIdx.x; i < n * stride_tok; i += blockDim.x) {
+    const int j = i / stride_tok, c = i - j * stride_tok;
+    bt_tok[(size_t)(t0 + j) * stride_tok + c] = src[c];
+  }
+  if (threadIdx.x == 0) last_idx[s] = n > 0 ? t1 - 1 : min(t0, n_tokens - 1);
+}
+
 }  // namespace
+
+hipError_t launch_prefill_rows(const int32_t* seq_starts, const int32_t* prior_lens, const int32_t* bt,
+                               int bt_stride, int n_seqs, int n_tokens, int stride_tok, int max_context,
+                               int32_t* lens_tok, int32_t* bt_tok, int32_t* last_idx, hipStream_t s) {
+  hipLaunchKernelGGL(prefill_rows_kernel, dim3(n_seqs), dim3(256), 0, s, seq_starts, prior_lens, bt, bt_stride,
+                     n_tokens, stride_tok, max_context, lens_tok, bt_tok, last_idx);
+  return hipGetLastError();
+}
 
 hipError_t launch_embed(const void* table, const int32_t* tokens, void* h, int batch, int hidden,
                         int* zero_p, int zero_n, hipStream_t s) {
