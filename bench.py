@@ -31,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
-MFMA_F16_PEAK_TFLOPS = 2500.0
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16 MFMA, TFLOP/s
 PAGES_TOKS_N256 = 40714.0  # rvLLM post, H100 1.5B table, N = 256 (other hardware)
 
 
@@ -97,9 +97,41 @@ class DecodeRun:
         self.graph.replay()
         self.pkv.argmax(self.logits, self.tok_d)
 
-    def prefill(self):
-        for t in range(self.prompt_len):
-            self.step(self.prompts[:, t])
+    def prefill(self, repeats=3):
+        """All prompts in one batched prefill call (every prompt token of every
+        row), then argmax of each row's last logits gives its first token.
+        The call is repeated `repeats` more times (it rewrites the same cache
+        slots with the same values) to time it."""
+        torch, pkv = self.torch, self.pkv
+        b, p = self.batch, self.prompt_len
+        for r in range(b):
+            self.alloc.grow(self.bt[r], 0, p)
+        self.lens[:] = p
+        self.bt_d.copy_(torch.from_numpy(self.bt))
+        tokens = torch.from_numpy(self.prompts.reshape(-1).copy()).cuda()
+        starts = torch.arange(0, (b + 1) * p, p, dtype=torch.int32, device="cuda")
+        prior = torch.zeros(b, dtype=torch.int32, device="cuda")
+        ws = torch.empty(pkv.prefill_workspace_bytes(self.model, self.cache, b * p, b, self.max_context),
+                         dtype=torch.uint8, device="cuda")
+
+        def call():
+            pkv.prefill(self.model, self.cache, tokens, starts, prior, self.bt_d, self.max_context, self.logits, ws)
+
+        call()
+        ms = None
+        if repeats:
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(repeats):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / repeats
+        pkv.argmax(self.logits, self.tok_d)
+        torch.cuda.synchronize()
+        del ws
+        return ms
 
     def close(self):
         self.graph.close()
@@ -108,7 +140,7 @@ class DecodeRun:
 
 def time_decode(pkv, torch, model, shape, batch, prompt_len, warmup, steps, seed, kv_dtype="f16"):
     run = DecodeRun(pkv, torch, model, shape, batch, prompt_len, prompt_len + warmup + steps, seed, kv_dtype)
-    run.prefill()
+    prefill_ms = run.prefill()
     for _ in range(warmup):
         run.step()
     torch.cuda.synchronize()
@@ -123,8 +155,23 @@ def time_decode(pkv, torch, model, shape, batch, prompt_len, warmup, steps, seed
     ms = e0.elapsed_time(e1)
     ctx_mean = float(run.lens.mean()) - steps / 2.0
     run.close()
+    flops = prefill_flops(shape, batch, prompt_len)
     return {"batch": batch, "ms_per_step": ms / steps, "tok_s": batch * steps / (ms / 1e3),
-            "wall_s": wall, "mean_context": ctx_mean}
+            "wall_s": wall, "mean_context": ctx_mean,
+            "prefill_ms": prefill_ms, "prefill_tok_s": batch * prompt_len / (prefill_ms / 1e3),
+            "prefill_tflops": flops / (prefill_ms / 1e3) / 1e12,
+            "prefill_frac_of_mfma_peak": flops / (prefill_ms / 1e3) / 1e12 / MFMA_F16_PEAK_TFLOPS}
+
+
+def prefill_flops(shape, batch, prompt_len):
+    """Algorithmic FLOPs of one prefill of `batch` prompts of `prompt_len`
+    tokens: the projections of every token, causal attention (QK^T and PV over
+    positions 0..t for token t) and the LM head of each prompt's last token."""
+    h, d, f = shape.hidden, shape.head_dim, shape.ffn
+    qkv = (shape.n_q_heads + 2 * shape.n_kv_heads) * d
+    per_tok = shape.n_layers * 2 * (qkv * h + h * shape.n_q_heads * d + 2 * f * h + h * f)
+    attn = shape.n_layers * 4 * shape.n_q_heads * d * (prompt_len * (prompt_len + 1) // 2)
+    return batch * (prompt_len * per_tok + attn) + batch * 2 * h * shape.vocab
 
 
 def step_bytes(shape, batch, mean_ctx, kv_elt=2):
@@ -346,7 +393,8 @@ def main():
         r["frac_of_roofline"] = r["roofline_ms"] / r["ms_per_step"]
         per_batch[n] = r
         log(f"batch {n}: {r['ms_per_step']:.3f} ms/step, {r['tok_s']:.0f} tok/s, "
-            f"{100 * r['frac_of_roofline']:.1f}% of the HBM roofline")
+            f"{100 * r['frac_of_roofline']:.1f}% of the HBM roofline; prefill {r['prefill_ms']:.2f} ms, "
+            f"{r['prefill_tok_s']:.0f} prompt tok/s, {r['prefill_tflops']:.0f} TFLOP/s")
 
     per_batch_fp8 = {}
     for n in ([int(x) for x in args.fp8_batches.split(",") if x.strip()] if batches else []):
