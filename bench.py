@@ -97,6 +97,11 @@ class DecodeRun:
         self.graph.replay()
         self.pkv.argmax(self.logits, self.tok_d)
 
+    def teacher_forced(self):
+        """Prompt tokens through the decode graph, one position per step."""
+        for t in range(self.prompt_len):
+            self.step(self.prompts[:, t])
+
     def prefill(self, repeats=3):
         """All prompts in one batched prefill call (every prompt token of every
         row), then argmax of each row's last logits gives its first token.
@@ -138,9 +143,14 @@ class DecodeRun:
         self.cache.close()
 
 
-def time_decode(pkv, torch, model, shape, batch, prompt_len, warmup, steps, seed, kv_dtype="f16"):
+def time_decode(pkv, torch, model, shape, batch, prompt_len, warmup, steps, seed, kv_dtype="f16",
+                prompt_fill="prefill", prefill_repeats=3):
     run = DecodeRun(pkv, torch, model, shape, batch, prompt_len, prompt_len + warmup + steps, seed, kv_dtype)
-    prefill_ms = run.prefill()
+    if prompt_fill == "prefill":
+        prefill_ms = run.prefill(prefill_repeats)
+    else:
+        run.teacher_forced()
+        prefill_ms = None
     for _ in range(warmup):
         run.step()
     torch.cuda.synchronize()
@@ -155,12 +165,13 @@ def time_decode(pkv, torch, model, shape, batch, prompt_len, warmup, steps, seed
     ms = e0.elapsed_time(e1)
     ctx_mean = float(run.lens.mean()) - steps / 2.0
     run.close()
-    flops = prefill_flops(shape, batch, prompt_len)
-    return {"batch": batch, "ms_per_step": ms / steps, "tok_s": batch * steps / (ms / 1e3),
-            "wall_s": wall, "mean_context": ctx_mean,
-            "prefill_ms": prefill_ms, "prefill_tok_s": batch * prompt_len / (prefill_ms / 1e3),
-            "prefill_tflops": flops / (prefill_ms / 1e3) / 1e12,
-            "prefill_frac_of_mfma_peak": flops / (prefill_ms / 1e3) / 1e12 / MFMA_F16_PEAK_TFLOPS}
+    r = {"batch": batch, "ms_per_step": ms / steps, "tok_s": batch * steps / (ms / 1e3),
+         "wall_s": wall, "mean_context": ctx_mean}
+    if prefill_ms:
+        tflops = prefill_flops(shape, batch, prompt_len) / (prefill_ms / 1e3) / 1e12
+        r.update({"prefill_ms": prefill_ms, "prefill_tok_s": batch * prompt_len / (prefill_ms / 1e3),
+                  "prefill_tflops": tflops, "prefill_frac_of_mfma_peak": tflops / MFMA_F16_PEAK_TFLOPS})
+    return r
 
 
 def prefill_flops(shape, batch, prompt_len):
@@ -351,6 +362,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-attn", action="store_true")
     ap.add_argument("--no-sample", action="store_true")
+    ap.add_argument("--prompt-fill", choices=("prefill", "decode"), default="prefill",
+                    help="prompts enter by one batched prefill call (timed) or one decode step per position")
+    ap.add_argument("--prefill-repeats", type=int, default=3, help="timed repeats of the prefill call")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "kernel for scaling rocprof FETCH_SIZE / WRITE_SIZE)")
@@ -386,20 +400,23 @@ def main():
 
     per_batch = {}
     for n in batches:
-        r = time_decode(pkv, torch, model, shape, n, args.prompt, args.warmup, args.steps, seed=2003 + n)
+        r = time_decode(pkv, torch, model, shape, n, args.prompt, args.warmup, args.steps, seed=2003 + n,
+                        prompt_fill=args.prompt_fill, prefill_repeats=args.prefill_repeats)
         nbytes = step_bytes(shape, n, r["mean_context"])
         r["bytes_per_step"] = nbytes
         r["roofline_ms"] = nbytes / (HBM_PEAK_GBS * 1e9) * 1e3
         r["frac_of_roofline"] = r["roofline_ms"] / r["ms_per_step"]
         per_batch[n] = r
         log(f"batch {n}: {r['ms_per_step']:.3f} ms/step, {r['tok_s']:.0f} tok/s, "
-            f"{100 * r['frac_of_roofline']:.1f}% of the HBM roofline; prefill {r['prefill_ms']:.2f} ms, "
-            f"{r['prefill_tok_s']:.0f} prompt tok/s, {r['prefill_tflops']:.0f} TFLOP/s")
+            f"{100 * r['frac_of_roofline']:.1f}% of the HBM roofline")
+        if "prefill_ms" in r:
+            log(f"  prefill of {n} x {args.prompt} tokens: {r['prefill_ms']:.2f} ms, "
+                f"{r['prefill_tok_s']:.0f} prompt tok/s, {r['prefill_tflops']:.0f} TFLOP/s")
 
     per_batch_fp8 = {}
     for n in ([int(x) for x in args.fp8_batches.split(",") if x.strip()] if batches else []):
         r = time_decode(pkv, torch, model, shape, n, args.prompt, args.warmup, args.steps, seed=2003 + n,
-                        kv_dtype="fp8")
+                        kv_dtype="fp8", prompt_fill=args.prompt_fill, prefill_repeats=args.prefill_repeats)
         nbytes = step_bytes(shape, n, r["mean_context"], kv_elt=1)
         r["bytes_per_step"] = nbytes
         r["roofline_ms"] = nbytes / (HBM_PEAK_GBS * 1e9) * 1e3
