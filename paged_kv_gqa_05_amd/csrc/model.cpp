@@ -105,6 +105,9 @@ struct PrefillBuffers {
   int32_t* lens_tok;
   int32_t* bt_tok;
   int32_t* last_idx;
+  int32_t* items;    // prefill attention work list: max_items int32 pairs
+  int32_t* n_items;
+  int max_items;
   _Float16* h_last;
   void* lm_ws;
   size_t total;
@@ -125,6 +128,9 @@ PrefillBuffers carve_prefill(const pkv_model* m, int n_tokens, int n_seqs, int m
   pb.lens_tok = reinterpret_cast<int32_t*>(take((size_t)n_tokens * 4));
   pb.bt_tok = reinterpret_cast<int32_t*>(take((size_t)n_tokens * pb.stride_tok * 4));
   pb.last_idx = reinterpret_cast<int32_t*>(take((size_t)n_seqs * 4));
+  pb.max_items = prefill_max_items(n_tokens, n_seqs, m->d.num_q_heads / m->d.num_kv_heads);
+  pb.items = reinterpret_cast<int32_t*>(take((size_t)pb.max_items * 8));
+  pb.n_items = reinterpret_cast<int32_t*>(take(4));
   pb.h_last = reinterpret_cast<_Float16*>(take((size_t)n_seqs * m->d.hidden * 2));
   pb.lm_ws = take(linear_ws_bytes(n_seqs, m->d.vocab, m->d.hidden, EPI_F16));
   pb.total = off;
@@ -153,9 +159,11 @@ pkv_status check_step(const pkv_model* m, const pkv_cache* cache, const int32_t*
   return PKV_OK;
 }
 
+// pre (prefill only): attention runs as the causal multi-token kernel over the
+// new tokens' sequences instead of one decode row per token.
 hipError_t run_layer(const pkv_model* m, pkv_cache* cache, int layer, _Float16* h, const int32_t* bt,
                      int bt_stride, const int32_t* lens, int batch, const StepBuffers& sb,
-                     const AttnPlan& plan, hipStream_t s) {
+                     const AttnPlan& plan, hipStream_t s, const PrefillAttnArgs* pre = nullptr) {
   const pkv_model_desc& d = m->d;
   const pkv_layer_weights& w = m->layers[layer];
   const int qkv_n = (d.num_q_heads + 2 * d.num_kv_heads) * d.head_dim;
@@ -182,12 +190,20 @@ hipError_t run_layer(const pkv_model* m, pkv_cache* cache, int layer, _Float16* 
   a.rope.fp8 = fp8; a.rope.k_scale = ks; a.rope.v_scale = vs;
   if ((e = launch_linear(a, EPI_ROPE, sb.gemm_ws, sb.counters, s)) != hipSuccess) return e;
   // 2. paged attention
+  if (pre) {
+    PrefillAttnArgs pa = *pre;
+    pa.k_pool = kp; pa.v_pool = vp; pa.q = sb.q; pa.out = sb.o;
+    pa.hq = d.num_q_heads; pa.hkv = d.num_kv_heads; pa.head_dim = d.head_dim; pa.fp8 = fp8;
+    pa.scale = 1.0f / std::sqrt((float)d.head_dim); pa.k_scale = ks; pa.v_scale = vs;
+    if ((e = launch_prefill_attention(pa, s)) != hipSuccess) return e;
+  } else {
   AttnArgs at{};
   at.k_pool = kp; at.v_pool = vp; at.q = sb.q; at.out = sb.o; at.lse = nullptr;
   at.bt = bt; at.bt_stride = bt_stride; at.lens = lens; at.batch = batch;
   at.hq = d.num_q_heads; at.hkv = d.num_kv_heads; at.head_dim = d.head_dim; at.fp8 = fp8;
   at.scale = 1.0f / std::sqrt((float)d.head_dim); at.k_scale = ks; at.v_scale = vs; at.ws = sb.attn_ws;
   if ((e = launch_paged_attention(at, plan, s)) != hipSuccess) return e;
+  }
   // 3. O projection + residual add
   a = LinArgs{};
   a.eps = d.rms_eps;
@@ -380,8 +396,12 @@ pkv_status pkv_prefill(const pkv_model* m, pkv_cache* cache, const int32_t* toke
   PKV_HIP(launch_prefill_rows(seq_starts, prior_lens, bt, bt_stride, n_seqs, n_tokens, pb.stride_tok, max_context,
                               pb.lens_tok, pb.bt_tok, pb.last_idx, s));
   PKV_HIP(launch_embed(m->embed, tokens, sb.h, n_tokens, d.hidden, sb.counters, sb.n_counters, s));
+  PrefillAttnArgs pre{};
+  pre.seq_starts = seq_starts; pre.prior_lens = prior_lens; pre.bt = bt; pre.bt_stride = bt_stride;
+  pre.items = pb.items; pre.n_items = pb.n_items; pre.max_items = pb.max_items;
+  pre.n_seqs = n_seqs; pre.n_tokens = n_tokens; pre.max_context = max_context;
   for (int l = 0; l < d.num_layers; ++l)
-    PKV_HIP(run_layer(m, cache, l, sb.h, pb.bt_tok, pb.stride_tok, pb.lens_tok, n_tokens, sb, plan, s));
+    PKV_HIP(run_layer(m, cache, l, sb.h, pb.bt_tok, pb.stride_tok, pb.lens_tok, n_tokens, sb, plan, s, &pre));
   // the last new token of every sequence -> final RMSNorm -> LM head
   PKV_HIP(launch_embed(sb.h, pb.last_idx, pb.h_last, n_seqs, d.hidden, sb.counters, sb.n_counters, s));
   LinArgs a{};

@@ -12,6 +12,28 @@ hipError_t launch_sample(const void* logits, int batch, int vocab, const float* 
 hipError_t launch_prefill_rows(const int32_t* seq_starts, const int32_t* prior_lens, const int32_t* bt,
                                int bt_stride, int n_seqs, int n_tokens, int stride_tok, int max_context,
                                int32_t* lens_tok, int32_t* bt_tok, int32_t* last_idx, hipStream_t s);
+// Causal attention of a prefill's new tokens over the paged cache (their k and
+// v already appended): q and out are [n_tokens][hq][head_dim] f16; items
+// (int32 pairs, max_items of them) and n_items are scratch for the work list.
+struct PrefillAttnArgs {
+  const void* k_pool;
+  const void* v_pool;
+  const void* q;
+  void* out;
+  const int32_t* seq_starts;
+  const int32_t* prior_lens;
+  const int32_t* bt;
+  int bt_stride;
+  int32_t* items;
+  int32_t* n_items;
+  int max_items;
+  int n_seqs, n_tokens, hq, hkv, head_dim, max_context;
+  bool fp8;
+  float scale, k_scale, v_scale;
+};
+int prefill_max_items(int n_tokens, int n_seqs, int group);
+hipError_t launch_prefill_attention(const PrefillAttnArgs& a, hipStream_t s);
+
 hipError_t launch_argmax(const void* logits, int batch, int vocab, int32_t* tokens, const int32_t* lens,
                          hipStream_t s);
 

@@ -10,7 +10,8 @@ import torch
 
 import oracle
 import pkv_inputs as inp
-from gpu_util import dev, assert_parity, weights_to_device, oracle_config, k_to_lib, k_from_lib
+from gpu_util import (ATOL, RTOL, dev, assert_parity, weights_to_device, oracle_config, k_to_lib, k_from_lib,
+                      v_to_lib, v_from_lib)
 from test_gpu_model import MID
 
 pytestmark = pytest.mark.gpu
@@ -47,11 +48,15 @@ def prefill_case(shape, new_lens, prior_lens, seed, spare_blocks=3):
 
 def run_prefill_gpu(pkv, shape, case, max_context=None, model=None, weights=None):
     model = model or pkv.Model(shape, weights or weights_to_device(case["weights"]), max_positions=4096)
-    cache = pkv.KVCache(shape.n_layers, case["nb"], shape.n_kv_heads, shape.head_dim)
+    if "k_scales" in case:
+        cache = pkv.KVCache(shape.n_layers, case["nb"], shape.n_kv_heads, shape.head_dim, dtype=pkv.KV_FP8_E4M3,
+                            k_scales=case["k_scales"], v_scales=case["v_scales"])
+    else:
+        cache = pkv.KVCache(shape.n_layers, case["nb"], shape.n_kv_heads, shape.head_dim)
     for li in range(shape.n_layers):
         k, v = cache.layer(li)
         k.copy_(torch.from_numpy(k_to_lib(case["k"][li])))
-        v.copy_(torch.from_numpy(case["v"][li]))
+        v.copy_(torch.from_numpy(v_to_lib(case["v"][li])))
     mc = max_context or case["max_context"]
     bt = case["bt"]
     if bt.shape[1] * BS < mc:
@@ -63,7 +68,7 @@ def run_prefill_gpu(pkv, shape, case, max_context=None, model=None, weights=None
     pkv.prefill(model, cache, dev(case["tokens"]), dev(case["starts"]), dev(case["prior"]), dev(bt), mc, logits, ws)
     torch.cuda.synchronize()
     ks = [k_from_lib(cache.layer(li)[0].cpu().numpy()) for li in range(shape.n_layers)]
-    vs = [cache.layer(li)[1].cpu().numpy() for li in range(shape.n_layers)]
+    vs = [v_from_lib(cache.layer(li)[1].cpu().numpy()) for li in range(shape.n_layers)]
     return logits.cpu().numpy(), ks, vs
 
 
@@ -71,7 +76,8 @@ def run_prefill_oracle(shape, case):
     kp = [k.copy() for k in case["k"]]
     vp = [v.copy() for v in case["v"]]
     logits, _ = oracle.prefill(oracle_config(shape), case["weights"], kp, vp, case["tokens"], case["starts"],
-                               case["prior"], case["bt"])
+                               case["prior"], case["bt"], k_scales=case.get("k_scales"),
+                               v_scales=case.get("v_scales"))
     return logits, kp, vp
 
 
@@ -157,3 +163,27 @@ def test_prefill_full_shape_sampled_sequences(lib):
     r_logits, rk, rv = run_prefill_oracle(shape, sub)
     assert_parity(g_logits[seqs], r_logits, "full-shape last-token logits")
     check_cache(sub, shape, gk, gv, rk, rv, seqs=range(4))
+
+
+def test_prefill_fp8_cache(lib):
+    """One layer over an E4M3 cache (cached prefixes quantised with scale
+    amax/448, NaN slots as the NaN code): logits within 3x the parity bar,
+    appended codes within the bar plus one code step, every other byte
+    identical (the quantiser itself is pinned bit-exact by the append tests)."""
+    shape = inp.Shape(MID.hidden, MID.n_q_heads, MID.n_kv_heads, MID.head_dim, MID.ffn, MID.vocab, 1)
+    case = prefill_case(shape, [20, 33, 1], [30, 0, 100], 5009)
+    kq, ks = inp.quantize_e4m3(case["k"][0].astype(np.float32))
+    vq, vs = inp.quantize_e4m3(case["v"][0].astype(np.float32))
+    case = dict(case, k=[kq], v=[vq], k_scales=[ks], v_scales=[vs])
+    g_logits, gk, gv = run_prefill_gpu(lib, shape, case)
+    r_logits, rk, rv = run_prefill_oracle(shape, case)
+    assert_parity(g_logits, r_logits, "fp8-cache last-token logits", atol=3 * ATOL, rtol=3 * RTOL)
+    written = np.zeros(kq.shape, bool)
+    for s_ in range(3):
+        t = np.arange(case["prior"][s_], case["prior"][s_] + case["starts"][s_ + 1] - case["starts"][s_])
+        written[case["bt"][s_][t // BS], :, t % BS, :] = True
+    for got, ref, orig, sc, m in ((gk[0], rk[0], kq, ks, written), (gv[0], rv[0], vq, vs, np.moveaxis(written, 2, 3))):
+        assert np.array_equal(got[~m], orig[~m])
+        dg = oracle.e4m3_decode(got[m]) * sc
+        dr = oracle.e4m3_decode(ref[m]) * sc
+        assert np.all(np.abs(dg - dr) <= ATOL + RTOL * np.abs(dr) + np.abs(dr) / 8 + sc * 2.0 ** -9)
