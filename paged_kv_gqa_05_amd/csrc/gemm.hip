@@ -433,6 +433,7 @@ hipError_t launch_epi(const GemmPlan& pl, const GemmParams& gp, hipStream_t s) {
     case GEMM_32x64: return launch_cfg<32, 64, 4, EPI>(gp, s);
     case GEMM_64x128: return launch_cfg<64, 128, 3, EPI>(gp, s);
     case GEMM_128x128: return launch_cfg<128, 128, 2, EPI, 4, 2>(gp, s);
+    case GEMM_128x256: return launch_cfg<128, 256, 3, EPI, 2, 4>(gp, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -449,7 +450,10 @@ hipError_t launch_epi(const GemmPlan& pl, const GemmParams& gp, hipStream_t s) {
 // fewer partial tiles to merge (down projection, batch 256: 23 us vs 32 us).
 // When 64 x 128 would already need 512 tiles or more, 128 x 128 (gate/up at
 // batch 256: 37 us vs 41 us; LM head).  No tile is taller than the batch
-// rounded up to 32.
+// rounded up to 32.  Prefill-sized long reductions (K >= 4096 with at least
+// 256 tiles of 128 x 256) take 128 x 256 tiles with 3 stages on 2 x 4 waves:
+// the deeper pipeline pays over the long K (down projection, 32768 rows:
+// 934 us vs 1645 us with 128 x 128 and 2 stages).
 GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
   const bool pair = epi_pair(epi);
   static const int kCfg[3][3] = {{GEMM_32x64, 32, 64}, {GEMM_64x128, 64, 128}, {GEMM_128x128, 128, 128}};
@@ -462,6 +466,11 @@ GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
   pl.cfg = kCfg[c][0];
   pl.mt = kCfg[c][1];
   pl.nt = kCfg[c][2];
+  if (K >= 4096 && ceil_div(M, 128) * ceil_div(n_out, pair ? 128 : 256) >= 256) {
+    pl.cfg = GEMM_128x256;
+    pl.mt = 128;
+    pl.nt = 256;
+  }
   pl.n_mt = ceil_div(M, pl.mt);
   pl.n_nt = ceil_div(n_out, pair ? pl.nt / 2 : pl.nt);
   const int n_kc = ceil_div(K, 64);

@@ -129,7 +129,7 @@ struct LinArgs {
   RopeArgs rope;         // EPI_ROPE only (n_out = (Hq + 2 Hkv) D / 2 pairs)
 };
 
-enum { GEMM_32x64 = 0, GEMM_64x128 = 1, GEMM_128x128 = 2 };
+enum { GEMM_32x64 = 0, GEMM_64x128 = 1, GEMM_128x128 = 2, GEMM_128x256 = 3 };
 
 struct GemmPlan {
   int cfg, mt, nt;
