@@ -25,9 +25,16 @@
 //    to the workspace; the last part to finish a tile (per-tile arrival
 //    counter, reset by that same workgroup) adds the S parts in a fixed order
 //    and runs the epilogue, so results do not depend on arrival order.
+//  * Balance (tiles of up to 64 rows): when the tiles are more than the CUs
+//    but not a whole number of rounds, the whole rounds run as they are and
+//    the remaining tiles are split over K (the last round is a fraction of a
+//    tile, not a tile).
 //  * Tile order is XCD-aware: the hardware deals workgroups round-robin over
-//    the 8 XCDs; each XCD takes a contiguous range of tiles, M tiles fastest,
-//    so the M tiles that share a weight tile share one L2.
+//    the 8 XCDs; each XCD takes a contiguous range of whole tiles, then a
+//    contiguous range of split parts, M tiles fastest, so the M tiles that
+//    share a weight tile share one L2.
+#include <algorithm>
+
 #include "coherent.h"
 #include "linear.h"
 
@@ -40,7 +47,8 @@ typedef h16 h16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int BK = 64;  // K elements per stage (one 128-byte chunk of a row)
+constexpr int BK = 64;     // K elements per stage (one 128-byte chunk of a row)
+constexpr int kCUs = 256;  // compute units of an MI355X (8 XCDs x 32)
 
 __device__ __forceinline__ float dot8(h16x8 a, h16x8 b, float c) {
   c = __builtin_amdgcn_fdot2(h16x2{a[0], a[1]}, h16x2{b[0], b[1]}, c, false);
@@ -108,17 +116,27 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmParams p) {
   __shared__ int s_last;
 
   // ---- tile of this workgroup (XCD-aware order, M tiles fastest)
-  const int L = blockIdx.x;
-  const int T = (L & 7) * p.per_xcd + (L >> 3);
-  if (T >= p.n_mt * p.n_nt * p.splits) return;
-  const int mt = T % p.n_mt;
-  const int rest = T / p.n_mt;
-  const int sp = rest % p.splits;
-  const int nt = rest / p.splits;
-  const int m0 = mt * MT;
+  const int L = blockIdx.x, xcd = L & 7, li = L >> 3;
   const int n_kc = (p.K + BK - 1) / BK;
-  const int kc0 = sp * p.kc_per_split;
-  const int n_iter = min(n_kc, kc0 + p.kc_per_split) - kc0;  // >= 1 by construction
+  int mt, nt, sp = 0, splits = 1, kc_per = n_kc;
+  if (li < p.full_per_xcd) {  // a whole tile
+    const int t = xcd * p.full_per_xcd + li;
+    if (t >= p.nt_full * p.n_mt) return;
+    mt = t % p.n_mt;
+    nt = t / p.n_mt;
+  } else {  // a K range of a split tile
+    const int u = xcd * p.per_xcd + (li - p.full_per_xcd);
+    if (u >= p.split_items) return;
+    splits = p.splits;
+    kc_per = p.kc_per_split;
+    mt = u % p.n_mt;
+    const int rest = u / p.n_mt;
+    sp = rest % splits;
+    nt = p.nt_full + rest / splits;
+  }
+  const int m0 = mt * MT;
+  const int kc0 = sp * kc_per;
+  const int n_iter = min(n_kc, kc0 + kc_per) - kc0;  // >= 1 by construction
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -244,18 +262,18 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmParams p) {
     }
   }
 
-  const int tile = mt + p.n_mt * nt;
-  if (p.splits > 1) {
+  const int tile = mt + p.n_mt * (nt - p.nt_full);  // index among the split tiles
+  if (splits > 1) {
     // partial tile in the accumulator layout: lane-contiguous float4s
     constexpr int TILE_F = MT * NT;
-    float* part = p.part + ((size_t)tile * p.splits + sp) * TILE_F + wave * (FM * FN * 256);
+    float* part = p.part + ((size_t)tile * splits + sp) * TILE_F + wave * (FM * FN * 256);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) st_agent(part + ((i * FN + j) * 64 + lane) * 4, acc[i][j]);
     if constexpr (NORM) {
       if (wn == 0 && fg == 0) {
-        float* ssp = p.part_ss + ((size_t)tile * p.splits + sp) * MT;
+        float* ssp = p.part_ss + ((size_t)tile * splits + sp) * MT;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
           __hip_atomic_store(ssp + arow[i], ss[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -265,7 +283,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmParams p) {
     __syncthreads();
     if (tid == 0)
       s_last = __hip_atomic_fetch_add(p.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               p.splits - 1;
+               splits - 1;
     __syncthreads();
     if (!s_last) return;
     // the last part: add all parts in split order
@@ -275,12 +293,12 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmParams p) {
       for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // G parts in flight at a time, added in split order
     constexpr int G = (FM * FN >= 8) ? 1 : (FM * FN >= 4 ? 2 : 4);
-    for (int q0 = 0; q0 < p.splits; q0 += G) {
+    for (int q0 = 0; q0 < splits; q0 += G) {
       f32x4 t[G][FM][FN];
 #pragma unroll
       for (int u = 0; u < G; ++u) {
-        const int q = min(q0 + u, p.splits - 1);
-        const float* pq = p.part + ((size_t)tile * p.splits + q) * TILE_F + wave * (FM * FN * 256);
+        const int q = min(q0 + u, splits - 1);
+        const float* pq = p.part + ((size_t)tile * splits + q) * TILE_F + wave * (FM * FN * 256);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -288,7 +306,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmParams p) {
       }
 #pragma unroll
       for (int u = 0; u < G; ++u) {
-        if (q0 + u < p.splits) {
+        if (q0 + u < splits) {
 #pragma unroll
           for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -301,8 +319,8 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           float t = 0.f;
-          for (int q = 0; q < p.splits; ++q)
-            t += __hip_atomic_load(p.part_ss + ((size_t)tile * p.splits + q) * MT + arow[i], __ATOMIC_RELAXED,
+          for (int q = 0; q < splits; ++q)
+            t += __hip_atomic_load(p.part_ss + ((size_t)tile * splits + q) * MT + arow[i], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
           ss[i] = t;
         }
@@ -422,7 +440,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmParams p) {
 
 template <int MT, int NT, int NS, int EPI, int WM = 2, int WN = 2>
 hipError_t launch_cfg(const GemmParams& gp, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<MT, NT, NS, EPI, epi_norm(EPI), WM, WN>), dim3(gp.per_xcd * 8),
+  hipLaunchKernelGGL((gemm_kernel<MT, NT, NS, EPI, epi_norm(EPI), WM, WN>), dim3((gp.full_per_xcd + gp.per_xcd) * 8),
                      dim3(64 * WM * WN), 0, s, gp);
   return hipGetLastError();
 }
@@ -479,11 +497,28 @@ GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
   // part keeps at least 4 stages; a split tile needs an arrival counter
   int splits = 1;
   while (tiles * splits < 240 && n_kc / (splits + 1) >= 4 && splits < 16 && tiles <= kGemmMaxCounters) ++splits;
+  pl.nt_full = splits > 1 ? 0 : pl.n_nt;
+  // more tiles than CUs but not whole rounds: the whole rounds stay as they
+  // are and the last, partial round is split over K.  Only for tiles of up to
+  // 64 rows, which sit two or three to a CU: decode step at batch 64 1.95 ->
+  // 1.89 ms.  With 128 x 128 tiles the split parts share CUs with the whole
+  // tiles and slowed gate/up at batch 256 (38.9 -> 42.1 us).
+  int split_tiles = splits > 1 ? tiles : 0;
+  if (splits == 1 && pl.mt <= 64 && tiles > kCUs && tiles % kCUs != 0 &&
+      (tiles / kCUs * kCUs) % pl.n_mt == 0) {
+    const int rem = tiles % kCUs;
+    const int s = std::min(kCUs / rem, n_kc / 2);
+    if (s >= 2 && rem <= kGemmMaxCounters) {
+      pl.nt_full = tiles / kCUs * kCUs / pl.n_mt;
+      splits = s;
+      split_tiles = rem;
+    }
+  }
   pl.kc_per_split = ceil_div(n_kc, splits);
   pl.splits = ceil_div(n_kc, pl.kc_per_split);  // every part non-empty
   pl.part_bytes = pl.splits > 1
-                      ? align_up((size_t)tiles * pl.splits * pl.mt * pl.nt * 4, 256) +
-                            align_up((size_t)tiles * pl.splits * pl.mt * 4, 256)
+                      ? align_up((size_t)split_tiles * pl.splits * pl.mt * pl.nt * 4, 256) +
+                            align_up((size_t)split_tiles * pl.splits * pl.mt * 4, 256)
                       : 0;
   return pl;
 }
@@ -495,13 +530,17 @@ hipError_t launch_gemm(const LinArgs& a, int epi, const GemmPlan& pl, void* part
   gp.M = a.M; gp.K = a.K; gp.lda = a.lda; gp.ldo = a.ldo; gp.n_out = a.n_out;
   gp.eps = a.eps;
   gp.rope = a.rope;
-  gp.n_mt = pl.n_mt; gp.n_nt = pl.n_nt; gp.splits = pl.splits; gp.kc_per_split = pl.kc_per_split;
-  gp.per_xcd = ceil_div(pl.n_mt * pl.n_nt * pl.splits, 8);
+  gp.n_mt = pl.n_mt; gp.n_nt = pl.n_nt; gp.nt_full = pl.nt_full;
+  gp.splits = pl.splits; gp.kc_per_split = pl.kc_per_split;
+  gp.full_per_xcd = ceil_div(pl.nt_full * pl.n_mt, 8);
+  gp.split_items = pl.splits > 1 ? (pl.n_nt - pl.nt_full) * pl.n_mt * pl.splits : 0;
+  gp.per_xcd = ceil_div(gp.split_items, 8);
   gp.counters = counters;
   if (pl.splits > 1) {
+    const size_t split_tiles = (size_t)(pl.n_nt - pl.nt_full) * pl.n_mt;
     gp.part = static_cast<float*>(part_ws);
     gp.part_ss = reinterpret_cast<float*>(static_cast<char*>(part_ws) +
-                                          align_up((size_t)pl.n_mt * pl.n_nt * pl.splits * pl.mt * pl.nt * 4, 256));
+                                          align_up(split_tiles * pl.splits * pl.mt * pl.nt * 4, 256));
   }
   switch (epi) {
     case EPI_F16: return launch_epi<EPI_F16>(pl, gp, s);

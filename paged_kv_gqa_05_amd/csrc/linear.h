@@ -131,9 +131,11 @@ struct LinArgs {
 
 enum { GEMM_32x64 = 0, GEMM_64x128 = 1, GEMM_128x128 = 2, GEMM_128x256 = 3 };
 
+// Tiles of N-tile columns [0, nt_full) are computed whole; those of columns
+// [nt_full, n_nt) are cut into `splits` K ranges of kc_per_split stages.
 struct GemmPlan {
   int cfg, mt, nt;
-  int n_mt, n_nt, splits, kc_per_split;
+  int n_mt, n_nt, nt_full, splits, kc_per_split;
   size_t part_bytes;  // split-K workspace (0 without a split)
 };
 
@@ -148,7 +150,8 @@ struct GemmParams {
   int* counters;   // split-K arrival counters (zero between launches)
   int M, K, lda, ldo, n_out;
   float eps;
-  int n_mt, n_nt, splits, kc_per_split, per_xcd;
+  int n_mt, n_nt, nt_full, splits, kc_per_split;
+  int full_per_xcd, per_xcd, split_items;  // workgroups per XCD: whole tiles, then split parts
   RopeArgs rope;
 };
 
