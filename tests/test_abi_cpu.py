@@ -136,3 +136,17 @@ def test_graph_set_argument_errors():
     assert lib.pkv_graph_set_capture(None, None, None, 0, None, None, 1, None, 16, None, None, None, 0, None,
                                      C.byref(out)) == 1
     assert lib.pkv_graph_set_replay(None, 1, None, None) == 6
+
+
+def test_sample_and_prefill_argument_errors():
+    """Host checks of pkv_sample and pkv_prefill reject bad sizes and NULL
+    buffers before anything is enqueued (no device is touched)."""
+    lib = pkv.lib()
+    for batch, vocab, msg in ((0, 10, b"batch and vocab"), (2, 0, b"batch and vocab"),
+                              (2, (1 << 24) + 1, b"2^24"), (2, 10, b"NULL")):
+        assert lib.pkv_sample(None, batch, vocab, None, None, None, None, None, None, None) == 1
+        assert msg in lib.pkv_last_error()
+    n = C.c_size_t()
+    assert lib.pkv_prefill_workspace_bytes(None, None, 4, 1, 16, C.byref(n)) == 1
+    assert lib.pkv_prefill(None, None, None, None, None, 1, 4, None, 1, 16, None, None, 0, None) == 1
+    assert b"model / cache is NULL" in lib.pkv_last_error()
