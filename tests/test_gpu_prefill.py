@@ -187,3 +187,19 @@ def test_prefill_fp8_cache(lib):
         dg = oracle.e4m3_decode(got[m]) * sc
         dr = oracle.e4m3_decode(ref[m]) * sc
         assert np.all(np.abs(dg - dr) <= ATOL + RTOL * np.abs(dr) + np.abs(dr) / 8 + sc * 2.0 ** -9)
+
+
+@pytest.mark.parametrize("shape,new_lens,prior_lens,seed", [
+    # 7B head grouping (G = 7: chunks of 16 query rows straddle tokens unevenly)
+    (inp.Shape(512, 14, 2, 128, 1024, 500, 1), [37, 5, 64], [0, 21, 90], 5010),
+    # MHA (G = 1: 16 tokens of one head per chunk)
+    (inp.Shape(512, 4, 4, 128, 1024, 500, 1), [50, 3], [16, 7], 5011),
+    # long prompts: up to 63 pages per chunk, many rescaled page groups
+    (inp.Shape(512, 12, 2, 128, 1024, 500, 1), [700, 260], [300, 0], 5012),
+])
+def test_prefill_group_sizes_and_long_prompts(lib, shape, new_lens, prior_lens, seed):
+    case = prefill_case(shape, new_lens, prior_lens, seed)
+    g_logits, gk, gv = run_prefill_gpu(lib, shape, case)
+    r_logits, rk, rv = run_prefill_oracle(shape, case)
+    assert_parity(g_logits, r_logits, "last-token logits")
+    check_cache(case, shape, gk, gv, rk, rv)
