@@ -400,6 +400,7 @@ pkv_status pkv_prefill(const pkv_model* m, pkv_cache* cache, const int32_t* toke
   pre.seq_starts = seq_starts; pre.prior_lens = prior_lens; pre.bt = bt; pre.bt_stride = bt_stride;
   pre.items = pb.items; pre.n_items = pb.n_items; pre.max_items = pb.max_items;
   pre.n_seqs = n_seqs; pre.n_tokens = n_tokens; pre.max_context = max_context;
+  PKV_HIP(launch_prefill_items(pre, d.num_q_heads / d.num_kv_heads, s));
   for (int l = 0; l < d.num_layers; ++l)
     PKV_HIP(run_layer(m, cache, l, sb.h, pb.bt_tok, pb.stride_tok, pb.lens_tok, n_tokens, sb, plan, s, &pre));
   // the last new token of every sequence -> final RMSNorm -> LM head

@@ -32,6 +32,10 @@ struct PrefillAttnArgs {
   float scale, k_scale, v_scale;
 };
 int prefill_max_items(int n_tokens, int n_seqs, int group);
+// The (sequence, 16-row chunk) work list, built once per prefill call from
+// seq_starts (reads seq_starts, n_seqs, n_tokens, items, n_items, max_items).
+hipError_t launch_prefill_items(const PrefillAttnArgs& a, int group, hipStream_t s);
+// Attention of every layer, over the work list built above.
 hipError_t launch_prefill_attention(const PrefillAttnArgs& a, hipStream_t s);
 
 hipError_t launch_argmax(const void* logits, int batch, int vocab, int32_t* tokens, const int32_t* lens,

@@ -25,7 +25,8 @@
 //    at or past the sequence's cached length (prior + new tokens) are zeroed
 //    before the PV product, since unwritten slots may hold anything.
 //  * The (sequence, chunk) work list is built on the device by a one-workgroup
-//    kernel from the sequence offsets, so the host needs no copy of them.
+//    kernel from the sequence offsets (once per prefill call, shared by all
+//    layers), so the host needs no copy of them.
 #include "ops.h"
 
 namespace pkv {
@@ -292,13 +293,15 @@ int prefill_max_items(int n_tokens, int n_seqs, int group) {
   return (int)(((long long)n_tokens * group + 15) / 16) + n_seqs;
 }
 
+hipError_t launch_prefill_items(const PrefillAttnArgs& a, int group, hipStream_t s) {
+  hipLaunchKernelGGL(items_kernel, dim3(1), dim3(1024), 0, s, a.seq_starts, a.n_seqs, a.n_tokens, group,
+                     reinterpret_cast<int2*>(a.items), a.n_items, a.max_items);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill_attention(const PrefillAttnArgs& a, hipStream_t s) {
   if (a.head_dim != 64 && a.head_dim != 128) return hipErrorInvalidValue;
   const int group = a.hq / a.hkv;
-  hipLaunchKernelGGL(items_kernel, dim3(1), dim3(1024), 0, s, a.seq_starts, a.n_seqs, a.n_tokens, group,
-                     reinterpret_cast<int2*>(a.items), a.n_items, a.max_items);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   Params p{};
   p.k_pool = static_cast<const unsigned char*>(a.k_pool);
   p.v_pool = static_cast<const unsigned char*>(a.v_pool);
