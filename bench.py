@@ -365,6 +365,9 @@ def main():
     ap.add_argument("--prompt-fill", choices=("prefill", "decode"), default="prefill",
                     help="prompts enter by one batched prefill call (timed) or one decode step per position")
     ap.add_argument("--prefill-repeats", type=int, default=3, help="timed repeats of the prefill call")
+    ap.add_argument("--batches-7b", default="1,32,64,128",
+                    help="batches of the 28-layer 7B-shape decode (512-token prompts), reported beside the 1.5B lines")
+    ap.add_argument("--prompt-7b", type=int, default=512)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "kernel for scaling rocprof FETCH_SIZE / WRITE_SIZE)")
@@ -424,6 +427,29 @@ def main():
         per_batch_fp8[n] = r
         log(f"batch {n}, E4M3 KV cache: {r['ms_per_step']:.3f} ms/step, {r['tok_s']:.0f} tok/s")
 
+    per_batch_7b = {}
+    batches_7b = [int(x) for x in args.batches_7b.split(",") if x.strip()] if batches else []
+    if batches_7b:
+        model.close()   # the 1.5B weights stay for the CPU baseline
+        torch.cuda.empty_cache()
+        shape7 = inp.QWEN7
+        log(f"generating {shape7} weights on the device")
+        w7 = inp.model_weights_torch(shape7, seed=1007)
+        model7 = pkv.Model(shape7, w7, max_positions=max(4096, args.prompt_7b + args.warmup + args.steps + 1))
+        for n in batches_7b:
+            r = time_decode(pkv, torch, model7, shape7, n, args.prompt_7b, args.warmup, args.steps, seed=3007 + n,
+                            prompt_fill=args.prompt_fill, prefill_repeats=1)
+            nbytes = step_bytes(shape7, n, r["mean_context"])
+            r["bytes_per_step"] = nbytes
+            r["roofline_ms"] = nbytes / (HBM_PEAK_GBS * 1e9) * 1e3
+            r["frac_of_roofline"] = r["roofline_ms"] / r["ms_per_step"]
+            per_batch_7b[n] = r
+            log(f"7B batch {n}: {r['ms_per_step']:.3f} ms/step, {r['tok_s']:.0f} tok/s, "
+                f"{100 * r['frac_of_roofline']:.1f}% of the HBM roofline")
+        model7.close()
+        del w7
+        torch.cuda.empty_cache()
+
     attn = {}
     if not args.no_attn:
         attn["attn15"] = time_attention(pkv, torch, inp.ATTN15, 28, args.attn_rounds, seed=11)
@@ -474,6 +500,8 @@ def main():
                    for n, r in per_batch.items()},
         "decode_fp8_kv": {str(n): {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                           for n, r in per_batch_fp8.items()},
+        "decode_7b": {str(n): {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+                      for n, r in per_batch_7b.items()},
         "attention": attn,
         "sampling": sampling,
         "roofline": roofline,
