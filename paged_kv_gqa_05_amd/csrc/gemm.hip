@@ -497,6 +497,11 @@ GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
   // part keeps at least 4 stages; a split tile needs an arrival counter
   int splits = 1;
   while (tiles * splits < 240 && n_kc / (splits + 1) >= 4 && splits < 16 && tiles <= kGemmMaxCounters) ++splits;
+  // long reductions: more parts while a part is longer than 40 stages and the
+  // grid stays within two workgroups per CU (7B down projection at batch
+  // 128, K = 18944: 5 parts of 60 stages 71 us, 8 parts of 37 stages 58 us)
+  if (splits > 1)
+    while (ceil_div(n_kc, splits) > 40 && tiles * (splits + 1) <= 2 * kCUs && splits < 16) ++splits;
   pl.nt_full = splits > 1 ? 0 : pl.n_nt;
   // more tiles than CUs but not whole rounds: the whole rounds stay as they
   // are and the last, partial round is split over K.  Only for tiles of up to
