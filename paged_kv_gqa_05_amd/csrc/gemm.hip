@@ -452,6 +452,13 @@ hipError_t launch_epi(const GemmPlan& pl, const GemmParams& gp, hipStream_t s) {
     case GEMM_64x128: return launch_cfg<64, 128, 3, EPI>(gp, s);
     case GEMM_128x128: return launch_cfg<128, 128, 2, EPI, 4, 2>(gp, s);
     case GEMM_128x256: return launch_cfg<128, 256, 3, EPI, 2, 4>(gp, s);
+    // the gate/up plans (the planner picks them for EPI_SILU only)
+    case GEMM_128x128_S3:
+      if constexpr (EPI == EPI_SILU) return launch_cfg<128, 128, 3, EPI, 4, 2>(gp, s);
+      return hipErrorInvalidValue;
+    case GEMM_128x160:
+      if constexpr (EPI == EPI_SILU) return launch_cfg<128, 160, 3, EPI, 4, 1>(gp, s);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
@@ -489,6 +496,30 @@ GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
     pl.mt = 128;
     pl.nt = 256;
   }
+  // gate/up (paired rows) at batch 97..1024: 128-row tiles 128 or 160 weight
+  // rows wide, whichever loads fewer stage bytes on the busiest CU (rounds of
+  // the 256 CUs x rows per stage).  Bound by each CU's stage loads, the
+  // per-CU bytes set the time: 280 tiles of 128 x 128 leave 24 CUs with two
+  // tiles, 224 tiles of 128 x 160 fit one round (gate/up at batch 256: 38.2
+  // -> 30.6 us; 7B gate/up at batch 128: 85.7 -> 64.2 us).  A single round
+  // holds one workgroup per CU, which affords a third stage (gate/up at batch
+  // 128: 27.8 -> 25.1 us with 128 x 128).  These plans are never split.
+  bool whole = false;
+  if (epi == EPI_SILU && pl.cfg != GEMM_128x256 && m_cap >= 128 && M <= 1024) {
+    const int t128 = ceil_div(M, 128) * ceil_div(n_out, 64), t160 = ceil_div(M, 128) * ceil_div(n_out, 80);
+    const long c128 = (long)ceil_div(t128, kCUs) * 256, c160 = (long)ceil_div(t160, kCUs) * 288;
+    if (c160 < c128) {
+      pl.cfg = GEMM_128x160;
+      pl.mt = 128;
+      pl.nt = 160;
+      whole = true;
+    } else if (t128 <= kCUs) {
+      pl.cfg = GEMM_128x128_S3;
+      pl.mt = 128;
+      pl.nt = 128;
+      whole = true;
+    }
+  }
   pl.n_mt = ceil_div(M, pl.mt);
   pl.n_nt = ceil_div(n_out, pair ? pl.nt / 2 : pl.nt);
   const int n_kc = ceil_div(K, 64);
@@ -496,7 +527,8 @@ GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
   // split K while the grid holds fewer than ~one workgroup per CU and every
   // part keeps at least 4 stages; a split tile needs an arrival counter
   int splits = 1;
-  while (tiles * splits < 240 && n_kc / (splits + 1) >= 4 && splits < 16 && tiles <= kGemmMaxCounters) ++splits;
+  while (!whole && tiles * splits < 240 && n_kc / (splits + 1) >= 4 && splits < 16 && tiles <= kGemmMaxCounters)
+    ++splits;
   // long reductions: more parts while a part is longer than 40 stages and the
   // grid stays within two workgroups per CU (7B down projection at batch
   // 128, K = 18944: 5 parts of 60 stages 71 us, 8 parts of 37 stages 58 us)
@@ -509,7 +541,7 @@ GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
   // 1.89 ms.  With 128 x 128 tiles the split parts share CUs with the whole
   // tiles and slowed gate/up at batch 256 (38.9 -> 42.1 us).
   int split_tiles = splits > 1 ? tiles : 0;
-  if (splits == 1 && pl.mt <= 64 && tiles > kCUs && tiles % kCUs != 0 &&
+  if (splits == 1 && !whole && pl.mt <= 64 && tiles > kCUs && tiles % kCUs != 0 &&
       (tiles / kCUs * kCUs) % pl.n_mt == 0) {
     const int rem = tiles % kCUs;
     const int s = std::min(kCUs / rem, n_kc / 2);
