@@ -418,7 +418,9 @@ AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int 
   //  * else, when those exceed 256 workgroups, 4 waves x 4 blocks (256
   //    tokens, three per CU) if that fits in 768;
   //  * calls that need several rounds anyway keep 4 x 8 (measured best on the
-  //    long fp8 workload).
+  //    long fp8 workload);
+  //  * rows short enough for one 4-wave partition take no more blocks per
+  //    wave than they need (at least 4).
   // Fewer blocks per wave also when the grid would hold fewer workgroups than
   // CUs.  The estimate uses max_context for every row.
   const int mc = max_context > 0 ? max_context : 1;
@@ -431,6 +433,11 @@ AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int 
   } else {
     if (wgs(4, 8) > 256 && wgs(4, 4) <= 768) nt = 4;
     while (nt > 2 && wgs(4, nt) < 256 && ceil_div(mc, 64 * nt) > 1) nt /= 2;
+    // short rows: no more blocks per wave than a row can give each of the 4
+    // waves (a wave issues the loads of all nt blocks; at 165 tokens, 4 and
+    // not 8: decode step at batch 1 1.072 -> 1.027 ms, batch 64 1.887 -> 1.840 ms)
+    const int per_wave = ceil_div(ceil_div(mc, 16), 4);
+    while (nt > 4 && per_wave <= nt / 2) nt /= 2;
   }
   p.waves = waves;
   p.nt = nt;

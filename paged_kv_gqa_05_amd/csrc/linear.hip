@@ -83,6 +83,24 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinArgs a) {
   const h16* xrow[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) xrow[m] = a.A + (size_t)min(m, a.M - 1) * a.lda;
+  // At batch <= 4 the epilogue's inputs are fetched ahead of the weights: the
+  // QKV rows' context lengths and bias (the block id and the (cos, sin) that
+  // depend on the length follow once the weights are consumed, while the
+  // lanes reduce), and the residual of the O and down projections.  Fetched in
+  // the epilogue they were a chain of memory round trips after the reduction.
+  constexpr bool EARLY = MT <= 4 && (EPI == EPI_ROPE || EPI == EPI_RESID);
+  [[maybe_unused]] RopeRow rr[EARLY && EPI == EPI_ROPE ? MT : 1];
+  [[maybe_unused]] float2 rcs[EARLY && EPI == EPI_ROPE ? MT : 1], rbias;
+  [[maybe_unused]] float res[EARLY && EPI == EPI_RESID ? MT : 1];
+  if constexpr (EARLY && EPI == EPI_ROPE) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) rr[m] = rope_row_len(a.rope, min(m, a.M - 1));
+    rbias = rope_bias(a.rope, a.bias, col);
+  }
+  if constexpr (EARLY && EPI == EPI_RESID) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) res[m] = (float)static_cast<const h16*>(a.out)[(size_t)min(m, a.M - 1) * a.ldo + col];
+  }
   float acc0[MT], acc1[MT], ss[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc0[m] = acc1[m] = ss[m] = 0.f;
@@ -116,6 +134,13 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinArgs a) {
         acc0[m] = dot8(valid ? wv0[u] : zero, xg, acc0[m]);
         if constexpr (PAIR) acc1[m] = dot8(valid ? wv1[u] : zero, xg, acc1[m]);
       }
+    }
+  }
+  if constexpr (EARLY && EPI == EPI_ROPE) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      rope_row_blk(a.rope, min(m, a.M - 1), rr[m]);
+      rcs[m] = rope_cs(a.rope, rr[m], col);
     }
   }
   // reduce over the row's lanes: within the wave, then across waves in LDS
@@ -159,7 +184,12 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinArgs a) {
   for (int m = 0; m < MT; ++m) {
     if (m < a.M && (m % LW) == lig) {
       const float r = NORM ? rsqrtf(ss[m] / (float)a.K + a.eps) : 1.0f;
-      epilogue<EPI>(a, m, col, acc0[m] * r, acc1[m] * r);
+      if constexpr (EARLY && EPI == EPI_ROPE)
+        rope_put(a.rope, rr[m], m, col, acc0[m] * r + rbias.x, acc1[m] * r + rbias.y, rcs[m]);
+      else if constexpr (EARLY && EPI == EPI_RESID)
+        static_cast<h16*>(a.out)[(size_t)m * a.ldo + col] = (h16)(res[m] + acc0[m] * r);
+      else
+        epilogue<EPI>(a, m, col, acc0[m] * r, acc1[m] * r);
     }
   }
 }
