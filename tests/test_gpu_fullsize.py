@@ -39,8 +39,10 @@ def _layer_shape(shape):
                      shape.rms_eps, shape.rope_theta)
 
 
-@pytest.mark.parametrize("name,batch", [("1.5B", 1), ("1.5B", 64), ("1.5B", 128), ("1.5B", 256),
-                                        ("7B", 1), ("7B", 32), ("7B", 64), ("7B", 128)])
+# batch 100: a partial 128-row tile in the gate/up plans (3-stage 128 x 128 tiles at the 1.5B
+# shape, 128 x 160 tiles at the 7B shape, whose last column tile is partial too)
+@pytest.mark.parametrize("name,batch", [("1.5B", 1), ("1.5B", 64), ("1.5B", 100), ("1.5B", 128), ("1.5B", 256),
+                                        ("7B", 1), ("7B", 32), ("7B", 64), ("7B", 100), ("7B", 128)])
 def test_decode_layer_full_shape(lib, name, batch):
     shape = _layer_shape(inp.QWEN15 if name == "1.5B" else inp.QWEN7)
     case = inp.tiny_layer_case(seed=4000 + batch, batch=batch, ctx_lo=100, ctx_hi=700, shape=shape)
