@@ -534,15 +534,23 @@ GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
     while (!whole && tiles * (splits + 1) <= kCUs && n_kc >= 6 * (splits + 1) && splits < 16 &&
            tiles <= kGemmMaxCounters)
       ++splits;
+  } else if (pl.n_mt == 1) {
+    // one row of tiles: a grid a little over one workgroup per CU leaves the
+    // CUs that get two with twice the stages (7B at batch 32: QKV 3 parts 12.3
+    // us vs 4 parts 15.3 us; O 4 vs 5 parts 10.5 vs 13.7 us; down 4 vs 8 parts
+    // 29.6 vs 31.6 us), so the grid stays within one workgroup per CU
+    while (!whole && tiles * (splits + 1) <= kCUs && n_kc / (splits + 1) >= 4 && splits < 16 &&
+           tiles <= kGemmMaxCounters)
+      ++splits;
   } else {
     while (!whole && tiles * splits < 240 && n_kc / (splits + 1) >= 4 && splits < 16 && tiles <= kGemmMaxCounters)
       ++splits;
+    // long reductions: more parts while a part is longer than 40 stages and the
+    // grid stays within two workgroups per CU (7B down projection at batch
+    // 128, K = 18944: 5 parts of 60 stages 71 us, 8 parts of 37 stages 58 us)
+    if (splits > 1)
+      while (ceil_div(n_kc, splits) > 40 && tiles * (splits + 1) <= 2 * kCUs && splits < 16) ++splits;
   }
-  // long reductions: more parts while a part is longer than 40 stages and the
-  // grid stays within two workgroups per CU (7B down projection at batch
-  // 128, K = 18944: 5 parts of 60 stages 71 us, 8 parts of 37 stages 58 us)
-  if (splits > 1)
-    while (ceil_div(n_kc, splits) > 40 && tiles * (splits + 1) <= 2 * kCUs && splits < 16) ++splits;
   pl.nt_full = splits > 1 ? 0 : pl.n_nt;
   // more tiles than CUs but not whole rounds: the whole rounds stay as they
   // are and the last, partial round is split over K.  Only for tiles of up to
