@@ -543,13 +543,16 @@ GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
            tiles <= kGemmMaxCounters)
       ++splits;
   } else {
-    while (!whole && tiles * splits < 240 && n_kc / (splits + 1) >= 4 && splits < 16 && tiles <= kGemmMaxCounters)
+    // several rows of tiles: within one workgroup per CU, or two for 32-row
+    // tiles when there are at least 96 of them (they sit two to a CU: 7B at
+    // batch 64, QKV 3 parts (432 workgroups) 16.7 us vs 2 parts (288) 20.4 us;
+    // O 4 parts 13.7 vs 3 parts 15.1 us).  Grids a little over a multiple of
+    // 256 leave some CUs with twice the stages (7B down projection at batch
+    // 128 with 64 x 128 tiles: 4 parts 48.3 us, 5 parts 71 us, 8 parts 58 us).
+    const int cap = (pl.mt <= 32 && tiles >= 96) ? 2 * kCUs : kCUs;
+    while (!whole && tiles * (splits + 1) <= cap && n_kc / (splits + 1) >= 4 && splits < 16 &&
+           tiles <= kGemmMaxCounters)
       ++splits;
-    // long reductions: more parts while a part is longer than 40 stages and the
-    // grid stays within two workgroups per CU (7B down projection at batch
-    // 128, K = 18944: 5 parts of 60 stages 71 us, 8 parts of 37 stages 58 us)
-    if (splits > 1)
-      while (ceil_div(n_kc, splits) > 40 && tiles * (splits + 1) <= 2 * kCUs && splits < 16) ++splits;
   }
   pl.nt_full = splits > 1 ? 0 : pl.n_nt;
   // more tiles than CUs but not whole rounds: the whole rounds stay as they
