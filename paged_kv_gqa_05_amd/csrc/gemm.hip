@@ -452,12 +452,15 @@ hipError_t launch_epi(const GemmPlan& pl, const GemmParams& gp, hipStream_t s) {
     case GEMM_64x128: return launch_cfg<64, 128, 3, EPI>(gp, s);
     case GEMM_128x128: return launch_cfg<128, 128, 2, EPI, 4, 2>(gp, s);
     case GEMM_128x256: return launch_cfg<128, 256, 3, EPI, 2, 4>(gp, s);
-    // the gate/up plans (the planner picks them for EPI_SILU only)
+    // plans the planner picks for gate/up (EPI_SILU) or O/down (EPI_RESID) only
     case GEMM_128x128_S3:
-      if constexpr (EPI == EPI_SILU) return launch_cfg<128, 128, 3, EPI, 4, 2>(gp, s);
+      if constexpr (EPI == EPI_SILU || EPI == EPI_RESID) return launch_cfg<128, 128, 3, EPI, 4, 2>(gp, s);
       return hipErrorInvalidValue;
     case GEMM_128x160:
       if constexpr (EPI == EPI_SILU) return launch_cfg<128, 160, 3, EPI, 4, 1>(gp, s);
+      return hipErrorInvalidValue;
+    case GEMM_64x64:
+      if constexpr (EPI == EPI_RESID) return launch_cfg<64, 64, 4, EPI, 2, 2>(gp, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -520,6 +523,39 @@ GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
       whole = true;
     }
   }
+  // O and down projections over long reductions (K >= 3072) at decode batches:
+  // of four tile shapes, each with its split count by the rules below, the
+  // one with the fewest stage bytes on the busiest CU (rounds of the CUs x
+  // stages per part x bytes per stage) plus twice the fp32 partial bytes the
+  // last part of a tile reads back.  Measured over the O and down shapes of
+  // the 1.5B and 7B models at batch 32-256 it keeps or beats every earlier
+  // plan (7B down at batch 64: 64 x 64 tiles, 42.7 -> 35.0 us; at batch 256:
+  // 3-stage 128 x 128 tiles, 80.1 -> 64.7 us; 1.5B down at batch 128: 64 x
+  // 64 tiles, 21.9 -> 18.8 us).
+  int planned_splits = 0;
+  if (epi == EPI_RESID && K >= 3072 && M <= 1024) {
+    static const int kRes[4][3] = {
+        {GEMM_32x64, 32, 64}, {GEMM_64x64, 64, 64}, {GEMM_64x128, 64, 128}, {GEMM_128x128_S3, 128, 128}};
+    const int kc = ceil_div(K, 64);
+    long best = -1;
+    for (const auto& r : kRes) {
+      const int mt = r[1], nt = r[2], nm = ceil_div(M, mt), t = nm * ceil_div(n_out, nt);
+      if (mt > m_cap || t > kGemmMaxCounters) continue;
+      const int cap = (mt <= 32 && t >= 96 && nm > 1) ? 2 * kCUs : kCUs;
+      int sp = 1;
+      while (t * (sp + 1) <= cap && kc / (sp + 1) >= 4 && sp < 16) ++sp;
+      const int per = ceil_div(kc, sp);
+      sp = ceil_div(kc, per);
+      const long cost = (long)ceil_div(t * sp, kCUs) * per * (mt + nt) * 128 + (sp > 1 ? 2L * sp * mt * nt * 4 : 0);
+      if (best < 0 || cost < best) {
+        best = cost;
+        pl.cfg = r[0];
+        pl.mt = mt;
+        pl.nt = nt;
+        planned_splits = sp;
+      }
+    }
+  }
   pl.n_mt = ceil_div(M, pl.mt);
   pl.n_nt = ceil_div(n_out, pair ? pl.nt / 2 : pl.nt);
   const int n_kc = ceil_div(K, 64);
@@ -527,7 +563,9 @@ GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
   // split K while the grid holds fewer than ~one workgroup per CU and every
   // part keeps at least 4 stages; a split tile needs an arrival counter
   int splits = 1;
-  if (K < 3072) {
+  if (planned_splits > 0) {
+    splits = planned_splits;
+  } else if (K < 3072) {
     // short reductions: as many parts as keep the grid within one workgroup
     // per CU and every part at least 6 stages (1.5B O projection at batch
     // 256: 1 part, 11.0 -> 10.0 us; at batch 32: 4 parts, 7.5 -> 7.1 us)
@@ -561,7 +599,7 @@ GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
   // 1.89 ms.  With 128 x 128 tiles the split parts share CUs with the whole
   // tiles and slowed gate/up at batch 256 (38.9 -> 42.1 us).
   int split_tiles = splits > 1 ? tiles : 0;
-  if (splits == 1 && !whole && pl.mt <= 64 && tiles > kCUs && tiles % kCUs != 0 &&
+  if (splits == 1 && !whole && planned_splits == 0 && pl.mt <= 64 && tiles > kCUs && tiles % kCUs != 0 &&
       (tiles / kCUs * kCUs) % pl.n_mt == 0) {
     const int rem = tiles % kCUs;
     const int s = std::min(kCUs / rem, n_kc / 2);

@@ -129,7 +129,8 @@ struct LinArgs {
   RopeArgs rope;         // EPI_ROPE only (n_out = (Hq + 2 Hkv) D / 2 pairs)
 };
 
-enum { GEMM_32x64 = 0, GEMM_64x128 = 1, GEMM_128x128 = 2, GEMM_128x256 = 3, GEMM_128x128_S3 = 4, GEMM_128x160 = 5 };
+enum { GEMM_32x64 = 0, GEMM_64x128 = 1, GEMM_128x128 = 2, GEMM_128x256 = 3, GEMM_128x128_S3 = 4, GEMM_128x160 = 5,
+       GEMM_64x64 = 6 };
 
 // Tiles of N-tile columns [0, nt_full) are computed whole; those of columns
 // [nt_full, n_nt) are cut into `splits` K ranges of kc_per_split stages.
