@@ -481,7 +481,9 @@ hipError_t launch_epi(const GemmPlan& pl, const GemmParams& gp, hipStream_t s) {
 // rounded up to 32.  Prefill-sized long reductions (K >= 4096 with at least
 // 256 tiles of 128 x 256) take 128 x 256 tiles with 3 stages on 2 x 4 waves:
 // the deeper pipeline pays over the long K (down projection, 32768 rows:
-// 934 us vs 1645 us with 128 x 128 and 2 stages).
+// 934 us vs 1645 us with 128 x 128 and 2 stages).  So do all projections of
+// more than 1024 rows (32768 rows at the 1.5B shape: QKV 390 -> 328 us, O 252
+// -> 239 us, gate/up 2918 -> 2734 us: half the stage bytes per flop).
 GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
   const bool pair = epi_pair(epi);
   static const int kCfg[3][3] = {{GEMM_32x64, 32, 64}, {GEMM_64x128, 64, 128}, {GEMM_128x128, 128, 128}};
@@ -494,7 +496,7 @@ GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
   pl.cfg = kCfg[c][0];
   pl.mt = kCfg[c][1];
   pl.nt = kCfg[c][2];
-  if (K >= 4096 && ceil_div(M, 128) * ceil_div(n_out, pair ? 128 : 256) >= 256) {
+  if ((K >= 4096 || M > 1024) && ceil_div(M, 128) * ceil_div(n_out, pair ? 128 : 256) >= 256) {
     pl.cfg = GEMM_128x256;
     pl.mt = 128;
     pl.nt = 256;
