@@ -363,34 +363,41 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmParams p) {
       pok[j] = col < p.n_out;
       pc[j] = min(col, p.n_out - 1);
     }
-    RopeRow rr[FM][4];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) rr[i][v] = rope_row_len(p.rope, mrow[i][v]);
     float2 bias[FP];
 #pragma unroll
     for (int j = 0; j < FP; ++j) bias[j] = rope_bias(p.rope, p.bias, pc[j]);
+    // metadata in groups of RG fragment rows (all of them up to 4 row x pair
+    // fragments a lane; one at a time above, where a whole tile's worth
+    // would not fit in registers)
+    constexpr int RG = FM * FP <= 4 ? FM : 1;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i0 = 0; i0 < FM; i0 += RG) {
+      RopeRow rr[RG][4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) rope_row_blk(p.rope, mrow[i][v], rr[i][v]);
-    float2 cs[FM][4][FP];
+      for (int ii = 0; ii < RG; ++ii)
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+        for (int v = 0; v < 4; ++v) rr[ii][v] = rope_row_len(p.rope, mrow[i0 + ii][v]);
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+      for (int ii = 0; ii < RG; ++ii)
 #pragma unroll
-        for (int j = 0; j < FP; ++j) cs[i][v][j] = rope_cs(p.rope, rr[i][v], pc[j]);
+        for (int v = 0; v < 4; ++v) rope_row_blk(p.rope, mrow[i0 + ii][v], rr[ii][v]);
+      float2 cs[RG][4][FP];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int ii = 0; ii < RG; ++ii)
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+        for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int j = 0; j < FP; ++j)
-          if (mok[i][v] && pok[j])
-            rope_put(p.rope, rr[i][v], mrow[i][v], pc[j], acc[i][j][v] * rs[i][v] + bias[j].x,
-                     acc[i][j + FP][v] * rs[i][v] + bias[j].y, cs[i][v][j]);
+          for (int j = 0; j < FP; ++j) cs[ii][v][j] = rope_cs(p.rope, rr[ii][v], pc[j]);
+#pragma unroll
+      for (int ii = 0; ii < RG; ++ii)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int j = 0; j < FP; ++j)
+            if (mok[i0 + ii][v] && pok[j])
+              rope_put(p.rope, rr[ii][v], mrow[i0 + ii][v], pc[j], acc[i0 + ii][j][v] * rs[i0 + ii][v] + bias[j].x,
+                       acc[i0 + ii][j + FP][v] * rs[i0 + ii][v] + bias[j].y, cs[ii][v][j]);
+    }
   } else if constexpr (EPI == EPI_SILU) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -413,28 +420,34 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmParams p) {
       cok[j] = col < p.n_out;
       cc[j] = min(col, p.n_out - 1);
     }
-    // EPI_F16: the bias of each column; EPI_RESID: the residual h itself
-    float add[FM][4][FN];
+    // EPI_F16: the bias of each column; EPI_RESID: the residual h itself.
+    // Loaded in groups of FG fragment rows (all of them up to 8 fragments a
+    // lane; one at a time above, where a whole tile's worth would spill).
+    constexpr int FG = FM * FN <= 8 ? FM : 1;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i0 = 0; i0 < FM; i0 += FG) {
+      float add[FG][4][FN];
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+      for (int ii = 0; ii < FG; ++ii)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          if constexpr (EPI == EPI_F16)
-            add[i][v][j] = p.bias ? (float)p.bias[cc[j]] : 0.f;
-          else
-            add[i][v][j] = (float)static_cast<const h16*>(p.out)[(size_t)mrow[i][v] * p.ldo + cc[j]];
-        }
+        for (int v = 0; v < 4; ++v)
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+          for (int j = 0; j < FN; ++j) {
+            if constexpr (EPI == EPI_F16)
+              add[ii][v][j] = p.bias ? (float)p.bias[cc[j]] : 0.f;
+            else
+              add[ii][v][j] = (float)static_cast<const h16*>(p.out)[(size_t)mrow[i0 + ii][v] * p.ldo + cc[j]];
+          }
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+      for (int ii = 0; ii < FG; ++ii)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          if (mok[i][v] && cok[j])
-            static_cast<h16*>(p.out)[(size_t)mrow[i][v] * p.ldo + cc[j]] =
-                (h16)(acc[i][j][v] * rs[i][v] + add[i][v][j]);
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            if (mok[i0 + ii][v] && cok[j])
+              static_cast<h16*>(p.out)[(size_t)mrow[i0 + ii][v] * p.ldo + cc[j]] =
+                  (h16)(acc[i0 + ii][j][v] * rs[i0 + ii][v] + add[ii][v][j]);
+    }
   }
 }
 
@@ -462,8 +475,8 @@ hipError_t launch_epi(const GemmPlan& pl, const GemmParams& gp, hipStream_t s) {
     case GEMM_64x64:
       if constexpr (EPI == EPI_RESID) return launch_cfg<64, 64, 4, EPI, 2, 2>(gp, s);
       return hipErrorInvalidValue;
-    case GEMM_256x256:
-      if constexpr (EPI == EPI_SILU) return launch_cfg<256, 256, 2, EPI, 4, 2>(gp, s);
+    case GEMM_256x256:  // not for the QKV epilogue (its per-row RoPE state would need scratch)
+      if constexpr (EPI != EPI_ROPE) return launch_cfg<256, 256, 2, EPI, 4, 2>(gp, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -503,9 +516,11 @@ GemmPlan gemm_plan(int M, int n_out, int K, int epi) {
     pl.cfg = GEMM_128x256;
     pl.mt = 128;
     pl.nt = 256;
-    // prefill-sized gate/up: 256 x 256 tiles on 4 x 2 waves, a third fewer
-    // stage bytes per flop again (32768 rows at the 1.5B shape: 2631 -> 2074 us)
-    if (epi == EPI_SILU && M > 1024 && ceil_div(M, 256) * ceil_div(n_out, 128) >= 256) {
+    // prefill-sized projections other than QKV: 256 x 256 tiles on 4 x 2
+    // waves, a third fewer stage bytes per flop again (32768 rows at the 1.5B
+    // shape: gate/up 2631 -> 2074 us, down 1107 -> 907 us, O 216 -> 174 us;
+    // QKV with RoPE was slower, 450 -> 571 us)
+    if (epi != EPI_ROPE && M > 1024 && ceil_div(M, 256) * ceil_div(n_out, pair ? 128 : 256) >= 256) {
       pl.cfg = GEMM_256x256;
       pl.mt = 256;
     }
