@@ -196,6 +196,9 @@ def test_prefill_fp8_cache(lib):
     (inp.Shape(512, 4, 4, 128, 1024, 500, 1), [50, 3], [16, 7], 5011),
     # long prompts: up to 63 pages per chunk, many rescaled page groups
     (inp.Shape(512, 12, 2, 128, 1024, 500, 1), [700, 260], [300, 0], 5012),
+    # 1100 new tokens with FFN 16040: the gate/up projection on 256 x 256 tiles,
+    # partial in both the last row tile and the last column tile
+    (inp.Shape(256, 4, 2, 64, 16040, 500, 1), [600, 500], [0, 40], 5013),
 ])
 def test_prefill_group_sizes_and_long_prompts(lib, shape, new_lens, prior_lens, seed):
     case = prefill_case(shape, new_lens, prior_lens, seed)
