@@ -130,7 +130,7 @@ struct LinArgs {
 };
 
 enum { GEMM_32x64 = 0, GEMM_64x128 = 1, GEMM_128x128 = 2, GEMM_128x256 = 3, GEMM_128x128_S3 = 4, GEMM_128x160 = 5,
-       GEMM_64x64 = 6, GEMM_256x256 = 7 };
+       GEMM_64x64 = 6, GEMM_256x256 = 7, GEMM_32x96 = 8, GEMM_32x160 = 9, GEMM_64x96 = 10, GEMM_64x160 = 11 };
 
 // Tiles of N-tile columns [0, nt_full) are computed whole; those of columns
 // [nt_full, n_nt) are cut into `splits` K ranges of kc_per_split stages.

@@ -42,7 +42,7 @@ def _layer_shape(shape):
 # batch 100: a partial 128-row tile in the gate/up plans (3-stage 128 x 128 tiles at the 1.5B
 # shape, 128 x 160 tiles at the 7B shape, whose last column tile is partial too) and partial
 # 64-row tiles in the O/down plans; 7B at batch 256: 3-stage 128 x 128 tiles for the down projection
-@pytest.mark.parametrize("name,batch", [("1.5B", 1), ("1.5B", 64), ("1.5B", 100), ("1.5B", 128), ("1.5B", 256),
+@pytest.mark.parametrize("name,batch", [("1.5B", 1), ("1.5B", 32), ("1.5B", 64), ("1.5B", 100), ("1.5B", 128), ("1.5B", 256),
                                         ("7B", 1), ("7B", 32), ("7B", 64), ("7B", 100), ("7B", 128), ("7B", 256)])
 def test_decode_layer_full_shape(lib, name, batch):
     shape = _layer_shape(inp.QWEN15 if name == "1.5B" else inp.QWEN7)
