@@ -39,13 +39,18 @@ __device__ __forceinline__ int v_tile_off(bool fp8, int t, int d) {
 
 // Stores x (rounded to f16, the precision of the new token's k and v) at
 // element `off` of a pool: as f16, or as the E4M3 code of f16(x) / scale with
-// the quotient formed in float32.
+// the quotient formed in float32.  One token fills only 1-2 bytes of every 32
+// bytes of a K or V tile, so the store writes through L2 (agent scope):
+// leaving such lines partly dirty in L2 until the end of the kernel cost the
+// QKV projection at batch 256 about 1 us more per layer.
 __device__ __forceinline__ void kv_store(void* pool, size_t off, bool fp8, float scale, float x) {
   const _Float16 h = (_Float16)x;
   if (fp8)
-    static_cast<uint8_t*>(pool)[off] = e4m3_encode(__fdiv_rn((float)h, scale));
+    __hip_atomic_store(static_cast<uint8_t*>(pool) + off, e4m3_encode(__fdiv_rn((float)h, scale)), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   else
-    static_cast<_Float16*>(pool)[off] = h;
+    __hip_atomic_store(static_cast<unsigned short*>(pool) + off, __builtin_bit_cast(unsigned short, h),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace pkv
