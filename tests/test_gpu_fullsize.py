@@ -115,7 +115,7 @@ class FullStep:
                                   self.lens[rows], acc=np.float32)
 
 
-@pytest.mark.parametrize("batch", [64, 256])
+@pytest.mark.parametrize("batch", [64, 200, 256])
 def test_lm_head_full_vocabulary(lib, batch):
     rig = FullStep(lib, inp.QWEN15, 1, batch, 1, 40, seed=5100 + batch)
     logits, hidden, tok = rig.run_graph()
