@@ -18,6 +18,8 @@ on the host cores on a bounded sample.
     python bench.py [--gpus 1] [--steps 32] [--warmup 5]
 """
 import argparse
+import contextlib
+import gc
 import hashlib
 import json
 import math
@@ -26,6 +28,19 @@ import sys
 import time
 
 import numpy as np
+
+
+@contextlib.contextmanager
+def no_gc():
+    """A timed region with Python's cyclic garbage collector off (collected
+    just before): steps are enqueued from Python, and a collection pause
+    there can leave the GPU idle inside the timed region."""
+    gc.collect()
+    gc.disable()
+    try:
+        yield
+    finally:
+        gc.enable()
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -125,13 +140,14 @@ class DecodeRun:
         call()
         ms = None
         if repeats:
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(repeats):
-                call()
-            e1.record()
-            torch.cuda.synchronize()
+            with no_gc():
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(repeats):
+                    call()
+                e1.record()
+                torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / repeats
         pkv.argmax(self.logits, self.tok_d)
         torch.cuda.synchronize()
@@ -153,15 +169,16 @@ def time_decode(pkv, torch, model, shape, batch, prompt_len, warmup, steps, seed
         prefill_ms = None
     for _ in range(warmup):
         run.step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(steps):
-        run.step()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with no_gc():
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            run.step()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1)
     ctx_mean = float(run.lens.mean()) - steps / 2.0
     run.close()
@@ -236,14 +253,15 @@ def time_attention(pkv, torch, w, n_pools, rounds, seed):
 
     for layer in range(n_pools):
         call(layer)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(rounds):
-        for layer in range(n_pools):
-            call(layer)
-    e1.record()
-    torch.cuda.synchronize()
+    with no_gc():
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(rounds):
+            for layer in range(n_pools):
+                call(layer)
+        e1.record()
+        torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / (rounds * n_pools)
     elt = 1 if fp8 else 2
     kv_bytes = int(lens.sum()) * w.n_kv_heads * w.head_dim * 2 * elt
@@ -274,13 +292,14 @@ def time_sampling(pkv, torch, inp, batch, vocab, rounds, seed, mode):
     tok = torch.empty(batch, dtype=torch.int32, device="cuda")
     for _ in range(3):
         pkv.sample(*args, tok)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(rounds):
-        pkv.sample(*args, tok)
-    e1.record()
-    torch.cuda.synchronize()
+    with no_gc():
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(rounds):
+            pkv.sample(*args, tok)
+        e1.record()
+        torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / rounds * 1e3
     return {"batch": batch, "vocab": vocab, "mode": mode, "us_per_call": us,
             "logit_bytes": batch * vocab * 2}
