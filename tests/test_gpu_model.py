@@ -137,13 +137,18 @@ def test_decode_step_parity_and_greedy(lib, batch):
     assert agree / total >= 0.99
 
 
-def test_argmax_kernel(lib):
+@pytest.mark.parametrize("vocab", [151936, 152064, 163840, 163848, 1000, 999])
+def test_argmax_kernel(lib, vocab):
+    # vocab 163840 fills exactly one round of loads per thread, 163848 needs a
+    # second round for one vector, 999 takes the unaligned (scalar) path
     rng = np.random.default_rng(3)
-    lg = rng.standard_normal((6, 151936)).astype(np.float16)
-    lg[1, [5, 77, 150000]] = 30.0          # ties: lowest index wins
+    lg = rng.standard_normal((7, vocab)).astype(np.float16)
+    lg[1, [5, 77, vocab - 3]] = 30.0       # ties: lowest index wins
     lg[2, :] = -1.0
     lg[3, 100] = np.nan
-    out = torch.empty(6, dtype=torch.int32, device="cuda")
+    lg[4, vocab - 1] = 40.0                # the row's very last logit
+    lg[5, [vocab - 1, vocab - 9]] = 35.0   # a tie inside the last vector and the one before
+    out = torch.empty(7, dtype=torch.int32, device="cuda")
     lib.argmax(dev(lg), out)
     torch.cuda.synchronize()
     assert out.cpu().numpy().tolist() == oracle.greedy_argmax(np.nan_to_num(lg, nan=-np.inf)).tolist()
