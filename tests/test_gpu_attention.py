@@ -39,6 +39,8 @@ def oracle_attention(case):
     (5, 28, 4, 128, 1, 300, 4),        # 7B head shape, G = 7
     (3, 16, 1, 64, 1, 2100, 5),        # G = 16, one KV head
     (6, 8, 8, 128, 1, 90, 6),          # MHA (G = 1)
+    (9, 12, 2, 128, 900, 2000, 7),     # 18 pairs x 2 partitions dealt to the XCDs, last round partly empty
+    (9, 12, 2, 128, 1, 4000, 9),       # the same with up to 4 partitions per pair
 ])
 def test_attention_parity_f16(lib, b, hq, hkv, d, lo, hi, seed):
     case = inp.attention_case(b, hq, hkv, d, lo, hi, seed)
