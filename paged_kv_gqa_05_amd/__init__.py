@@ -42,6 +42,8 @@ def lib():
 
 
 def _destroy(fn_name, obj):
+    # also called from __del__ at interpreter exit, when the module's globals
+    # may already be None (callers bind this function as a default argument)
     h = getattr(obj, "handle", None)
     if h and _lib is not None:
         getattr(_lib, fn_name)(h)
@@ -89,7 +91,7 @@ class KVCache:
             return kt.view(nb, hkv, d // c, BLOCK_SIZE, c), vt.view(nb, hkv, d // 64, 4, 16, 4, 4)
         return kt.view(nb, hkv, d // c, BLOCK_SIZE, c), vt.view(nb, hkv, d, BLOCK_SIZE)
 
-    def close(self):
+    def close(self, _destroy=_destroy):
         _destroy("pkv_kv_cache_destroy", self)
 
     __del__ = close
@@ -152,7 +154,7 @@ class Model:
                                      _p(weights["w_final_norm"]), _p(weights["w_lm_head"]), C.byref(h)))
         self.handle = h
 
-    def close(self):
+    def close(self, _destroy=_destroy):
         _destroy("pkv_model_destroy", self)
 
     __del__ = close
@@ -233,7 +235,7 @@ class Graph:
     def replay(self, stream=None):
         _check(_lib.pkv_graph_replay(self.handle, _stream(stream)))
 
-    def close(self):
+    def close(self, _destroy=_destroy):
         _destroy("pkv_graph_destroy", self)
 
     __del__ = close
@@ -277,7 +279,7 @@ class GraphSet:
         _check(_lib.pkv_graph_set_replay(self.handle, int(batch), _stream(stream), C.byref(bk)))
         return bk.value
 
-    def close(self):
+    def close(self, _destroy=_destroy):
         _destroy("pkv_graph_set_destroy", self)
 
     __del__ = close
@@ -303,7 +305,7 @@ class BlockAllocator:
     def free_blocks(self):
         return _lib.pkv_alloc_free_blocks(self.handle)
 
-    def close(self):
+    def close(self, _destroy=_destroy):
         _destroy("pkv_alloc_destroy", self)
 
     __del__ = close

@@ -150,3 +150,19 @@ def test_sample_and_prefill_argument_errors():
     assert lib.pkv_prefill_workspace_bytes(None, None, 4, 1, 16, C.byref(n)) == 1
     assert lib.pkv_prefill(None, None, None, None, None, 1, 4, None, 1, 16, None, None, 0, None) == 1
     assert b"model / cache is NULL" in lib.pkv_last_error()
+
+
+def test_handle_alive_at_interpreter_exit_is_released_quietly():
+    """An object still holding a native handle when the interpreter exits is
+    destroyed by __del__ while the module's globals are being cleared; that
+    must not raise (Python reports such errors as 'Exception ignored')."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import paged_kv_gqa_05_amd as pkv\n"
+            "a = pkv.BlockAllocator(64, seed=1)\n"
+            "print('ok', a.free_blocks)\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "ok 64"
+    assert "Exception ignored" not in r.stderr and "Traceback" not in r.stderr, r.stderr
