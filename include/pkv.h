@@ -132,7 +132,11 @@ pkv_status pkv_kv_append(pkv_cache* cache, int layer, const void* k, const void*
 /* Scratch bytes paged_attn_decode needs for this shape (host only).  The
  * workspace must be zero-filled once before its first use (e.g. hipMemset);
  * every call leaves it in a state valid for the next call, of any shape that
- * fits it. */
+ * fits it.  Layout of a workspace of W bytes: the per-(row, KV head) arrival
+ * counters sit in a leading region whose size depends on W only (W / 64 in
+ * whole 256-byte units, at least 256 bytes), the partial results after it; a
+ * call fits W when its batch x Hkv counters fit that region and its partials
+ * fit behind it, which every W >= the returned size guarantees. */
 pkv_status pkv_attn_workspace_bytes(const pkv_cache* cache, int batch, int num_q_heads,
                                     int max_context, size_t* bytes);
 

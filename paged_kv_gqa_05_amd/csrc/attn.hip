@@ -471,9 +471,10 @@ hipError_t launch_paged_attention(const AttnArgs& a, const AttnPlan& plan, hipSt
   sp.v_scale = a.fp8 ? a.v_scale : 1.0f;
   const size_t ml = align_up((size_t)a.batch * a.hq * plan.n_parts_max * sizeof(float2), 256);
   char* ws = static_cast<char*>(a.ws);
+  const size_t cr = a.counter_region ? a.counter_region : plan.counter_bytes;
   sp.counters = reinterpret_cast<int*>(ws);
-  sp.ws_ml = reinterpret_cast<float2*>(ws + plan.counter_bytes);
-  sp.ws_o = reinterpret_cast<float*>(ws + plan.counter_bytes + ml);
+  sp.ws_ml = reinterpret_cast<float2*>(ws + cr);
+  sp.ws_o = reinterpret_cast<float*>(ws + cr + ml);
   if (a.head_dim == 128) return a.fp8 ? launch_impl<128, true>(sp, plan, s) : launch_impl<128, false>(sp, plan, s);
   return a.fp8 ? launch_impl<64, true>(sp, plan, s) : launch_impl<64, false>(sp, plan, s);
 }

@@ -142,7 +142,7 @@ pkv_status pkv_attn_workspace_bytes(const pkv_cache* cache, int batch, int num_q
   const int hkv = cache->desc.num_kv_heads;
   if (num_q_heads < hkv || num_q_heads % hkv) return fail(PKV_E_ARG, "num_q_heads must be a multiple of num_kv_heads");
   if (num_q_heads / hkv > kMaxGroup) return fail(PKV_E_UNSUPPORTED, "more than 16 query heads per KV head");
-  *bytes = attn_plan(batch, num_q_heads, hkv, cache->desc.head_dim, cache->elt(), max_context).ws_bytes;
+  *bytes = attn_standalone_bytes(attn_plan(batch, num_q_heads, hkv, cache->desc.head_dim, cache->elt(), max_context));
   return PKV_OK;
 }
 
@@ -157,11 +157,12 @@ pkv_status pkv_paged_attn_decode(const pkv_cache* cache, int layer, const void* 
   size_t need = 0;
   st = pkv_attn_workspace_bytes(cache, batch, num_q_heads, max_context, &need);
   if (st != PKV_OK) return st;
-  if (!workspace || workspace_bytes < need)
+  const pkv_cache_desc& d = cache->desc;
+  const AttnPlan plan = attn_plan(batch, num_q_heads, d.num_kv_heads, d.head_dim, cache->elt(), max_context);
+  if (!workspace || !attn_ws_fits(plan, workspace_bytes))
     return fail(PKV_E_ARG, "workspace too small: need " + std::to_string(need) + " bytes");
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(PKV_E_ARG, "workspace must be 256-byte aligned");
   if (!(scale > 0.f)) return fail(PKV_E_ARG, "scale must be positive");
-  const pkv_cache_desc& d = cache->desc;
   AttnArgs a{};
   a.k_pool = cache->k_pool(layer);
   a.v_pool = cache->v_pool(layer);
@@ -180,7 +181,7 @@ pkv_status pkv_paged_attn_decode(const pkv_cache* cache, int layer, const void* 
   a.k_scale = a.fp8 ? cache->k_scales[layer] : 1.f;
   a.v_scale = a.fp8 ? cache->v_scales[layer] : 1.f;
   a.ws = workspace;
-  const AttnPlan plan = attn_plan(batch, num_q_heads, d.num_kv_heads, d.head_dim, cache->elt(), max_context);
+  a.counter_region = attn_counter_region(workspace_bytes);
   PKV_HIP(launch_paged_attention(a, plan, static_cast<hipStream_t>(stream)));
   return PKV_OK;
 }

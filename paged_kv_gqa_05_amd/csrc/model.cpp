@@ -95,6 +95,16 @@ StepBuffers carve(const pkv_model* m, int batch, const AttnPlan& plan, void* bas
 
 int cache_elt(const pkv_cache_desc& cd) { return cd.dtype == PKV_KV_FP8_E4M3 ? 1 : 2; }
 
+// A prefill's attention is the causal multi-token kernel, which needs none of
+// the decode attention's counters or partials: its step buffers are carved
+// with an empty attention workspace.
+AttnPlan prefill_attn_plan() {
+  AttnPlan p{};
+  p.counter_bytes = 0;
+  p.ws_bytes = 0;
+  return p;
+}
+
 // A prefill runs the decode layers over its n_tokens new tokens as rows of
 // their own; after the step buffers for that many rows come the per-token
 // rows (context length, block-table copy), the last row of every sequence,
@@ -363,9 +373,7 @@ pkv_status pkv_prefill_workspace_bytes(const pkv_model* m, const pkv_cache* cach
   if (!m || !cache || !bytes) return fail(PKV_E_ARG, "NULL argument");
   if (n_tokens < 1 || n_seqs < 1 || max_context < 1)
     return fail(PKV_E_ARG, "n_tokens, n_seqs and max_context must be >= 1");
-  const AttnPlan plan =
-      attn_plan(n_tokens, m->d.num_q_heads, m->d.num_kv_heads, m->d.head_dim, cache_elt(cache->desc), max_context);
-  *bytes = carve_prefill(m, n_tokens, n_seqs, max_context, plan, nullptr).total;
+  *bytes = carve_prefill(m, n_tokens, n_seqs, max_context, prefill_attn_plan(), nullptr).total;
   return PKV_OK;
 }
 
@@ -384,8 +392,7 @@ pkv_status pkv_prefill(const pkv_model* m, pkv_cache* cache, const int32_t* toke
     return fail(PKV_E_ARG, "max_context must be in [1, max_positions]");
   if (max_context > kAttnMaxContext) return fail(PKV_E_UNSUPPORTED, "max_context above 262144");
   if (bt_stride < ceil_div(max_context, kBlock)) return fail(PKV_E_ARG, "bt_stride < ceil(max_context / 16)");
-  const AttnPlan plan =
-      attn_plan(n_tokens, m->d.num_q_heads, m->d.num_kv_heads, m->d.head_dim, cache_elt(cd), max_context);
+  const AttnPlan plan = prefill_attn_plan();
   const size_t need = carve_prefill(m, n_tokens, n_seqs, max_context, plan, nullptr).total;
   if (!ws || ws_bytes < need) return fail(PKV_E_ARG, "workspace too small: need " + std::to_string(need) + " bytes");
   if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(PKV_E_ARG, "workspace must be 256-byte aligned");

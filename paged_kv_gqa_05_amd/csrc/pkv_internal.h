@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
+#include <algorithm>
 #include <cstdint>
 #include <string>
 #include <vector>
@@ -55,6 +56,31 @@ struct AttnPlan {
 };
 AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int max_context);
 
+// A standalone attention workspace (pkv_paged_attn_decode) of W bytes keeps
+// its arrival counters in a leading region whose size depends on W alone
+// (1/64 of it in whole 256-byte units, at least 256 bytes); the partial
+// results follow that region.  Every call that fits W therefore uses the same
+// counter region, and the partials of one call never land on the counters of
+// a later call of another shape.  A call fits when its counters fit the region
+// and its partials fit behind it.
+inline size_t attn_counter_region(size_t ws_bytes) {
+  const size_t r = ws_bytes / 64 / 256 * 256;
+  return r < 256 ? 256 : r;
+}
+inline size_t attn_partial_bytes(const AttnPlan& p) { return p.ws_bytes - p.counter_bytes; }
+inline bool attn_ws_fits(const AttnPlan& p, size_t ws_bytes) {
+  const size_t r = attn_counter_region(ws_bytes);
+  return r >= p.counter_bytes && ws_bytes >= r + attn_partial_bytes(p);
+}
+// Smallest standalone workspace that fits the plan.
+inline size_t attn_standalone_bytes(const AttnPlan& p) {
+  size_t w = align_up(64 * p.counter_bytes, 256);
+  const size_t part = attn_partial_bytes(p);
+  if (part) w = std::max(w, align_up(part + part / 63 + 512, 256));
+  while (!attn_ws_fits(p, w)) w += 256;
+  return w;
+}
+
 struct AttnArgs {
   const void* k_pool;
   const void* v_pool;
@@ -68,7 +94,8 @@ struct AttnArgs {
   bool fp8;
   float scale;        // softmax scale
   float k_scale, v_scale;
-  void* ws;           // partials (layout of attn_plan)
+  void* ws;           // counters, then the partials (layout of attn_plan)
+  size_t counter_region;  // bytes before the partials: 0 = the plan's counter_bytes
 };
 hipError_t launch_paged_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
 

@@ -156,8 +156,32 @@ def test_workspace_reused_across_calls(lib):
         out, _ = run_attention(lib, case, ws=ws)
         ref, _ = oracle_attention(case)
         assert_parity(out, ref, "workspace reuse")
-        n_counter_bytes = case.q.shape[0] * 2 * 4
-        assert not ws[:n_counter_bytes].any().item()
+        assert not ws[:_counter_region(ws.numel())].any().item()
+
+
+def _counter_region(ws_bytes):
+    """Leading bytes of a standalone attention workspace that hold the arrival
+    counters (include/pkv.h: W / 64 in whole 256-byte units, at least 256)."""
+    return max(256, ws_bytes // 64 // 256 * 256)
+
+
+def test_workspace_small_batch_then_large_batch(lib):
+    """A batch-3 call whose rows span several partitions writes partial results,
+    then a batch-64 call (the attn15 workload) on the same workspace: the large
+    call's counters must not read the small call's partials.  Every call
+    matches the oracle and leaves the whole counter region zero."""
+    small = inp.attention_case(3, 12, 2, 128, 900, 1500, seed=21)
+    big = inp.workload_case(inp.ATTN15)
+    cache = load_case_into_cache(lib, big)
+    need = max(lib.attn_workspace_bytes(cache, 3, 12, small.max_context),
+               lib.attn_workspace_bytes(cache, 64, 12, big.max_context))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    region = _counter_region(need)
+    for case in (small, big, small, big):
+        out, _ = run_attention(lib, case, ws=ws)
+        ref, _ = oracle_attention(case)
+        assert_parity(out, ref, f"batch {case.q.shape[0]} after reuse")
+        assert not ws[:region].any().item()
 
 
 def test_inactive_rows(lib):

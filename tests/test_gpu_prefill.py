@@ -147,6 +147,23 @@ def test_prefill_host_errors(lib):
         lib.prefill(model, cache, args[0], args[1][:1], args[2], dev(case["bt"]), 4, logits, small)
 
 
+def test_prefill_workspace_bytes_long_prompt(lib):
+    """The prefill workspace holds no decode-attention partials: for one
+    32768-token prompt at the 7B layer shape it stays within the per-token
+    buffers (hidden, q, o, FFN activation, block-table copies: ~2.3 GB), where
+    sizing the decode partials for 32768 rows needed ~30 GB more."""
+    shape = inp.QWEN7
+    one = torch.zeros(16, dtype=torch.float16, device="cuda")   # never read: only sizes are asked for
+    lw = {k: one for k in ("w_in", "w_qkv", "b_qkv", "w_o", "w_post", "w_gate_up", "w_down")}
+    w = {"embed": one, "w_final_norm": one, "w_lm_head": one, "layers": [lw]}
+    model = lib.Model(inp.Shape(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn,
+                                shape.vocab, 1), w, max_positions=32768)
+    cache = lib.KVCache(1, 16, shape.n_kv_heads, shape.head_dim)
+    n = lib.prefill_workspace_bytes(model, cache, 32768, 1, 32768)
+    per_token = 2 * (shape.hidden + 2 * shape.n_q_heads * shape.head_dim + shape.ffn) + 4 * (1 + 32768 // 16)
+    assert 32768 * per_token <= n < 32768 * per_token + (1 << 30), n
+
+
 def test_prefill_full_shape_sampled_sequences(lib):
     """Qwen2.5-1.5B layer shape (one layer, a 16-token vocabulary: the layer
     does not depend on it), 256 prompts of 128 tokens in one call (32768 new
