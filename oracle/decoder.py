@@ -224,10 +224,12 @@ def kv_append(k_pool, v_pool, k_new, v_new, block_tables, ctx_lens, k_scale=None
 # ---------------------------------------------------------------- one layer
 
 def _linear(x, w, acc, bias=None):
-    """y = x W^T (+ b) with W stored [out, in]; x [..., in]."""
-    y = np.asarray(x, dtype=acc) @ np.asarray(w).astype(acc).T
+    """y = x W^T (+ b) with W stored [out, in]; x [..., in].  W may be given
+    as f16 or already widened to ``acc`` (exact: every f16 is an fp32 value);
+    a widened W is used without a copy."""
+    y = np.asarray(x, dtype=acc) @ np.asarray(w, dtype=acc).T
     if bias is not None:
-        y = y + np.asarray(bias).astype(acc)
+        y = y + np.asarray(bias, dtype=acc)
     return y
 
 
