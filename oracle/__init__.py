@@ -35,7 +35,7 @@ logits of a random-weight model have no external pin ("parity unpinned by the
 pages": the pages publish no logits or tokens).
 """
 from .fp8 import e4m3_decode, e4m3_encode, e4m3_quantize, e4m3_table
-from .sampling import candidates, sample, sample_row
+from .sampling import apply_penalties, candidates, draw, exp_f32, sample, sample_penalized, sample_row, weight_fixed
 from .decoder import (
     ModelConfig,
     rmsnorm,
@@ -53,7 +53,8 @@ from .decoder import (
 )
 
 __all__ = [
-    "e4m3_decode", "e4m3_encode", "e4m3_quantize", "e4m3_table", "candidates", "sample", "sample_row", "ModelConfig", "rmsnorm", "silu", "rope",
+    "e4m3_decode", "e4m3_encode", "e4m3_quantize", "e4m3_table", "apply_penalties", "candidates", "draw",
+    "exp_f32", "sample", "sample_penalized", "sample_row", "weight_fixed", "ModelConfig", "rmsnorm", "silu", "rope",
     "rope_angles", "paged_attention", "paged_attention_batch", "kv_append",
     "decode_layer", "decode_step", "greedy_argmax", "causal_forward", "prefill",
 ]

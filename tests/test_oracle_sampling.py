@@ -1,13 +1,17 @@
 """Pins for the oracle's sampler (oracle/sampling.py): greedy at temperature
 0, closed-form probabilities on a 3-token example (the logits of the rvLLM
 post's usage example), the inverse-CDF draw against torch's softmax, top-k /
-top-p kept sets against brute-force enumeration, and ties at both thresholds
-kept (the reading of zingnex.cn, section 支持的参数)."""
+top-p kept sets against brute-force enumeration, ties at both thresholds kept
+(the reading of zingnex.cn, section 支持的参数), the float32 exponential and
+the 2^-40 fixed-point weights against numpy's double-precision exp, and the
+repetition / frequency / presence penalties (zingnex.cn, section CPU操作优化)
+in closed form."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import candidates, greedy_argmax, sample, sample_row
+from oracle.sampling import apply_penalties, draw, exp_f32, sample_penalized, weight_fixed
 
 
 def test_temperature_zero_is_greedy():
@@ -66,8 +70,10 @@ def test_top_p_is_the_smallest_descending_prefix():
             n += 1
         ids, w = candidates(lg, 1.0, -1, top_p)
         assert sorted(order[:n].tolist()) == ids.tolist(), top_p
+        w = w.astype(np.float64)
         q = w / w.sum()                                  # renormalised kept probabilities
-        assert np.allclose(q, p[ids] / p[ids].sum(), rtol=1e-12, atol=0)
+        # fixed-point weights of a float32 exponential: a few float32 roundings
+        assert np.allclose(q, p[ids] / p[ids].sum(), rtol=2e-6, atol=0)
 
 
 def test_top_p_keeps_ties_at_the_threshold():
@@ -96,3 +102,76 @@ def test_top_p_matches_enumeration_with_many_ties():
                 break
         want = np.nonzero(w >= t)[0]
         assert candidates(lg, 0.9, -1, top_p)[0].tolist() == want.tolist(), top_p
+
+
+def test_exp_f32_against_double_exp():
+    """The float32 exponential within 3 float32 roundings of numpy's double exp
+    on every float32 value in [-30, 0] sampled densely, exact at 0, 0 below
+    -30 and non-decreasing."""
+    y = np.concatenate([np.linspace(-30, 0, 1_000_001, dtype=np.float32),
+                        -np.logspace(-30, 1, 20001).astype(np.float32), np.float32([0.0, -0.0])])
+    y.sort()
+    e = exp_f32(y)
+    ref = np.exp(y.astype(np.float64))
+    assert np.max(np.abs(e - ref) / ref) <= 3 * 2.0 ** -24
+    assert np.all(np.diff(e) >= 0)
+    assert exp_f32(np.float32(0.0)) == 1.0
+    assert np.all(exp_f32(np.float32([-30.5, -100.0, -np.inf])) == 0.0)
+
+
+def test_weight_fixed_closed_forms():
+    # the maximum weighs exactly 2^40; one step of ln 2 below it, 2^39 within rounding
+    assert int(weight_fixed(np.float16(3.0), np.float16(3.0), 0.7)) == 1 << 40
+    assert int(weight_fixed(np.float16(3.0), np.float16(3.0), 1e-40)) == 1 << 40   # 1/T overflows
+    w = int(weight_fixed(np.float16(-np.log(2.0)), np.float16(0.0), 1.0))
+    assert abs(w - (1 << 39)) <= (1 << 39) * 4e-4        # the f16 rounding of -ln 2
+    x = np.arange(-40.0, 0.25, 0.25).astype(np.float16)
+    got = weight_fixed(x, np.float16(0.0), 1.3).astype(np.float64)
+    y = x.astype(np.float64) / np.float64(np.float32(1.3))
+    want = np.floor(np.exp(y) * 2.0 ** 40)
+    # the exponential's roundings plus the float32 rounding of y (relative |y| 2^-24 in e^y)
+    assert np.all(np.abs(got - want) <= np.maximum(want * (4 + 2 * np.abs(y)) * 2.0 ** -24, 1.0))
+    assert np.all(got[y < -30.01] == 0)
+
+
+def test_draw_is_an_integer_inverse_cdf():
+    ids = np.array([3, 5, 9])
+    w = np.array([1 << 38, 1 << 39, 1 << 40], np.uint64)   # masses 1/7, 2/7, 4/7
+    assert draw(ids, w, 0.0) == 3 and draw(ids, w, np.nan) == 3 and draw(ids, w, -1.0) == 3
+    assert draw(ids, w, 1.0) == 9 and draw(ids, w, 0.9999999) == 9
+    # boundaries at 1/7 and 3/7 of the mass: u24 = floor(u 2^24) and t = floor(u24 Z / 2^24)
+    b1 = (1 << 24) // 7                                   # largest u24 with t < Z/7 ... or equal
+    for u24, tok in ((b1, 3), (b1 + 1, 5), (3 * (1 << 24) // 7, 5), (3 * (1 << 24) // 7 + 1, 9)):
+        z = 7 << 38
+        t = (u24 * z) >> 24
+        want = 3 if t < (1 << 38) else (5 if t < 3 << 38 else 9)
+        assert want == tok, (u24, t)
+        assert draw(ids, w, u24 / float(1 << 24)) == tok
+
+
+def test_penalties_closed_forms():
+    x = np.array([2.0, -2.0, 1.0, -1.0, 0.0, 3.0, np.nan, -np.inf, np.inf], np.float16)
+    c = np.array([1, 1, 0, 0, 2, 3, 1, 1, 1])
+    got = apply_penalties(x, c, 2.0, 0.5, 0.25)
+    # seen: positive / r, negative * r, then - f c - p; unseen tokens unchanged bit for bit
+    want = np.array([2 / 2 - 0.5 - 0.25, -2 * 2 - 0.5 - 0.25, 1.0, -1.0, 0.0 - 1.0 - 0.25,
+                     3 / 2 - 1.5 - 0.25, np.nan, -np.inf, np.inf], np.float16)
+    assert np.array_equal(got.view(np.uint16)[:6], want.view(np.uint16)[:6])
+    assert np.isnan(got[6]) and got[7] == -np.inf and got[8] == np.inf
+    assert np.array_equal(apply_penalties(x, np.zeros(9, int), 1.3, 0.7, 0.1).view(np.uint16), x.view(np.uint16))
+    # neutral parameters leave every seen logit unchanged too
+    assert np.array_equal(apply_penalties(x[:6], c[:6], 1.0, 0.0, 0.0).view(np.uint16), x[:6].view(np.uint16))
+    # rounding to f16 after the float32 arithmetic: 1/3 of a logit of 1
+    assert apply_penalties(np.float16([1.0]), [1], 3.0, 0.0, 0.0)[0] == np.float16(np.float32(1.0) / np.float32(3.0))
+
+
+def test_penalised_greedy_and_counts():
+    lg = np.zeros((2, 6), np.float16)
+    lg[:, 4], lg[:, 2] = 5.0, 4.5
+    counts = np.zeros((2, 6), np.int32)
+    counts[0, 4] = 1                                      # row 0 already produced token 4
+    tok, pen, new = sample_penalized(lg, counts, [1.0, 1.0], [0.0, 0.0], [1.0, 1.0], [0.0, 0.0], [-1, -1],
+                                     [1.0, 1.0], [0.5, 0.5])
+    assert tok.tolist() == [2, 4]                         # presence 1 pushes token 4 below token 2 in row 0
+    assert pen[0, 4] == np.float16(4.0) and pen[1, 4] == np.float16(5.0)
+    assert new[0, 4] == 1 and new[0, 2] == 1 and new[1, 4] == 1 and new.sum() == 3
