@@ -101,18 +101,26 @@ typedef struct {
   int32_t dtype;        /* pkv_kv_dtype */
 } pkv_cache_desc;
 
-/* Bytes of device memory a cache with this description needs (host only). */
+/* Bytes of device memory a cache with this description needs (host only).
+ * The cache is the paged KV store of the rvLLM post (section
+ * "PagedAttention과 FlashAttention-3": keys and values of past tokens kept in
+ * a block-table cache) and of the aitrends.kr glossary (용어 해설, the
+ * PagedAttention entry: the KV cache split into fixed-size pages); here a page
+ * is a block of 16 tokens per KV head, laid out as above. */
 pkv_status pkv_cache_bytes(const pkv_cache_desc* desc, size_t* bytes);
 
 /* Wrap caller-owned device memory (>= pkv_cache_bytes, 256-byte aligned) as a
- * paged KV cache.  For fp8 caches k_scales / v_scales (host, [num_layers]) are
+ * paged KV cache (the pages above; rvLLM post, section
+ * "PagedAttention과 FlashAttention-3", FP8 E4M3 as the optional cache type).  For fp8 caches k_scales / v_scales (host, [num_layers]) are
  * the per-layer, per-tensor f32 scales (stored value = code value * scale);
  * they must be NULL for f16 caches.  The memory is not initialised. */
 pkv_status pkv_kv_cache_create(const pkv_cache_desc* desc, void* dev_mem, size_t bytes,
                                const float* k_scales, const float* v_scales, pkv_cache** out);
 void pkv_kv_cache_destroy(pkv_cache* cache);
 
-/* Device addresses of layer `layer`'s K and V pools (tile layouts above). */
+/* Device addresses of layer `layer`'s K and V pools (tile layouts above).
+ * PKV_E_ARG for a NULL argument or a layer outside [0, num_layers); the
+ * addresses point into the caller's memory (nothing is allocated). */
 pkv_status pkv_kv_cache_layer(const pkv_cache* cache, int layer, void** k_pool, void** v_pool);
 
 /* Append one token per row: k and v are f16 [batch][Hkv][D]; row b is stored
@@ -205,7 +213,13 @@ pkv_status pkv_model_create(const pkv_model_desc* desc, const void* embed,
                             const void* w_lm_head, pkv_model** out);
 void pkv_model_destroy(pkv_model* model);
 
-/* Scratch bytes decode_layer / decode_step / graph_capture need (host only). */
+/* Scratch bytes decode_layer / decode_step / graph_capture need (host only):
+ * the per-step buffers of the fused layer (rvLLM post, section "퓨즈드 CUDA
+ * 커널": q, the attention output and the SiLU*mul activation), the split-K
+ * partial tiles of the projections and the attention partials.  Contents
+ * need no initialisation (the step zeroes its arrival counters in its first
+ * kernel, the memset removal of the post's optimisation history).
+ * PKV_E_ARG for NULL arguments or sizes below 1. */
 pkv_status pkv_step_workspace_bytes(const pkv_model* model, const pkv_cache* cache, int batch,
                                     int max_context, size_t* bytes);
 
@@ -271,21 +285,46 @@ pkv_status pkv_argmax(const void* logits, int batch, int vocab, int32_t* tokens,
  * 支持的参数: temperature (0 = greedy), top_p, top_k (-1 = disabled)).  All
  * per-row arrays are device memory, [batch]: temperature f32, top_k int32,
  * top_p f32, uniform f32 in [0, 1) (the caller's random numbers; values
- * outside are clamped).  For row b with T = temperature[b]:
+ * outside, and NaN, are clamped into [0, 1 - 2^-24]).  For row b with
+ * T = temperature[b] and m its largest finite logit:
  *   T <= 0 (or NaN): the greedy token, as pkv_argmax;
- *   z = logit / T; top_k > 0 keeps every token with z at or above the k-th
- *   largest z (ties at the boundary kept); w = exp(z - max z);
- *   top_p < 1 keeps every token with w at or above tau, the largest weight
- *   whose kept mass reaches top_p * sum(w) (ties kept; top_p <= 0 keeps the
- *   largest weight and its ties);
+ *   every finite logit x weighs W(x) = floor(2^40 E((x - m) * (1/T))), where
+ *   1/T and the product are float32 and E is this float32 exponential, each
+ *   operation rounded on its own: n = floor(y * log2(e) + 0.5),
+ *   r = (y - n * 0.693359375) - n * (-2.12194440e-4), e^r by the degree-7
+ *   Taylor polynomial 1 + r(1 + r(1/2 + r(1/6 + ... + r/5040))) in Horner
+ *   form, times 2^n; E = 0 below -30 (W(m) = 2^40);
+ *   top_k > 0 keeps every token whose logit is at or above the k-th largest
+ *   (ties at the boundary kept);
+ *   top_p < 1 keeps the tokens whose logit is at or above the largest value t
+ *   for which the kept tokens at or above t sum to at least
+ *   ceil(max(top_p, 0) * sum W) (in double; ties kept; top_p <= 0 keeps the
+ *   largest logit and its ties);
  *   the result is the first kept token, in index order, whose running sum of
- *   w exceeds uniform[b] * (kept mass).
- * Non-finite logits are never kept; a row with none finite gets 0.
- * context_lens (nullable): rows of length 0 get -1.  vocab <= 2^24.  Sums are float32; a draw within rounding of a boundary of the
- * cumulative mass may fall on either neighbour. */
+ *   W exceeds floor(u24 * Z / 2^24), Z the kept sum, u24 = floor(u * 2^24).
+ * Every sum is an exact 64-bit integer, so the token is a function of the
+ * inputs alone.  Non-finite logits are never kept; a row with none finite
+ * gets 0.  context_lens (nullable): rows of length 0 get -1.  vocab <= 2^24. */
 pkv_status pkv_sample(const void* logits, int batch, int vocab, const float* temperature, const int32_t* top_k,
                       const float* top_p, const float* uniform, int32_t* tokens, const int32_t* context_lens,
                       pkv_stream_t stream);
+
+/* pkv_sample after repetition, frequency and presence penalties (zingnex.cn
+ * article, section CPU操作优化: the three penalties applied together).
+ * counts: int32 [batch][vocab] (device, caller-owned, in/out), how many times
+ * each token was already sampled for the row (the caller zeroes a row when a
+ * sequence starts).  Per active row, for every token with c = counts > 0,
+ * in float32 with each operation rounded on its own:
+ *   x = x > 0 ? x / repetition : x * repetition;  x = (x - frequency * c) - presence
+ * and the result is written back into logits as f16 (logits are in/out; rows
+ * with repetition 1, frequency 0 and presence 0, and inactive rows, are left
+ * untouched).  Then the row is sampled as pkv_sample does, and counts of the
+ * sampled token is incremented (active rows only).  repetition, frequency,
+ * presence: f32 [batch]; repetition must be > 0 and finite. */
+pkv_status pkv_sample_penalized(void* logits, int batch, int vocab, const float* temperature, const int32_t* top_k,
+                                const float* top_p, const float* repetition, const float* frequency,
+                                const float* presence, const float* uniform, int32_t* counts, int32_t* tokens,
+                                const int32_t* context_lens, pkv_stream_t stream);
 
 /* ------------------------------------------------------------- graph replay */
 
@@ -329,7 +368,12 @@ void pkv_graph_set_destroy(pkv_graph_set* set);
 
 /* ----------------------------------------------------- host block allocator */
 
-/* Free list of num_blocks physical block ids.  seed 0 hands ids out in
+/* The block allocator of a paged cache (aitrends.kr glossary, 용어 해설,
+ * PagedAttention entry: the cache is split into fixed-size pages, so memory
+ * is handed out page by page and not reserved per sequence; rvLLM post,
+ * section "CUDA 그래프 리플레이": block tables are host metadata uploaded
+ * before each step).  Host memory only; no device call.
+ * Free list of num_blocks physical block ids.  seed 0 hands ids out in
  * ascending order; any other seed shuffles the free list once (deterministic
  * for a given seed), which tests use to scatter a sequence's blocks. */
 pkv_status pkv_alloc_create(int num_blocks, uint64_t seed, pkv_alloc** out);
@@ -345,7 +389,10 @@ void pkv_alloc_destroy(pkv_alloc* alloc);
 
 /* Check (host) metadata: every length in [0, max_context], every needed block
  * id in [0, num_blocks), no block used twice across rows, and
- * bt_stride >= ceil(max_context / 16).  PKV_E_ARG with a message otherwise. */
+ * bt_stride >= ceil(max_context / 16).  PKV_E_ARG with a message otherwise.
+ * These are the per-step block tables and context lengths of the rvLLM post
+ * (section "CUDA 그래프 리플레이"), which the device path trusts; this check is
+ * for callers and tests that hold host copies. */
 pkv_status pkv_validate_metadata(const int32_t* block_tables, int bt_stride,
                                  const int32_t* context_lens, int batch, int num_blocks,
                                  int max_context);

@@ -256,6 +256,26 @@ def sample(logits, temperature, top_k, top_p, uniform, tokens, context_lens=None
                            _p(uniform), _p(tokens), _p(context_lens), _stream(stream)))
 
 
+def sample_penalized(logits, temperature, top_k, top_p, repetition, frequency, presence, uniform, counts, tokens,
+                     context_lens=None, stream=None):
+    """sample() after repetition / frequency / presence penalties from the
+    per-row token counts [batch, vocab] (int32); logits are overwritten with
+    the penalised logits and counts gain each active row's sampled token."""
+    _need(logits, torch.float16, "logits")
+    for t, n in ((temperature, "temperature"), (top_p, "top_p"), (repetition, "repetition"),
+                 (frequency, "frequency"), (presence, "presence"), (uniform, "uniform")):
+        _need(t, torch.float32, n)
+    for t, n in ((top_k, "top_k"), (counts, "counts"), (tokens, "tokens")):
+        _need(t, torch.int32, n)
+    if counts.shape != logits.shape:
+        raise ValueError("counts must have the logits' shape [batch, vocab]")
+    if context_lens is not None:
+        _need(context_lens, torch.int32, "context_lens")
+    _check(_lib.pkv_sample_penalized(_p(logits), logits.shape[0], logits.shape[1], _p(temperature), _p(top_k),
+                                     _p(top_p), _p(repetition), _p(frequency), _p(presence), _p(uniform),
+                                     _p(counts), _p(tokens), _p(context_lens), _stream(stream)))
+
+
 class GraphSet:
     """One captured decode step per batch-size bucket over shared buffers sized
     for the largest bucket; replay(n) runs rows [0, n) in the smallest bucket

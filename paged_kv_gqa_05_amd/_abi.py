@@ -3,7 +3,9 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpkv.so")
+# PKV_LIB_PATH selects another build of the same library (the host-sanitizer
+# build that tests/test_host_sanitizers.py makes); the default is the in-tree one.
+LIB_PATH = os.environ.get("PKV_LIB_PATH") or os.path.join(HERE, "libpkv.so")
 
 c_status = C.c_int
 vp = C.c_void_p
@@ -53,6 +55,8 @@ SIGNATURES = {
     "pkv_prefill": (c_status, [vp, vp, i32p, i32p, i32p, C.c_int, C.c_int, i32p, C.c_int, C.c_int, vp, vp,
                                C.c_size_t, vp]),
     "pkv_sample": (c_status, [vp, C.c_int, C.c_int, vp, i32p, vp, vp, i32p, i32p, vp]),
+    "pkv_sample_penalized": (c_status, [vp, C.c_int, C.c_int, vp, i32p, vp, vp, vp, vp, vp, i32p, i32p, i32p,
+                                        vp]),
     "pkv_graph_capture": (c_status, [vp, vp, i32p, i32p, C.c_int, i32p, C.c_int, C.c_int, vp, vp,
                                      vp, size_t, vp, C.POINTER(vp)]),
     "pkv_graph_replay": (c_status, [vp, vp]),

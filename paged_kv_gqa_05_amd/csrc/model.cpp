@@ -441,6 +441,20 @@ pkv_status pkv_sample(const void* logits, int batch, int vocab, const float* tem
   return PKV_OK;
 }
 
+pkv_status pkv_sample_penalized(void* logits, int batch, int vocab, const float* temperature, const int32_t* top_k,
+                                const float* top_p, const float* repetition, const float* frequency,
+                                const float* presence, const float* uniform, int32_t* counts, int32_t* tokens,
+                                const int32_t* context_lens, pkv_stream_t stream) {
+  if (batch < 1 || vocab < 1) return fail(PKV_E_ARG, "batch and vocab must be >= 1");
+  if (vocab > (1 << 24)) return fail(PKV_E_ARG, "vocab must be <= 2^24");
+  if (!logits || !temperature || !top_k || !top_p || !repetition || !frequency || !presence || !uniform ||
+      !counts || !tokens)
+    return fail(PKV_E_ARG, "NULL argument");
+  PKV_HIP(launch_sample(logits, batch, vocab, temperature, top_k, top_p, uniform, context_lens, tokens,
+                        static_cast<hipStream_t>(stream), logits, counts, repetition, frequency, presence));
+  return PKV_OK;
+}
+
 pkv_status pkv_graph_capture(const pkv_model* m, pkv_cache* cache, const int32_t* tokens, const int32_t* bt,
                              int bt_stride, const int32_t* lens, int batch, int max_context, void* logits,
                              void* hidden_out, void* ws, size_t ws_bytes, pkv_stream_t capture_stream,

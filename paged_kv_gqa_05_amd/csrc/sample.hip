@@ -1,25 +1,33 @@
-// Sampling of the next token after the captured forward pass: temperature,
-// top-k, top-p and an inverse-CDF draw with a uniform number per row supplied
-// by the caller (zingnex.cn article, section 支持的参数: temperature with 0 =
-// greedy, top_p, top_k with -1 = disabled; rvLLM post, section "CUDA 그래프
-// 리플레이": sampling stays outside the graph).
+// Sampling of the next token after the captured forward pass: penalties,
+// temperature, top-k, top-p and an inverse-CDF draw with a uniform number per
+// row supplied by the caller (zingnex.cn article, section 支持的参数:
+// temperature with 0 = greedy, top_p, top_k with -1 = disabled; section
+// CPU操作优化: repetition, frequency and presence penalties, combined; rvLLM
+// post, section "CUDA 그래프 리플레이": sampling stays outside the graph).
+//
+// Penalties (penalize_kernel, before the sampler, in place): for every token
+// already sampled c > 0 times for the row, in float32 with one rounding per
+// operation, x = x > 0 ? x / r : x * r, then x = (x - f c) - p, rounded to f16.
 //
 // Per row (one workgroup of 1024 threads), for T > 0:
-//   z = logit / T; top-k keeps every token with z at or above the k-th
-//   largest (ties kept); w = exp(z - max z); top-p keeps every token with w at
-//   or above tau, the largest weight whose kept mass reaches top_p * sum w
-//   (ties kept); the draw takes the first kept token in index order whose
-//   running sum of w exceeds u * (kept mass).
-// z and w are increasing functions of the f16 logit, so both thresholds are
-// found as a logit: radix descent over the logit's 16-bit order-preserving
-// key, an 11-bit digit then a 5-bit one, counting tokens (top-k) or summing
-// their w (top-p) per bin.  Masses are summed in 64-bit fixed point (w times
-// 2^40, w <= 1), so every sum is exact and order-free and a row's result is
-// the same on every run.  The kept sets, ties included, are then exactly
-// the ones the definitions give.  Passes over the row: max and count (fused
+//   every finite logit x weighs W(x) = floor(2^40 E((x - m) (1/T))), m the
+//   largest finite logit and E a float32 exponential with one rounding per
+//   operation (no fused multiply-add), so the weights, every mass and the
+//   draw are exact integers that a plain reimplementation reproduces;
+//   top-k keeps every token whose logit is at least the k-th largest (ties
+//   kept); top-p keeps the tokens whose logit is at least the largest value t
+//   for which the kept tokens at or above t carry ceil(top_p sum W) (ties
+//   kept); the draw takes the first kept token in index order whose running
+//   sum of W exceeds floor(u24 Z / 2^24), u24 = floor(u 2^24), Z the kept mass.
+// Both thresholds are found as a logit: radix descent over the logit's
+// 16-bit order-preserving key, an 11-bit digit then a 5-bit one, counting
+// tokens (top-k) or summing W (top-p) per bin; sums are 64-bit integers, so
+// they are exact and order-free.  Passes over the row: max and count (fused
 // into the first top-k pass), two for top-k, two for top-p (the first also
-// gives sum w), one to sum w per wave segment and per 64-unit step of it;
-// then one wave loads the step where the draw lands.  Non-finite logits are never kept.
+// gives sum W), one to sum W per wave segment and per 64-unit step of it;
+// then one wave loads the step where the draw lands.  Non-finite logits are
+// never kept.  With a counts buffer the row's count of the sampled token is
+// incremented at the end.
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -84,8 +92,36 @@ __device__ __forceinline__ void for_row(const Row<VEC>& r, F&& f) {
 
 typedef unsigned long long u64;
 
-// w in [0, 1] as a 2^-40 fixed-point integer (sums of up to 2^24 stay below 2^64)
-__device__ __forceinline__ u64 wfix(float w) { return (u64)(w * 0x1p40f); }
+// float32 constants of the exponential: log2(e), ln 2 split as c1 + c2 (c1
+// exact in 9 bits, so n c1 is exact), Taylor coefficients 1/k!
+__device__ constexpr float kL2E = (float)1.4426950408889634;
+__device__ constexpr float kLn2Hi = 0.693359375f;
+__device__ constexpr float kLn2Lo = (float)-2.12194440e-4;
+__device__ constexpr float kC7 = (float)(1.0 / 5040.0), kC6 = (float)(1.0 / 720.0), kC5 = (float)(1.0 / 120.0),
+                           kC4 = (float)(1.0 / 24.0), kC3 = (float)(1.0 / 6.0);
+
+// W = floor(2^40 e^y) for y = (x - mx) * inv_t <= 0 (1 for x = mx, 0 for
+// y < -30): n = floor(y log2 e + 1/2), r = (y - n c1) - n c2, e^r by the
+// degree-7 Taylor polynomial in Horner form, scaled by 2^(n + 40).  Every
+// operation is rounded on its own (no contraction into fused multiply-adds),
+// so the integer is fixed by the float32 arithmetic alone.
+__device__ __forceinline__ u64 wfixed(float x, float mx, float inv_t) {
+#pragma clang fp contract(off)
+  const float d = x - mx;
+  const float y = d == 0.f ? 0.f : d * inv_t;
+  if (!(y >= -30.f)) return 0ull;
+  const float n = floorf(y * kL2E + 0.5f);
+  const float r = (y - n * kLn2Hi) - n * kLn2Lo;
+  float p = kC7;
+  p = p * r + kC6;
+  p = p * r + kC5;
+  p = p * r + kC4;
+  p = p * r + kC3;
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  return (u64)ldexpf(p, (int)n + 40);
+}
 
 struct Smem {
   union {
@@ -93,8 +129,8 @@ struct Smem {
     u64 l[kBins];
   } hist;
   u64 wl[kSW];
-  float steps[kSW * kMaxSteps];
-  float wf[kSW];
+  u64 steps[kSW * kMaxSteps];
+  u64 wf[kSW];
   int wi[kSW];
   int bin;
   u64 before, total, target;
@@ -162,7 +198,8 @@ __global__ void __launch_bounds__(kST) sample_kernel(const uint16_t* __restrict_
                                                      const int32_t* __restrict__ top_k,
                                                      const float* __restrict__ top_p,
                                                      const float* __restrict__ uniform,
-                                                     const int32_t* __restrict__ lens, int32_t* __restrict__ out) {
+                                                     const int32_t* __restrict__ lens, int32_t* __restrict__ out,
+                                                     int32_t* __restrict__ counts) {
   __shared__ Smem sm;
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (lens && lens[b] == 0) {  // inactive row
@@ -191,7 +228,9 @@ __global__ void __launch_bounds__(kST) sample_kernel(const uint16_t* __restrict_
         const uint32_t oh = (uint32_t)sm.hist.i[2 * w], ol = (uint32_t)sm.hist.i[2 * w + 1];
         if (oh > hi || (oh == hi && ol > lo)) hi = oh, lo = ol;
       }
-      out[b] = hi == 0 ? 0 : (int)(0xffffffffu - lo);
+      const int tok = hi == 0 ? 0 : (int)(0xffffffffu - lo);
+      out[b] = tok;
+      if (counts) counts[(size_t)b * vocab + tok] += 1;
     }
     return;
   }
@@ -234,9 +273,7 @@ __global__ void __launch_bounds__(kST) sample_kernel(const uint16_t* __restrict_
     __syncthreads();
   }
   auto kept = [&](uint32_t key) { return key_finite(key) && key >= thr; };
-  // w = exp((x - max) / T) on the hardware's base-2 exponential
-  const float c2 = inv_t * 1.44269504088896341f;
-  auto weight_of = [&](float x) { return __builtin_amdgcn_exp2f((x - mx) * c2); };
+  auto weight_of = [&](float x) { return wfixed(x, mx, inv_t); };
   auto weight = [&](uint32_t u) { return weight_of(logit_of(u)); };
 
   // ---- top-p: the key of tau (mass per bin; the first pass also gives sum w)
@@ -246,7 +283,7 @@ __global__ void __launch_bounds__(kST) sample_kernel(const uint16_t* __restrict_
     clear_hist(sm);
     for_row(row, [&](int, uint32_t u) {
       const uint32_t key = hkey(u);
-      if (kept(key)) atomicAdd(&sm.hist.l[key >> 5], wfix(weight(u)));
+      if (kept(key)) atomicAdd(&sm.hist.l[key >> 5], weight(u));
     });
     __syncthreads();
     select_bin<true>(sm, 0, 0, frac);
@@ -263,20 +300,20 @@ __global__ void __launch_bounds__(kST) sample_kernel(const uint16_t* __restrict_
     __syncthreads();
     const uint32_t cnt = tid < 32 ? sm.hist.i[tid] : 0u;
     __syncthreads();
-    if (tid < 32) sm.hist.l[tid] = cnt ? (u64)cnt * wfix(weight_of(key_value((hb << 5) | tid))) : 0ull;
+    if (tid < 32) sm.hist.l[tid] = cnt ? (u64)cnt * weight_of(key_value((hb << 5) | tid)) : 0ull;
     __syncthreads();
     select_bin<true>(sm, above, target, 0.f);
     thr = max(thr, (hb << 5) | sm.bin);
     __syncthreads();
   }
 
-  // ---- the draw: each wave sums w over its contiguous segment of units, 64
+  // ---- the draw: each wave sums W over its contiguous segment of units, 64
   // units per step, keeping the step sums (up to kMaxSteps) for the walk
   const int n = row.units();
   const int seg = (n + kSW - 1) / kSW;
   const int s0 = min(wave * seg, n), s1 = min(s0 + seg, n);
   const int nsteps = (s1 - s0 + 63) >> 6;
-  float ws = 0.f;
+  u64 ws = 0;
   int lastk = -1;
   for (int st0 = 0; st0 < nsteps; st0 += 4) {
     uint4 q[4];
@@ -286,7 +323,7 @@ __global__ void __launch_bounds__(kST) sample_kernel(const uint16_t* __restrict_
     for (int u = 0; u < 4; ++u) {
       const int st = st0 + u, v = s0 + st * 64 + lane;
       if (st >= nsteps) break;
-      float uw = 0.f;
+      u64 uw = 0;
       if (v < s1) {
 #pragma unroll
         for (int j = 0; j < Row<VEC>::kElems; ++j) {
@@ -294,7 +331,6 @@ __global__ void __launch_bounds__(kST) sample_kernel(const uint16_t* __restrict_
           if (kept(hkey(e))) uw += weight(e), lastk = v * Row<VEC>::kElems + j;
         }
       }
-      // butterfly: every lane ends with the same bits (each add is commutative)
       for (int o = 32; o > 0; o >>= 1) uw += __shfl_xor(uw, o, 64);
       if (lane == 0 && st < kMaxSteps) sm.steps[wave * kMaxSteps + st] = uw;
       ws += uw;
@@ -303,19 +339,21 @@ __global__ void __launch_bounds__(kST) sample_kernel(const uint16_t* __restrict_
   for (int o = 32; o > 0; o >>= 1) lastk = max(lastk, __shfl_xor(lastk, o, 64));
   if (lane == 0) sm.wf[wave] = ws, sm.wi[wave] = lastk;
   __syncthreads();
-  float total = 0.f;
+  u64 total = 0;
   for (int w = 0; w < kSW; ++w) total += sm.wf[w];
   float uu = uniform[b];
-  uu = uu < 0.f ? 0.f : (uu >= 1.f ? 0.99999994f : uu);
-  const float target = uu * total;
-  // the first segment whose running total passes the target; none (rounding,
-  // or nothing kept): the last kept token of the row
+  uu = uu > 0.f ? fminf(uu, 0.99999994f) : 0.f;  // [0, 1 - 2^-24]; NaN -> 0
+  const u64 u24 = (u64)(uu * 16777216.f);         // exact scaling, then truncation
+  // floor(u24 * total / 2^24) without overflow (total < 2^58)
+  const u64 target = ((u24 * (total >> 32)) << 8) + ((u24 * (total & 0xffffffffull)) >> 24);
+  // the first segment whose running total passes the target (none only when
+  // nothing is kept: then token 0)
   int hit = -1;
-  float run = 0.f;
+  u64 run = 0;
   int last_all = -1;
   for (int w = 0; w < kSW; ++w) {
     last_all = max(last_all, sm.wi[w]);
-    if (hit < 0 && sm.wf[w] > 0.f && run + sm.wf[w] > target) hit = w;
+    if (hit < 0 && sm.wf[w] > 0 && run + sm.wf[w] > target) hit = w;
     if (hit < 0) run += sm.wf[w];
   }
   if (tid == 0) sm.tok = last_all < 0 ? 0 : last_all;
@@ -326,38 +364,35 @@ __global__ void __launch_bounds__(kST) sample_kernel(const uint16_t* __restrict_
     if (nsteps <= kMaxSteps) {
       int st = 0;
       for (; st < nsteps; ++st) {
-        const float t = sm.steps[wave * kMaxSteps + st];
-        if (t > 0.f && run + t > target) break;
+        const u64 t = sm.steps[wave * kMaxSteps + st];
+        if (t > 0 && run + t > target) break;
         run += t;
       }
       stb = st;
       ste = st < nsteps ? st + 1 : st;
     }
-    int tok = -1, seen = -1;
+    int tok = -1;
     for (int st = stb; st < ste && tok < 0; ++st) {
       const int v = s0 + st * 64 + lane;
       const uint4 q = row.load(min(v, s1 - 1));
-      float uw = 0.f;
-      int ul = -1;
+      u64 uw = 0;
       if (v < s1) {
 #pragma unroll
         for (int j = 0; j < Row<VEC>::kElems; ++j) {
           const uint32_t e = Row<VEC>::elem(q, j);
-          if (kept(hkey(e))) uw += weight(e), ul = v * Row<VEC>::kElems + j;
+          if (kept(hkey(e))) uw += weight(e);
         }
       }
-      seen = max(seen, ul);
-      float incl = uw;
+      u64 incl = uw;
       for (int o = 1; o < 64; o <<= 1) {
-        const float t = __shfl_up(incl, o, 64);
+        const u64 t = __shfl_up(incl, o, 64);
         if (lane >= o) incl += t;
       }
-      const unsigned long long m = __ballot(uw > 0.f && run + incl > target);
+      const unsigned long long m = __ballot(uw > 0 && run + incl > target);
       if (m) {
         const int f = __ffsll((long long)m) - 1;
         if (lane == f) {
-          float r = run + incl - uw;
-          tok = ul;  // rounding: the unit's last kept token
+          u64 r = run + incl - uw;
 #pragma unroll
           for (int j = 0; j < Row<VEC>::kElems; ++j) {
             const uint32_t e = Row<VEC>::elem(q, j);
@@ -376,27 +411,60 @@ __global__ void __launch_bounds__(kST) sample_kernel(const uint16_t* __restrict_
         run += __shfl(incl, 63, 64);
       }
     }
-    // rounding left the draw past every walked token: the last kept one seen,
-    // else the segment's last kept token
-    for (int o = 32; o > 0; o >>= 1) seen = max(seen, __shfl_xor(seen, o, 64));
-    if (tok < 0 && lane == 0) sm.tok = seen >= 0 ? seen : sm.wi[wave];
   }
   __syncthreads();
-  if (tid == 0) out[b] = sm.tok;
+  if (tid == 0) {
+    out[b] = sm.tok;
+    if (counts) counts[(size_t)b * vocab + sm.tok] += 1;
+  }
+}
+
+// Penalties in place, before the sampler: tokens already sampled for the row
+// (counts > 0) get x / r (x > 0) or x * r, then - f c - p, in float32 with
+// one rounding per operation, stored back as f16.  Rows that are inactive or
+// whose three parameters are neutral are left untouched.
+__global__ void __launch_bounds__(256) penalize_kernel(uint16_t* __restrict__ logits, int vocab,
+                                                       const int32_t* __restrict__ counts,
+                                                       const float* __restrict__ repetition,
+                                                       const float* __restrict__ frequency,
+                                                       const float* __restrict__ presence,
+                                                       const int32_t* __restrict__ lens) {
+#pragma clang fp contract(off)
+  const int b = blockIdx.y;
+  if (lens && lens[b] == 0) return;
+  const float r = repetition[b], f = frequency[b], p = presence[b];
+  if (r == 1.f && f == 0.f && p == 0.f) return;
+  const int32_t* crow = counts + (size_t)b * vocab;
+  uint16_t* lrow = logits + (size_t)b * vocab;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < vocab; i += gridDim.x * blockDim.x) {
+    const int c = crow[i];
+    if (c > 0) {
+      float x = logit_of(lrow[i]);
+      x = x > 0.f ? x / r : x * r;
+      x = (x - f * (float)c) - p;
+      lrow[i] = __builtin_bit_cast(uint16_t, (h16)x);
+    }
+  }
 }
 
 }  // namespace
 
 hipError_t launch_sample(const void* logits, int batch, int vocab, const float* temperature, const int32_t* top_k,
                          const float* top_p, const float* uniform, const int32_t* lens, int32_t* tokens,
-                         hipStream_t s) {
+                         hipStream_t s, void* penalized_logits, int32_t* counts, const float* repetition,
+                         const float* frequency, const float* presence) {
+  if (counts && penalized_logits) {
+    const int per_row = std::min(64, (vocab + 1023) / 1024);
+    hipLaunchKernelGGL(penalize_kernel, dim3(per_row, batch), dim3(256), 0, s,
+                       static_cast<uint16_t*>(penalized_logits), vocab, counts, repetition, frequency, presence, lens);
+  }
   const auto* l = static_cast<const uint16_t*>(logits);
   if (vocab % 8 == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0)
     hipLaunchKernelGGL(sample_kernel<true>, dim3(batch), dim3(kST), 0, s, l, vocab, temperature, top_k, top_p,
-                       uniform, lens, tokens);
+                       uniform, lens, tokens, counts);
   else
     hipLaunchKernelGGL(sample_kernel<false>, dim3(batch), dim3(kST), 0, s, l, vocab, temperature, top_k, top_p,
-                       uniform, lens, tokens);
+                       uniform, lens, tokens, counts);
   return hipGetLastError();
 }
 

@@ -314,3 +314,24 @@ def sampling_case(batch, vocab, seed, masked_rows=True):
     lens = np.where(idx % 9 == 8, 0, 1 + idx).astype(np.int32)
     return SamplingCase(lg.astype(F16), temps[idx % 5], ks[(idx // 2) % 6], ps[(idx // 3) % 6],
                         rng.random(batch).astype(np.float32), lens)
+
+
+def penalty_case(batch, vocab, seed):
+    """Per-row token counts (200 random tokens of each row seen 1-5 times,
+    every fifth row never seen) and penalty parameters cycling over rows:
+    repetition {1, 1.1, 1.3, 0.8}, frequency {0, 0.2, 0.5}, presence
+    {0, 0.3, 1, 2.5}; every seventh row neutral (1, 0, 0)."""
+    rng = np.random.default_rng(seed)
+    counts = np.zeros((batch, vocab), np.int32)
+    for b in range(batch):
+        if b % 5 == 4:
+            continue
+        ids = rng.choice(vocab, size=min(200, vocab), replace=False)
+        counts[b, ids] = rng.integers(1, 6, size=ids.size)
+    idx = np.arange(batch)
+    rep = np.array([1.0, 1.1, 1.3, 0.8], np.float32)[idx % 4]
+    freq = np.array([0.0, 0.2, 0.5], np.float32)[idx % 3]
+    pres = np.array([0.0, 0.3, 1.0, 2.5], np.float32)[(idx // 2) % 4]
+    neutral = idx % 7 == 6
+    rep[neutral], freq[neutral], pres[neutral] = 1.0, 0.0, 0.0
+    return counts, rep, freq, pres
