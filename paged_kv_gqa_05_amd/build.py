@@ -58,5 +58,44 @@ def build(verbose=True):
     return LIB
 
 
+# Host-side sanitizer build (AddressSanitizer + UndefinedBehaviorSanitizer on
+# the host code only; the CPU tests that load it run no kernel): the
+# host runtime's argument checks, allocator and validation run under it in the
+# CPU tests.  Each -fsanitize= follows -Xarch_host.
+SAN_OBJ = os.path.join(CSRC, "_obj_hostsan")
+SAN_LIB = os.path.join(HERE, "libpkv_hostsan.so")
+SAN_FLAGS = ["-O1", "-g", "-std=c++17", "-fPIC", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def _compile_san(src):
+    obj = os.path.join(SAN_OBJ, os.path.basename(src) + ".o")
+    cmd = [HIPCC, "--offload-arch=gfx950", *SAN_FLAGS, "-x", "hip", "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    return src, obj, r.returncode, r.stdout + r.stderr
+
+
+def build_host_sanitized():
+    os.makedirs(SAN_OBJ, exist_ok=True)
+    srcs = sources()
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        results = list(ex.map(_compile_san, srcs))
+    bad = [r for r in results if r[2] != 0]
+    if bad:
+        raise RuntimeError("hipcc (host sanitizer build) failed:\n" + "\n".join(b[3] for b in bad))
+    tmp = SAN_LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libasan", "-o", tmp, *[r[1] for r in results]]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build())
+    if len(sys.argv) > 1 and sys.argv[1] == "--host-sanitized":
+        print(build_host_sanitized())
+    else:
+        print(build())

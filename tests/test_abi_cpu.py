@@ -111,6 +111,43 @@ def test_allocator_ascending_shuffled_and_capacity():
     assert sorted(full.tolist()) == list(range(50))
 
 
+def test_allocator_random_sequences_against_a_model():
+    """Random grow / release sequences over many rows: the allocator never
+    hands out a block twice, frees exactly the blocks a released row held,
+    reports the free count of a plain Python model, and leaves rows and its
+    state unchanged on every refused request."""
+    rng = np.random.default_rng(11)
+    nb, rows, stride = 97, 12, 10
+    a = pkv.BlockAllocator(nb, seed=5)
+    bt = np.full((rows, stride), -1, np.int32)
+    lens = np.zeros(rows, np.int64)
+    used = set()
+    for _ in range(3000):
+        r = int(rng.integers(rows))
+        if rng.random() < 0.7:
+            new = int(lens[r] + rng.integers(0, 40))
+            need = (new + 15) // 16 - (int(lens[r]) + 15) // 16
+            before, free = bt[r].copy(), a.free_blocks
+            if new > stride * 16 or need > nb - len(used):
+                with pytest.raises(pkv.PkvError):
+                    a.grow(bt[r], int(lens[r]), new)
+                assert np.array_equal(bt[r], before) and a.free_blocks == free
+                continue
+            a.grow(bt[r], int(lens[r]), new)
+            fresh = bt[r, (int(lens[r]) + 15) // 16:(new + 15) // 16].tolist()
+            assert not (set(fresh) & used) and len(set(fresh)) == len(fresh)
+            used |= set(fresh)
+            lens[r] = new
+        else:
+            n = (int(lens[r]) + 15) // 16
+            a.release(bt[r], int(lens[r]))
+            used -= set(bt[r, :n].tolist())
+            bt[r] = -1
+            lens[r] = 0
+        assert a.free_blocks == nb - len(used)
+        assert all(0 <= x < nb for x in used)
+
+
 def test_validate_metadata():
     bt = np.array([[3, 1, -1], [0, 2, -1]], np.int32)
     lens = np.array([20, 17], np.int32)
