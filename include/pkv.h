@@ -170,6 +170,27 @@ pkv_status pkv_paged_attn_decode(const pkv_cache* cache, int layer, const void* 
                                  int max_context, float scale, void* workspace,
                                  size_t workspace_bytes, pkv_stream_t stream);
 
+/* Allocation-free variant of pkv_paged_attn_decode, for callers that cannot
+ * allocate device memory (code under hipGraph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and errors as
+ * pkv_paged_attn_decode without the workspace: the arrival counters and the
+ * partial results live in a static device array of PKV_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) that each GPU the library runs on holds until the process ends.
+ * The call allocates nothing.  PKV_E_ARG when the shape needs more scratch
+ * than that (batch x Hkv above 131072 counters, or partials above ~31.5 MiB;
+ * the partials take batch x Hq x P x (D + 2) x 4 bytes for P partitions of
+ * 512-1024 tokens when a row spans several: e.g. batch 32, Hq 28, contexts up
+ * to 32768 need 29.8 MiB).  Every call on one GPU shares that GPU's array and
+ * leaves its counters zero; two calls in flight at once on one GPU (two
+ * streams, or two host threads) race and give wrong results.  The first call
+ * on a device clears the counters with a kernel on the given stream (a call
+ * under capture records that kernel; the next uncaptured call clears again). */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+pkv_status pkv_paged_attn_decode_noalloc(const pkv_cache* cache, int layer, const void* q, void* out,
+                                         float* lse, const int32_t* block_tables, int bt_stride,
+                                         const int32_t* context_lens, int batch, int num_q_heads,
+                                         int max_context, float scale, pkv_stream_t stream);
+
 /* --------------------------------------------------------------------- model */
 
 typedef struct {

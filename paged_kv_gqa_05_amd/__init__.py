@@ -132,6 +132,21 @@ def paged_attn_decode(cache, layer, q, out, block_tables, context_lens, max_cont
                                       _stream(stream)))
 
 
+def paged_attn_decode_noalloc(cache, layer, q, out, block_tables, context_lens, max_context, scale, lse=None,
+                              stream=None):
+    """paged_attn_decode with the library's static per-GPU scratch instead of a
+    workspace (allocates nothing; calls on one GPU must not overlap)."""
+    _need(q, torch.float16, "q")
+    _need(out, torch.float16, "out")
+    _need(block_tables, torch.int32, "block_tables")
+    _need(context_lens, torch.int32, "context_lens")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+    _check(_lib.pkv_paged_attn_decode_noalloc(cache.handle, layer, _p(q), _p(out), _p(lse), _p(block_tables),
+                                              block_tables.shape[1], _p(context_lens), q.shape[0], q.shape[1],
+                                              max_context, float(scale), _stream(stream)))
+
+
 # --------------------------------------------------------------------- model
 
 class Model:

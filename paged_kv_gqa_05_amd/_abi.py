@@ -42,6 +42,8 @@ SIGNATURES = {
     "pkv_attn_workspace_bytes": (c_status, [vp, C.c_int, C.c_int, C.c_int, C.POINTER(size_t)]),
     "pkv_paged_attn_decode": (c_status, [vp, C.c_int, vp, vp, vp, i32p, C.c_int, i32p, C.c_int,
                                          C.c_int, C.c_int, C.c_float, vp, size_t, vp]),
+    "pkv_paged_attn_decode_noalloc": (c_status, [vp, C.c_int, vp, vp, vp, i32p, C.c_int, i32p, C.c_int,
+                                                 C.c_int, C.c_int, C.c_float, vp]),
     "pkv_model_create": (c_status, [C.POINTER(ModelDesc), vp, C.POINTER(LayerWeights), vp, vp,
                                     C.POINTER(vp)]),
     "pkv_model_destroy": (None, [vp]),
