@@ -159,8 +159,62 @@ class DecodeRun:
         self.cache.close()
 
 
+OP_NAMES = ("qkv_rope_append", "attention", "o_proj_resid", "norm_gate_up_silu", "down_proj_resid")
+
+
+def op_bytes_flops(shape, batch, mean_ctx, kv_elt=2):
+    """Algorithmic HBM bytes and FLOPs of one launch of each fused op of one
+    layer at `batch` rows: the op's weights once, its activation input and
+    output, and for attention the KV of every row's context (read once per
+    KV head) plus q and o."""
+    h, d, f = shape.hidden, shape.head_dim, shape.ffn
+    hq, hkv = shape.n_q_heads, shape.n_kv_heads
+    qkv = (hq + 2 * hkv) * d
+    kv = batch * mean_ctx * hkv * d * 2 * kv_elt
+    return {
+        "qkv_rope_append": (2 * (qkv * h + qkv + h) + batch * h * 2 + batch * hq * d * 2 + batch * 2 * hkv * d * kv_elt,
+                            2 * batch * qkv * h),
+        "attention": (kv + 2 * batch * hq * d * 2, 4 * batch * mean_ctx * hq * d),
+        "o_proj_resid": (2 * h * hq * d + batch * hq * d * 2 + 2 * batch * h * 2, 2 * batch * h * hq * d),
+        "norm_gate_up_silu": (2 * (2 * f * h + h) + batch * h * 2 + batch * f * 2, 2 * batch * 2 * f * h),
+        "down_proj_resid": (2 * h * f + batch * f * 2 + 2 * batch * h * 2, 2 * batch * h * f),
+    }
+
+
+def time_layer_ops(pkv, torch, run, rounds=10):
+    """Each fused op alone (pkv_layer_op) on the run's cache and metadata,
+    cycling over every layer so that weights and KV come from HBM (28 layers
+    of weights exceed the 256 MB Infinity Cache), HIP events on the stream the
+    ops run on.  Returns microseconds per launch per op."""
+    shape, b = run.shape, run.batch
+    hidden = torch.empty(b, shape.hidden, dtype=torch.float16, device="cuda").normal_()
+    ws = torch.zeros(pkv.step_workspace_bytes(run.model, run.cache, b, run.max_context), dtype=torch.uint8,
+                     device="cuda")
+    lens_d, bt_d = run.lens_d, run.bt_d
+    for op in range(5):   # one pass in layer order fills q, o and act before the ops are timed alone
+        pkv.layer_op(run.model, run.cache, 0, op, hidden, bt_d, lens_d, run.max_context, ws)
+    out = {}
+    stream = torch.cuda.current_stream()
+    for op, name in enumerate(OP_NAMES):
+        for layer in range(shape.n_layers):
+            pkv.layer_op(run.model, run.cache, layer, op, hidden, bt_d, lens_d, run.max_context, ws)
+        with no_gc():
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(rounds):
+                for layer in range(shape.n_layers):
+                    pkv.layer_op(run.model, run.cache, layer, op, hidden, bt_d, lens_d, run.max_context, ws)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) * 1e3 / (rounds * shape.n_layers)
+        if op == 4 and not torch.isfinite(hidden).all().item():   # the residual adds keep growing hidden
+            hidden.normal_()
+    return out
+
+
 def time_decode(pkv, torch, model, shape, batch, prompt_len, warmup, steps, seed, kv_dtype="f16",
-                prompt_fill="prefill", prefill_repeats=3):
+                prompt_fill="prefill", prefill_repeats=3, ops=False, op_rounds=10):
     run = DecodeRun(pkv, torch, model, shape, batch, prompt_len, prompt_len + warmup + steps, seed, kv_dtype)
     if prompt_fill == "prefill":
         prefill_ms = run.prefill(prefill_repeats)
@@ -181,9 +235,17 @@ def time_decode(pkv, torch, model, shape, batch, prompt_len, warmup, steps, seed
         wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1)
     ctx_mean = float(run.lens.mean()) - steps / 2.0
+    op_us = time_layer_ops(pkv, torch, run, rounds=op_rounds) if ops else None
+    op_ctx = float(run.lens.mean())
     run.close()
     r = {"batch": batch, "ms_per_step": ms / steps, "tok_s": batch * steps / (ms / 1e3),
          "wall_s": wall, "mean_context": ctx_mean}
+    if op_us:
+        bf = op_bytes_flops(shape, batch, op_ctx, kv_elt=1 if kv_dtype == "fp8" else 2)
+        r["layer_ops"] = {n: {"us_per_launch": op_us[n], "bytes": int(bf[n][0]), "flops": int(bf[n][1]),
+                              "GBs": bf[n][0] / (op_us[n] * 1e-6) / 1e9,
+                              "TFLOPs": bf[n][1] / (op_us[n] * 1e-6) / 1e12} for n in OP_NAMES}
+        r["layer_ops_mean_context"] = op_ctx
     if prefill_ms:
         tflops = prefill_flops(shape, batch, prompt_len) / (prefill_ms / 1e3) / 1e12
         r.update({"prefill_ms": prefill_ms, "prefill_tok_s": batch * prompt_len / (prefill_ms / 1e3),
@@ -305,45 +367,93 @@ def time_sampling(pkv, torch, inp, batch, vocab, rounds, seed, mode):
             "logit_bytes": batch * vocab * 2}
 
 
-def attention_traffic():
-    """HBM bytes per attn15 launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE runs (scaled by a device copy of known size), or None when the
-    attention kernel's sources have changed since the counters were taken."""
+ATTN_SOURCES = ("attn.hip", "coherent.h", "pkv_internal.h")
+GEMM_SOURCES = ("gemm.hip", "linear.h", "linear.hip", "coherent.h", "kvstore.h", "pkv_internal.h")
+
+
+def sources_sha256(files):
+    """SHA-256 over the named kernel sources (in order)."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(here, "paged_kv_gqa_05_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counted_traffic(profile, files):
+    """HBM bytes per launch from a committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary under profiles/ (each counter scaled by what it reads for a device
+    copy of known size), or None when the kernel's sources have changed since
+    the counters were taken."""
     here = os.path.dirname(os.path.abspath(__file__))
     try:
-        text = open(os.path.join(here, "profiles", "paged_attention_attn15_counters.txt")).read()
+        text = open(os.path.join(here, "profiles", profile)).read()
         fields = dict(l.split(": ", 1) for l in text.splitlines() if l.startswith(("traffic_", "sources_")))
-        h = hashlib.sha256()
-        for f in ("attn.hip", "coherent.h", "pkv_internal.h"):
-            with open(os.path.join(here, "paged_kv_gqa_05_amd", "csrc", f), "rb") as fh:
-                h.update(fh.read())
-        if h.hexdigest() != fields["sources_sha256"].strip():
+        if sources_sha256(files) != fields["sources_sha256"].strip():
             return None
         return int(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
 
 
+def attention_traffic():
+    return counted_traffic("paged_attention_attn15_counters.txt", ATTN_SOURCES)
+
+
+def gate_up_traffic():
+    return counted_traffic("gemm_gate_up_qwen15_b256_counters.txt", GEMM_SOURCES)
+
+
 # ---------------------------------------------------------- CPU oracle leg
+
+def host_description():
+    """Host CPU as lscpu and the BLAS runtime report it."""
+    import subprocess
+    info = {"os_cpu_count": os.cpu_count()}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            k, v = k.strip(), v.strip()
+            if k in ("Model name", "Socket(s)", "Core(s) per socket", "Thread(s) per core", "CPU(s)"):
+                info[k] = v
+    except Exception as e:  # no lscpu: keep what os reports
+        info["lscpu_error"] = str(e)
+    try:
+        from threadpoolctl import threadpool_info
+        pools = threadpool_info()
+        info["blas"] = [{"api": p.get("internal_api"), "threads": p.get("num_threads")} for p in pools]
+        info["blas_threads"] = max([p.get("num_threads", 1) for p in pools] or [1])
+    except Exception:
+        info["blas_threads"] = os.cpu_count()
+    return info
+
+
+def _host_weights(weights, layers=None):
+    pick = range(len(weights["layers"])) if layers is None else layers
+    return {
+        "embed": weights["embed"].cpu().numpy(), "w_final_norm": weights["w_final_norm"].cpu().numpy(),
+        "w_lm_head": weights["w_lm_head"].cpu().numpy(),
+        "layers": [{k: (None if t is None else t.cpu().numpy()) for k, t in weights["layers"][i].items()}
+                   for i in pick],
+    }
+
+
+def _oracle_cfg(oracle, shape, n_layers=None):
+    return oracle.ModelConfig(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn,
+                              shape.vocab, shape.n_layers if n_layers is None else n_layers, shape.rms_eps,
+                              shape.rope_theta)
+
 
 def cpu_baseline(torch, weights, shape, batch_sample, ctx):
     """The oracle (as it stands, default precision) running one decode step of
-    the same model for a few rows with a pre-filled context of `ctx` tokens."""
+    the same model for the headline's rows with a pre-filled context of `ctx`
+    tokens, repeated from the same state until 10 s of CPU work (at most 6)."""
     import oracle
     import pkv_inputs as inp
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count()
-    host = {
-        "embed": weights["embed"].cpu().numpy(), "w_final_norm": weights["w_final_norm"].cpu().numpy(),
-        "w_lm_head": weights["w_lm_head"].cpu().numpy(),
-        "layers": [{k: (None if t is None else t.cpu().numpy()) for k, t in lw.items()}
-                   for lw in weights["layers"]],
-    }
-    cfg = oracle.ModelConfig(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn,
-                             shape.vocab, shape.n_layers, shape.rms_eps, shape.rope_theta)
+    host = _host_weights(weights)
+    cfg = _oracle_cfg(oracle, shape)
     rng = np.random.default_rng(7)
     lens = np.full(batch_sample, ctx, np.int32)
     bt, nb = inp.deal_block_tables(rng, lens, ctx)
@@ -354,16 +464,67 @@ def cpu_baseline(torch, weights, shape, batch_sample, ctx):
         kps.append(k)
         vps.append(v)
     toks = rng.integers(0, shape.vocab, size=batch_sample).astype(np.int32)
-    # the same step (same state: each repeat rewrites the same cache slots)
-    # until at least 10 s of CPU work, at most 6 times
     reps, t0 = 0, time.perf_counter()
     while reps < 6 and (reps == 0 or time.perf_counter() - t0 < 10.0):
         oracle.decode_step(cfg, host, kps, vps, toks, bt, lens)
         reps += 1
     dt = time.perf_counter() - t0
-    return {"value": batch_sample * reps / dt, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+    hd = host_description()
+    return {"value": batch_sample * reps / dt, "unit": "tok/s", "cores": int(hd["blas_threads"]), "kind": "oracle",
             "sample": f"{reps} x one oracle decode step (fp64) of the 28-layer 1.5B-shape model for "
-                      f"{batch_sample} rows at context {ctx}: {dt:.1f} s"}
+                      f"{batch_sample} rows at context {ctx}: {dt:.1f} s",
+            "host": hd}
+
+
+def cpu_attention_legs():
+    """The oracle's paged attention (fp64, one Python loop per row and head) on
+    the seeded attn15 workload (all 64 rows) and on the first 8 of the 32 rows
+    of the fp8 long-context workload; GB/s over the same algorithmic bytes as
+    the GPU figures."""
+    import oracle
+    import pkv_inputs as inp
+    legs = {}
+    for name, w, rows in (("attn15", inp.ATTN15, None), ("fp8long", inp.FP8LONG, 8)):
+        case = inp.workload_case(w)
+        sel = slice(None) if rows is None else slice(0, rows)
+        lens = case.ctx_lens[sel]
+        t0 = time.perf_counter()
+        oracle.paged_attention_batch(case.q[sel], case.k_pool, case.v_pool, case.block_tables[sel], lens, case.scale,
+                                     k_scale=case.k_scale, v_scale=case.v_scale)
+        dt = time.perf_counter() - t0
+        elt = 1 if w.kv_dtype == "fp8" else 2
+        nbytes = int(lens.sum()) * w.n_kv_heads * w.head_dim * 2 * elt + 2 * case.q[sel].size * 2
+        legs[name] = {"s_per_call": dt, "GBs": nbytes / dt / 1e9, "rows": int(len(lens)),
+                      "sample": f"one oracle call over {len(lens)} of {w.batch} rows ({int(lens.sum())} tokens)"}
+        del case
+    return legs
+
+
+def cpu_layer_leg(torch, weights, shape, batch, ctx, name):
+    """One oracle decode layer (fp64) of the model's layer 0 for `batch` rows
+    at context `ctx`, plus one final norm + LM head; the step estimate is
+    L x layer + head (a bounded sample of one decode step)."""
+    import oracle
+    import pkv_inputs as inp
+    host = _host_weights(weights, layers=[0])
+    cfg = _oracle_cfg(oracle, shape, 1)
+    rng = np.random.default_rng(8)
+    lens = np.full(batch, ctx, np.int32)
+    bt, nb = inp.deal_block_tables(rng, lens, ctx)
+    valid = inp.valid_slot_masks(bt, lens - 1, nb)
+    k, v = inp.random_pools(rng, nb, shape.n_kv_heads, shape.head_dim, valid)
+    h = rng.standard_normal((batch, shape.hidden)).astype(np.float16)
+    t0 = time.perf_counter()
+    oracle.decode_layer(cfg, host["layers"][0], h, k, v, bt, lens)
+    t_layer = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    n = oracle.rmsnorm(h, host["w_final_norm"], shape.rms_eps)
+    (n @ host["w_lm_head"].astype(np.float64).T).astype(np.float16)
+    t_head = time.perf_counter() - t0
+    step = shape.n_layers * t_layer + t_head
+    return {"name": name, "tok_s_estimate": batch / step, "s_per_layer": t_layer, "s_head": t_head,
+            "sample": f"one oracle layer (fp64) for {batch} rows at context {ctx}, x{shape.n_layers} layers, "
+                      f"+ one final norm and LM head"}
 
 
 # ---------------------------------------------------------------------- main
@@ -381,6 +542,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-attn", action="store_true")
     ap.add_argument("--no-sample", action="store_true")
+    ap.add_argument("--no-ops", action="store_true", help="skip timing the fused ops alone at the headline batch")
+    ap.add_argument("--op-rounds", type=int, default=10, help="rounds over the 28 layers per fused op timed alone")
     ap.add_argument("--prompt-fill", choices=("prefill", "decode"), default="prefill",
                     help="prompts enter by one batched prefill call (timed) or one decode step per position")
     ap.add_argument("--prefill-repeats", type=int, default=3, help="timed repeats of the prefill call")
@@ -423,7 +586,8 @@ def main():
     per_batch = {}
     for n in batches:
         r = time_decode(pkv, torch, model, shape, n, args.prompt, args.warmup, args.steps, seed=2003 + n,
-                        prompt_fill=args.prompt_fill, prefill_repeats=args.prefill_repeats)
+                        prompt_fill=args.prompt_fill, prefill_repeats=args.prefill_repeats,
+                        ops=(n == max(batches) and not args.no_ops), op_rounds=args.op_rounds)
         nbytes = step_bytes(shape, n, r["mean_context"])
         r["bytes_per_step"] = nbytes
         r["roofline_ms"] = nbytes / (HBM_PEAK_GBS * 1e9) * 1e3
@@ -446,6 +610,7 @@ def main():
         per_batch_fp8[n] = r
         log(f"batch {n}, E4M3 KV cache: {r['ms_per_step']:.3f} ms/step, {r['tok_s']:.0f} tok/s")
 
+    cpu_legs = {}
     per_batch_7b = {}
     batches_7b = [int(x) for x in args.batches_7b.split(",") if x.strip()] if batches else []
     if batches_7b:
@@ -465,6 +630,9 @@ def main():
             per_batch_7b[n] = r
             log(f"7B batch {n}: {r['ms_per_step']:.3f} ms/step, {r['tok_s']:.0f} tok/s, "
                 f"{100 * r['frac_of_roofline']:.1f}% of the HBM roofline")
+        if not args.no_cpu:
+            cpu_legs["full7_step"] = cpu_layer_leg(torch, w7, shape7, 8, args.prompt_7b, "7B shape, 8 rows")
+            log(f"cpu oracle 7B leg: {cpu_legs['full7_step']['tok_s_estimate']:.3f} tok/s (estimate)")
         model7.close()
         del w7
         torch.cuda.empty_cache()
@@ -488,16 +656,35 @@ def main():
         return
     h = per_batch[head]
     a = attn.get("attn15")
-    roofline = None
+    roofline = roofline_attention = None
+    g = (h.get("layer_ops") or {}).get("norm_gate_up_silu")
+    if g:
+        # the headline step's dominant kernel: its time per launch alone, weights from HBM
+        roofline = {"bound": "hbm", "kernel": f"RMSNorm + gate/up projection + SiLU*mul (MFMA GEMM), 1.5B shape, "
+                                              f"batch {head}: weights 2F x H f16 + hidden in + act out",
+                    "achieved": round(g["GBs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(g["GBs"] / HBM_PEAK_GBS, 4), "traffic": gate_up_traffic(),
+                    "bytes_per_launch": g["bytes"], "us_per_launch": round(g["us_per_launch"], 3),
+                    "flops_per_launch": g["flops"], "TFLOPs": round(g["TFLOPs"], 1),
+                    "mfma_frac": round(g["TFLOPs"] / MFMA_F16_PEAK_TFLOPS, 4)}
     if a:
-        roofline = {"bound": "hbm", "kernel": "paged attention (split + fused merge, one kernel), "
-                                              "attn15: 1.5B layer shape, batch 64, contexts U[128, 2048]",
-                    "achieved": round(a["GBs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(a["GBs"] / HBM_PEAK_GBS, 4), "traffic": attention_traffic()}
+        roofline_attention = {"bound": "hbm", "kernel": "paged attention (split + fused merge, one kernel), "
+                                                        "attn15: 1.5B layer shape, batch 64, contexts U[128, 2048]",
+                              "achieved": round(a["GBs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(a["GBs"] / HBM_PEAK_GBS, 4), "traffic": attention_traffic(),
+                              "bytes_per_launch": a["bytes_per_call"], "us_per_launch": round(a["us_per_call"], 3)}
+    if roofline is None:
+        roofline = roofline_attention
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(torch, weights, shape, head, args.prompt)
         log(f"cpu oracle: {cpu['value']:.3f} tok/s ({cpu['sample']})")
+        cpu_legs.update(cpu_attention_legs())
+        tiny_w = inp.model_weights_torch(inp.TINY, seed=1001)
+        cpu_legs["tiny_layer"] = cpu_layer_leg(torch, tiny_w, inp.TINY, 4, 64, "tiny layer, 4 rows")
+        cpu["legs"] = cpu_legs
+        log("cpu oracle legs: " + ", ".join(f"{k}: {v.get('GBs', v.get('tok_s_estimate')):.3g}"
+                                             for k, v in cpu_legs.items()))
 
     line = {
         "metric": "decode tok/s at N=1/64/128/256 + paged-attn HBM GB/s (% of 8 TB/s peak)",
@@ -524,6 +711,7 @@ def main():
         "attention": attn,
         "sampling": sampling,
         "roofline": roofline,
+        "roofline_attention": roofline_attention,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

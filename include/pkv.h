@@ -258,6 +258,28 @@ pkv_status pkv_decode_layer(const pkv_model* model, pkv_cache* cache, int layer,
                             const int32_t* context_lens, int batch, int max_context,
                             void* workspace, size_t workspace_bytes, pkv_stream_t stream);
 
+/* One of the five fused ops of a decoder layer (rvLLM post, section
+ * "퓨즈드 CUDA 커널"), run alone; in the order below they are exactly
+ * pkv_decode_layer (bit for bit), passing q, the attention output and the
+ * SiLU*mul activation through the workspace:
+ *   PKV_OP_QKV      RMSNorm(hidden) * w_in, QKV projection + bias, RoPE of q
+ *                   and k, q into the workspace, the new k and v into the cache
+ *   PKV_OP_ATTN     paged GQA attention of that q (split + merge)
+ *   PKV_OP_O        hidden += W_o o
+ *   PKV_OP_GATE_UP  RMSNorm(hidden) * w_post, gate/up projection, SiLU(g) * u
+ *                   into the workspace
+ *   PKV_OP_DOWN     hidden += W_down act
+ * Arguments as pkv_decode_layer, with the same batch, max_context and
+ * workspace for the ops of one layer step.  The workspace must be zero-filled
+ * before its first use by this call (its arrival counters must start at
+ * zero; every call, and every decode step or prefill, leaves them zero).
+ * PKV_E_ARG for an op outside the list.  Meant for profiling and testing a
+ * single fused kernel; the decode step runs all five in one graph. */
+enum { PKV_OP_QKV = 0, PKV_OP_ATTN = 1, PKV_OP_O = 2, PKV_OP_GATE_UP = 3, PKV_OP_DOWN = 4 };
+pkv_status pkv_layer_op(const pkv_model* model, pkv_cache* cache, int layer, int op, void* hidden,
+                        const int32_t* block_tables, int bt_stride, const int32_t* context_lens, int batch,
+                        int max_context, void* workspace, size_t workspace_bytes, pkv_stream_t stream);
+
 /* One decode step: h = embed[token_ids[b]], every layer, then
  * logits = W_lm RMSNorm(h) * w_final_norm.  token_ids int32 [batch];
  * logits f16 [batch][V]; hidden_out (nullable) f16 [batch][H] gets the final

@@ -189,6 +189,18 @@ def decode_layer(model, cache, layer, hidden, block_tables, context_lens, max_co
                                  _p(workspace), workspace.numel(), _stream(stream)))
 
 
+OP_QKV, OP_ATTN, OP_O, OP_GATE_UP, OP_DOWN = range(5)
+
+
+def layer_op(model, cache, layer, op, hidden, block_tables, context_lens, max_context, workspace, stream=None):
+    """One fused op of a decoder layer (OP_QKV .. OP_DOWN; in that order they
+    are decode_layer).  The workspace must start zero-filled."""
+    _need(hidden, torch.float16, "hidden")
+    _check(_lib.pkv_layer_op(model.handle, cache.handle, layer, int(op), _p(hidden), _p(block_tables),
+                             block_tables.shape[1], _p(context_lens), hidden.shape[0], max_context,
+                             _p(workspace), workspace.numel(), _stream(stream)))
+
+
 def decode_step(model, cache, token_ids, block_tables, context_lens, max_context, logits, workspace,
                 hidden_out=None, stream=None):
     _need(token_ids, torch.int32, "token_ids")

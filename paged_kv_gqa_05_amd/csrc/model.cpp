@@ -169,73 +169,81 @@ pkv_status check_step(const pkv_model* m, const pkv_cache* cache, const int32_t*
   return PKV_OK;
 }
 
-// pre (prefill only): attention runs as the causal multi-token kernel over the
-// new tokens' sequences instead of one decode row per token.
-hipError_t run_layer(const pkv_model* m, pkv_cache* cache, int layer, _Float16* h, const int32_t* bt,
-                     int bt_stride, const int32_t* lens, int batch, const StepBuffers& sb,
-                     const AttnPlan& plan, hipStream_t s, const PrefillAttnArgs* pre = nullptr) {
+// One of the layer's five fused ops (PKV_OP_*).  pre (prefill only):
+// attention runs as the causal multi-token kernel over the new tokens'
+// sequences instead of one decode row per token.
+hipError_t run_layer_op(const pkv_model* m, pkv_cache* cache, int layer, int op, _Float16* h, const int32_t* bt,
+                        int bt_stride, const int32_t* lens, int batch, const StepBuffers& sb, const AttnPlan& plan,
+                        hipStream_t s, const PrefillAttnArgs* pre = nullptr) {
   const pkv_model_desc& d = m->d;
   const pkv_layer_weights& w = m->layers[layer];
   const int qkv_n = (d.num_q_heads + 2 * d.num_kv_heads) * d.head_dim;
   const int qd = d.num_q_heads * d.head_dim;
   void* kp = cache->k_pool(layer);
   void* vp = cache->v_pool(layer);
-  hipError_t e;
-
-  LinArgs a{};
-  a.eps = d.rms_eps;
-  // 1. RMSNorm + QKV (+ bias) + RoPE; q out, k and v of the new token into the cache
-  a.A = h; a.lda = d.hidden; a.K = d.hidden; a.M = batch;
-  a.W = static_cast<const _Float16*>(w.w_qkv);
-  a.gain = static_cast<const _Float16*>(w.w_in); a.norm = 1;
-  a.bias = static_cast<const _Float16*>(w.b_qkv);
-  a.n_out = qkv_n / 2;  // rotation pairs (i, i + D/2) of every head
-  a.rope.cos_sin = static_cast<const float2*>(m->rope);
-  a.rope.lens = lens; a.rope.bt = bt; a.rope.bt_stride = bt_stride;
-  a.rope.q_out = sb.q;
   const bool fp8 = cache->desc.dtype == PKV_KV_FP8_E4M3;
   const float ks = fp8 ? cache->k_scales[layer] : 1.f, vs = fp8 ? cache->v_scales[layer] : 1.f;
-  a.rope.k_pool = kp; a.rope.v_pool = vp;
-  a.rope.hq = d.num_q_heads; a.rope.hkv = d.num_kv_heads; a.rope.d = d.head_dim;
-  a.rope.fp8 = fp8; a.rope.k_scale = ks; a.rope.v_scale = vs;
-  if ((e = launch_linear(a, EPI_ROPE, sb.gemm_ws, sb.counters, s)) != hipSuccess) return e;
-  // 2. paged attention
-  if (pre) {
-    PrefillAttnArgs pa = *pre;
-    pa.k_pool = kp; pa.v_pool = vp; pa.q = sb.q; pa.out = sb.o;
-    pa.hq = d.num_q_heads; pa.hkv = d.num_kv_heads; pa.head_dim = d.head_dim; pa.fp8 = fp8;
-    pa.scale = 1.0f / std::sqrt((float)d.head_dim); pa.k_scale = ks; pa.v_scale = vs;
-    if ((e = launch_prefill_attention(pa, s)) != hipSuccess) return e;
-  } else {
-  AttnArgs at{};
-  at.k_pool = kp; at.v_pool = vp; at.q = sb.q; at.out = sb.o; at.lse = nullptr;
-  at.bt = bt; at.bt_stride = bt_stride; at.lens = lens; at.batch = batch;
-  at.hq = d.num_q_heads; at.hkv = d.num_kv_heads; at.head_dim = d.head_dim; at.fp8 = fp8;
-  at.scale = 1.0f / std::sqrt((float)d.head_dim); at.k_scale = ks; at.v_scale = vs; at.ws = sb.attn_ws;
-  if ((e = launch_paged_attention(at, plan, s)) != hipSuccess) return e;
+  LinArgs a{};
+  a.eps = d.rms_eps;
+  switch (op) {
+    case PKV_OP_QKV: {  // RMSNorm + QKV (+ bias) + RoPE; q out, k and v of the new token into the cache
+      a.A = h; a.lda = d.hidden; a.K = d.hidden; a.M = batch;
+      a.W = static_cast<const _Float16*>(w.w_qkv);
+      a.gain = static_cast<const _Float16*>(w.w_in); a.norm = 1;
+      a.bias = static_cast<const _Float16*>(w.b_qkv);
+      a.n_out = qkv_n / 2;  // rotation pairs (i, i + D/2) of every head
+      a.rope.cos_sin = static_cast<const float2*>(m->rope);
+      a.rope.lens = lens; a.rope.bt = bt; a.rope.bt_stride = bt_stride;
+      a.rope.q_out = sb.q;
+      a.rope.k_pool = kp; a.rope.v_pool = vp;
+      a.rope.hq = d.num_q_heads; a.rope.hkv = d.num_kv_heads; a.rope.d = d.head_dim;
+      a.rope.fp8 = fp8; a.rope.k_scale = ks; a.rope.v_scale = vs;
+      return launch_linear(a, EPI_ROPE, sb.gemm_ws, sb.counters, s);
+    }
+    case PKV_OP_ATTN: {  // paged attention
+      if (pre) {
+        PrefillAttnArgs pa = *pre;
+        pa.k_pool = kp; pa.v_pool = vp; pa.q = sb.q; pa.out = sb.o;
+        pa.hq = d.num_q_heads; pa.hkv = d.num_kv_heads; pa.head_dim = d.head_dim; pa.fp8 = fp8;
+        pa.scale = 1.0f / std::sqrt((float)d.head_dim); pa.k_scale = ks; pa.v_scale = vs;
+        return launch_prefill_attention(pa, s);
+      }
+      AttnArgs at{};
+      at.k_pool = kp; at.v_pool = vp; at.q = sb.q; at.out = sb.o; at.lse = nullptr;
+      at.bt = bt; at.bt_stride = bt_stride; at.lens = lens; at.batch = batch;
+      at.hq = d.num_q_heads; at.hkv = d.num_kv_heads; at.head_dim = d.head_dim; at.fp8 = fp8;
+      at.scale = 1.0f / std::sqrt((float)d.head_dim); at.k_scale = ks; at.v_scale = vs; at.ws = sb.attn_ws;
+      return launch_paged_attention(at, plan, s);
+    }
+    case PKV_OP_O:  // O projection + residual add
+      a.A = sb.o; a.lda = qd; a.K = qd; a.M = batch;
+      a.W = static_cast<const _Float16*>(w.w_o);
+      a.out = h; a.ldo = d.hidden; a.n_out = d.hidden;
+      return launch_linear(a, EPI_RESID, sb.gemm_ws, sb.counters, s);
+    case PKV_OP_GATE_UP:  // RMSNorm + gate/up + SiLU*mul -> act
+      a.A = h; a.lda = d.hidden; a.K = d.hidden; a.M = batch;
+      a.W = static_cast<const _Float16*>(w.w_gate_up);
+      a.gain = static_cast<const _Float16*>(w.w_post); a.norm = 1;
+      a.out = sb.act; a.ldo = d.ffn; a.n_out = d.ffn;
+      return launch_linear(a, EPI_SILU, sb.gemm_ws, sb.counters, s);
+    case PKV_OP_DOWN:  // down projection + residual add
+      a.A = sb.act; a.lda = d.ffn; a.K = d.ffn; a.M = batch;
+      a.W = static_cast<const _Float16*>(w.w_down);
+      a.out = h; a.ldo = d.hidden; a.n_out = d.hidden;
+      return launch_linear(a, EPI_RESID, sb.gemm_ws, sb.counters, s);
+    default:
+      return hipErrorInvalidValue;
   }
-  // 3. O projection + residual add
-  a = LinArgs{};
-  a.eps = d.rms_eps;
-  a.A = sb.o; a.lda = qd; a.K = qd; a.M = batch;
-  a.W = static_cast<const _Float16*>(w.w_o);
-  a.out = h; a.ldo = d.hidden; a.n_out = d.hidden;
-  if ((e = launch_linear(a, EPI_RESID, sb.gemm_ws, sb.counters, s)) != hipSuccess) return e;
-  // 4. RMSNorm + gate/up + SiLU*mul -> act
-  a = LinArgs{};
-  a.eps = d.rms_eps;
-  a.A = h; a.lda = d.hidden; a.K = d.hidden; a.M = batch;
-  a.W = static_cast<const _Float16*>(w.w_gate_up);
-  a.gain = static_cast<const _Float16*>(w.w_post); a.norm = 1;
-  a.out = sb.act; a.ldo = d.ffn; a.n_out = d.ffn;
-  if ((e = launch_linear(a, EPI_SILU, sb.gemm_ws, sb.counters, s)) != hipSuccess) return e;
-  // 5. down projection + residual add
-  a = LinArgs{};
-  a.eps = d.rms_eps;
-  a.A = sb.act; a.lda = d.ffn; a.K = d.ffn; a.M = batch;
-  a.W = static_cast<const _Float16*>(w.w_down);
-  a.out = h; a.ldo = d.hidden; a.n_out = d.hidden;
-  return launch_linear(a, EPI_RESID, sb.gemm_ws, sb.counters, s);
+}
+
+hipError_t run_layer(const pkv_model* m, pkv_cache* cache, int layer, _Float16* h, const int32_t* bt,
+                     int bt_stride, const int32_t* lens, int batch, const StepBuffers& sb,
+                     const AttnPlan& plan, hipStream_t s, const PrefillAttnArgs* pre = nullptr) {
+  for (int op = PKV_OP_QKV; op <= PKV_OP_DOWN; ++op) {
+    const hipError_t e = run_layer_op(m, cache, layer, op, h, bt, bt_stride, lens, batch, sb, plan, s, pre);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t run_step(const pkv_model* m, pkv_cache* cache, const int32_t* tokens, const int32_t* bt,
@@ -344,6 +352,24 @@ pkv_status pkv_decode_layer(const pkv_model* m, pkv_cache* cache, int layer, voi
   PKV_HIP(launch_zero_i32(sb.counters, sb.n_counters, static_cast<hipStream_t>(stream)));
   PKV_HIP(run_layer(m, cache, layer, static_cast<_Float16*>(hidden), bt, bt_stride, lens, batch, sb, plan,
                     static_cast<hipStream_t>(stream)));
+  return PKV_OK;
+}
+
+pkv_status pkv_layer_op(const pkv_model* m, pkv_cache* cache, int layer, int op, void* hidden,
+                        const int32_t* bt, int bt_stride, const int32_t* lens, int batch, int max_context,
+                        void* ws, size_t ws_bytes, pkv_stream_t stream) {
+  StepBuffers sb{};
+  AttnPlan plan{};
+  pkv_status st = check_step(m, cache, bt, bt_stride, lens, batch, max_context, ws, ws_bytes, &sb, &plan);
+  if (st != PKV_OK) return st;
+  if (!hidden) return fail(PKV_E_ARG, "hidden is NULL");
+  if (layer < 0 || layer >= m->d.num_layers || layer >= cache->desc.num_layers)
+    return fail(PKV_E_ARG, "layer out of range");
+  if (op < PKV_OP_QKV || op > PKV_OP_DOWN) return fail(PKV_E_ARG, "op must be one of PKV_OP_*");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // no counter reset here (it would add a launch to every op): the caller's
+  // workspace starts zero-filled and every kernel leaves its counters zero
+  PKV_HIP(run_layer_op(m, cache, layer, op, static_cast<_Float16*>(hidden), bt, bt_stride, lens, batch, sb, plan, s));
   return PKV_OK;
 }
 

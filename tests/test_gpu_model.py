@@ -229,3 +229,31 @@ def test_graph_set_buckets_with_inactive_rows(lib):
         for b in (6, 7):
             assert not k[bt[b]].any() and not v[bt[b]].any()
     gs.close()
+
+
+@pytest.mark.parametrize("shape,batch,seed,hi", [(MID, 3, 1101, 300), (MID, 70, 1102, 200),
+                                                 (inp.Shape(1536, 12, 2, 128, 8960, 16, 1), 256, 1103, 700)])
+def test_layer_ops_in_order_equal_decode_layer(lib, shape, batch, seed, hi):
+    """pkv_layer_op for QKV, ATTN, O, GATE_UP, DOWN in order gives the hidden
+    state and cache of pkv_decode_layer bit for bit (1.5B layer at batch 256:
+    split-K and the 128 x 160 gate/up tiles of the bench)."""
+    case = _layer_case(shape, batch, seed, hi=hi)
+    h_ref, k_ref, v_ref = _run_layer_gpu(lib, shape, case)
+    w = weights_to_device(case["weights"])
+    model = lib.Model(shape, w, max_positions=4096)
+    cache = lib.KVCache(1, case["num_blocks"], shape.n_kv_heads, shape.head_dim)
+    k, v = cache.layer(0)
+    k.copy_(torch.from_numpy(k_to_lib(case["k_pool"])))
+    v.copy_(torch.from_numpy(case["v_pool"]))
+    mc = int(case["ctx_lens"].max())
+    hidden = dev(case["hidden"])
+    ws = torch.zeros(lib.step_workspace_bytes(model, cache, batch, mc), dtype=torch.uint8, device="cuda")
+    bt, lens = dev(case["block_tables"]), dev(case["ctx_lens"])
+    for op in (lib.OP_QKV, lib.OP_ATTN, lib.OP_O, lib.OP_GATE_UP, lib.OP_DOWN):
+        lib.layer_op(model, cache, 0, op, hidden, bt, lens, mc, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(hidden.cpu().numpy().view(np.uint16), h_ref.view(np.uint16))
+    assert np.array_equal(k_from_lib(k.cpu().numpy()).view(np.uint16), k_ref.view(np.uint16))
+    assert np.array_equal(v.cpu().numpy().view(np.uint16), v_ref.view(np.uint16))
+    with pytest.raises(lib.PkvError, match="op must be"):
+        lib.layer_op(model, cache, 0, 7, hidden, bt, lens, mc, ws)
