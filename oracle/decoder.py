@@ -19,10 +19,10 @@ What the pages fix, and the readings taken where they are silent:
   hidden state h that is stored in f16 between layers.
 * The KV cache is paged with a per-sequence block table (section
   "PagedAttention과 FlashAttention-3" of the same post; aitrends.kr glossary
-  entry on PagedAttention: fixed-size pages).  Layout (this library's reading;
-  block size BS = 16):
+  entry on PagedAttention: fixed-size pages).  Layout (the plain one; block
+  size BS = 16):
       K pool of a layer: [num_blocks, Hkv, BS, D]  (token-major inside a block)
-      V pool of a layer: [num_blocks, Hkv, D, BS]  (dim-major inside a block)
+      V pool of a layer: [num_blocks, Hkv, BS, D]  (the same)
   Token t of sequence b lives in physical block block_table[b][t // BS], slot
   t % BS.
 * GQA: query head h reads KV head h // (Hq / Hkv) (contiguous groups), which is
@@ -133,7 +133,7 @@ def gather_sequence(k_pool, v_pool, block_row, ctx_len, block_size):
     blocks = np.asarray(block_row)[t // block_size]
     slots = t % block_size
     k = k_pool[blocks, :, slots, :]          # [c, Hkv, D]
-    v = v_pool[blocks, :, :, slots]          # [c, Hkv, D]
+    v = v_pool[blocks, :, slots, :]          # [c, Hkv, D]
     return k, v
 
 
@@ -218,7 +218,7 @@ def kv_append(k_pool, v_pool, k_new, v_new, block_tables, ctx_lens, k_scale=None
         pos = c - 1
         blk = int(block_tables[b][pos // bs])
         k_pool[blk, :, pos % bs, :] = k_new[b]
-        v_pool[blk, :, :, pos % bs] = v_new[b]
+        v_pool[blk, :, pos % bs, :] = v_new[b]
 
 
 # ---------------------------------------------------------------- one layer

@@ -114,12 +114,15 @@ def valid_slot_masks(block_tables, ctx_lens, num_blocks):
 
 
 def random_pools(rng, num_blocks, n_kv_heads, head_dim, valid):
-    """K [NB, Hkv, 16, D] and V [NB, Hkv, D, 16] f16, N(0,1) in valid slots, NaN elsewhere."""
+    """K and V [NB, Hkv, 16, D] f16 (token-major blocks), N(0,1) in valid slots,
+    NaN elsewhere.  V is drawn in [NB, Hkv, D, 16] order and transposed (the
+    draw order of the first recipe, kept so that seeded values stay the same)."""
     k = rng.standard_normal((num_blocks, n_kv_heads, BLOCK_SIZE, head_dim), dtype=np.float32).astype(F16)
     v = rng.standard_normal((num_blocks, n_kv_heads, head_dim, BLOCK_SIZE), dtype=np.float32).astype(F16)
-    inval = ~valid
-    k[np.broadcast_to(inval[:, None, :, None], k.shape)] = np.nan
-    v[np.broadcast_to(inval[:, None, None, :], v.shape)] = np.nan
+    v = np.ascontiguousarray(v.transpose(0, 1, 3, 2))
+    mask = np.broadcast_to((~valid)[:, None, :, None], k.shape)
+    k[mask] = np.nan
+    v[mask] = np.nan
     return k, v
 
 
@@ -141,7 +144,7 @@ def quantize_e4m3(x, amax=None):
 class AttnCase:
     q: np.ndarray            # [B, Hq, D] f16
     k_pool: np.ndarray       # [NB, Hkv, 16, D] f16 or uint8
-    v_pool: np.ndarray       # [NB, Hkv, D, 16] f16 or uint8
+    v_pool: np.ndarray       # [NB, Hkv, 16, D] f16 or uint8
     block_tables: np.ndarray  # [B, stride] int32
     ctx_lens: np.ndarray     # [B] int32
     scale: float
@@ -267,9 +270,10 @@ def model_weights_torch(shape: Shape, seed, device="cuda", bias=True, std=0.02, 
 
 
 def random_pools_torch(seed, num_blocks, n_kv_heads, head_dim, valid, device="cuda"):
-    """The random_pools recipe (N(0, 1) in valid slots, NaN elsewhere) drawn
-    with torch's Philox generator on the device, for full-size caches whose
-    host generation would dominate a test.  valid: bool [num_blocks, 16]."""
+    """The random_pools recipe (N(0, 1) in valid slots, NaN elsewhere; K and V
+    [NB, Hkv, 16, D]) drawn with torch's Philox generator on the device, for
+    full-size caches whose host generation would dominate a test.
+    valid: bool [num_blocks, 16]."""
     import torch
     g = torch.Generator(device=device)
     g.manual_seed(seed)
@@ -277,9 +281,10 @@ def random_pools_torch(seed, num_blocks, n_kv_heads, head_dim, valid, device="cu
     v = torch.empty(num_blocks, n_kv_heads, head_dim, BLOCK_SIZE, dtype=torch.float16, device=device)
     k.normal_(generator=g)
     v.normal_(generator=g)
+    v = v.transpose(2, 3).contiguous()
     inval = torch.from_numpy(~np.asarray(valid, dtype=bool)).to(device)
     k.masked_fill_(inval[:, None, :, None], float("nan"))
-    v.masked_fill_(inval[:, None, None, :], float("nan"))
+    v.masked_fill_(inval[:, None, :, None], float("nan"))
     return k, v
 
 

@@ -34,7 +34,7 @@ def appended(case, kp, vp):
     for b, c in enumerate(case["ctx_lens"]):
         blk = case["block_tables"][b][(c - 1) // 16]
         ks.append(kp[blk, :, (c - 1) % 16, :])
-        vs.append(vp[blk, :, :, (c - 1) % 16])
+        vs.append(vp[blk, :, (c - 1) % 16, :])
     return np.stack(ks), np.stack(vs)
 
 

@@ -32,21 +32,32 @@ def k_from_lib(k):
 
 
 def v_to_lib(v):
-    """V pool [NB, Hkv, D, 16] (numpy) -> the library's tile layout: unchanged
-    for f16; fp8 codes [NB, Hkv, D/64, 4, 16, 4, 4] where dim d = 64 jj + 16 r + n
-    and token t = 4 q4 + tt sit at [jj, q4, n, r, tt]."""
+    """V pool [NB, Hkv, 16, D] (numpy or torch; token-major like K) -> the
+    library's tile layout: f16 dim-major [NB, Hkv, D, 16]; fp8 codes
+    [NB, Hkv, D/64, 4, 16, 4, 4] where dim d = 64 jj + 16 r + n and token
+    t = 4 q4 + tt sit at [jj, q4, n, r, tt]."""
+    nb, hkv, bs, d = v.shape
+    if isinstance(v, torch.Tensor):
+        if v.dtype != torch.uint8:
+            return v.transpose(2, 3).contiguous()
+        return v.reshape(nb, hkv, 4, 4, d // 64, 4, 16).permute(0, 1, 4, 2, 6, 5, 3).contiguous()
     if v.dtype != np.uint8:
-        return v
-    nb, hkv, d, bs = v.shape
-    return np.ascontiguousarray(v.reshape(nb, hkv, d // 64, 4, 16, 4, 4).transpose(0, 1, 2, 5, 4, 3, 6))
+        return np.ascontiguousarray(v.transpose(0, 1, 3, 2))
+    return np.ascontiguousarray(v.reshape(nb, hkv, 4, 4, d // 64, 4, 16).transpose(0, 1, 4, 2, 6, 5, 3))
 
 
 def v_from_lib(v):
-    """Inverse of v_to_lib for fp8 views [NB, Hkv, D/64, 4, 16, 4, 4]."""
+    """Inverse of v_to_lib: the library's f16 [NB, Hkv, D, 16] or fp8
+    [NB, Hkv, D/64, 4, 16, 4, 4] view -> [NB, Hkv, 16, D]."""
+    if isinstance(v, torch.Tensor):
+        if v.ndim == 4:
+            return v.transpose(2, 3).contiguous()
+        nb, hkv, ng = v.shape[:3]
+        return v.permute(0, 1, 3, 6, 2, 5, 4).reshape(nb, hkv, 16, ng * 64).contiguous()
     if v.ndim == 4:
-        return v
+        return np.ascontiguousarray(v.transpose(0, 1, 3, 2))
     nb, hkv, ng = v.shape[:3]
-    return np.ascontiguousarray(v.transpose(0, 1, 2, 5, 4, 3, 6).reshape(nb, hkv, ng * 64, 16))
+    return np.ascontiguousarray(v.transpose(0, 1, 3, 6, 2, 5, 4).reshape(nb, hkv, 16, ng * 64))
 
 
 def load_case_into_cache(pkv, case, num_layers=1, layer=0, cache=None):

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import pkv_inputs as inp
-from gpu_util import dev, load_case_into_cache, assert_parity, k_from_lib
+from gpu_util import dev, load_case_into_cache, assert_parity, k_from_lib, v_from_lib
 
 pytestmark = pytest.mark.gpu
 
@@ -80,8 +80,8 @@ def test_fp8_all_codes_decode_exactly(lib):
     """Single-token contexts make out = V exactly: all 256 E4M3 codes through the kernel."""
     codes = np.arange(256, dtype=np.uint8).reshape(2, 128)
     kp = np.full((2, 1, 16, 128), 0x38, np.uint8)      # K = 1.0 everywhere
-    vp = np.full((2, 1, 128, 16), 0x7F, np.uint8)      # NaN outside slot 0
-    vp[:, 0, :, 0] = codes
+    vp = np.full((2, 1, 16, 128), 0x7F, np.uint8)      # NaN outside slot 0
+    vp[:, 0, 0, :] = codes
     case = inp.AttnCase(q=np.ones((2, 1, 128), np.float16), k_pool=kp, v_pool=vp,
                         block_tables=np.array([[0], [1]], np.int32), ctx_lens=np.array([1, 1], np.int32),
                         scale=0.125, k_scale=1.0, v_scale=1.0, num_blocks=2, max_context=1)
@@ -115,7 +115,7 @@ def test_one_hot_probe_bit_exact(lib):
     out, _ = run_attention(lib, case, with_lse=False)
     for i in range(b):
         blk = case.block_tables[i][tstar[i] // 16]
-        want = case.v_pool[blk, 0, :, tstar[i] % 16]
+        want = case.v_pool[blk, 0, tstar[i] % 16, :]
         assert np.array_equal(out[i, 0].view(np.uint16), want.view(np.uint16)), i
         assert np.array_equal(out[i, 1].view(np.uint16), want.view(np.uint16)), i
 
@@ -204,7 +204,7 @@ def test_kv_append_bit_exact(lib):
     oracle.kv_append(kp, vp, k, v, case.block_tables, case.ctx_lens)
     gk, gv = cache.layer(0)
     assert np.array_equal(k_from_lib(gk.cpu().numpy()).view(np.uint16), kp.view(np.uint16))
-    assert np.array_equal(gv.cpu().numpy().view(np.uint16), vp.view(np.uint16))
+    assert np.array_equal(v_from_lib(gv.cpu().numpy()).view(np.uint16), vp.view(np.uint16))
 
 
 def test_host_errors_enqueue_nothing(lib):

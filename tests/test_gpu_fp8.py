@@ -113,8 +113,7 @@ def test_decode_layer_fp8(lib, batch, seed, hi):
     for b, c in enumerate(case["ctx_lens"]):
         if c > 0:
             kmask[case["block_tables"][b][(c - 1) // 16], :, (c - 1) % 16, :] = True
-    vmask = np.moveaxis(kmask, 2, 3)
-    for got, ref, orig, sc, m in ((ck, rk, kq, ks, kmask), (cv, rv, vq, vs, vmask)):
+    for got, ref, orig, sc, m in ((ck, rk, kq, ks, kmask), (cv, rv, vq, vs, kmask)):
         assert np.array_equal(got[~m], orig[~m])
         assert (got[m] == ref[m]).mean() > 0.95
         dg = oracle.e4m3_decode(got[m]) * sc
@@ -155,7 +154,7 @@ def test_decode_steps_fp8_cache_greedy(lib):
     ws = torch.empty(lib.step_workspace_bytes(model, cache, batch, mc), dtype=torch.uint8, device="cuda")
     logits = torch.empty(batch, shape.vocab, dtype=torch.float16, device="cuda")
     kp = [np.full((nb, shape.n_kv_heads, 16, shape.head_dim), 0x7F, np.uint8) for _ in range(n_layers)]
-    vp = [np.full((nb, shape.n_kv_heads, shape.head_dim, 16), 0x7F, np.uint8) for _ in range(n_layers)]
+    vp = [np.full((nb, shape.n_kv_heads, 16, shape.head_dim), 0x7F, np.uint8) for _ in range(n_layers)]
     cfg = oracle_config(shape)
     agree = total = 0
     worst = 0.0
@@ -172,12 +171,11 @@ def test_decode_steps_fp8_cache_greedy(lib):
         kmask = np.zeros(kp[0].shape, bool)
         for b, c in enumerate(lens):
             kmask[bt[b][(c - 1) // 16], :, (c - 1) % 16, :] = True
-        vmask = np.moveaxis(kmask, 2, 3)
         for layer in range(n_layers):
             gk, gv = cache.layer(layer)
             gk, gv = k_from_lib(gk.cpu().numpy()), v_from_lib(gv.cpu().numpy())
             _check_appended(gk, kp[layer], kmask, ks[layer])
-            _check_appended(gv, vp[layer], vmask, vs[layer])
+            _check_appended(gv, vp[layer], kmask, vs[layer])
             kp[layer][...] = gk
             vp[layer][...] = gv
         g_tok = lg.argmax(-1)

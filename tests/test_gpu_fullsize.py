@@ -27,7 +27,7 @@ import torch
 
 import oracle
 import pkv_inputs as inp
-from gpu_util import dev, assert_parity, calibrated, oracle_config, k_to_lib, tie_aware_agree
+from gpu_util import dev, assert_parity, calibrated, oracle_config, k_to_lib, v_to_lib, tie_aware_agree
 from test_gpu_model import _run_layer_gpu, _oracle_layer
 
 pytestmark = pytest.mark.gpu
@@ -54,7 +54,7 @@ def test_decode_layer_full_shape(lib, name, batch):
     blk = case["block_tables"][rows, (case["ctx_lens"] - 1) // 16]
     slot = (case["ctx_lens"] - 1) % 16
     assert_parity(k[blk, :, slot, :], rk[blk, :, slot, :], "appended K")
-    assert_parity(v[blk, :, :, slot], rv[blk, :, :, slot], "appended V")
+    assert_parity(v[blk, :, slot, :], rv[blk, :, slot, :], "appended V")
 
 
 def _host(w):
@@ -81,7 +81,7 @@ class FullStep:
             kd, vd = inp.random_pools_torch(seed + 100 + layer, self.nb, shape.n_kv_heads, shape.head_dim, valid)
             k, v = self.cache.layer(layer)
             k.copy_(k_to_lib(kd))
-            v.copy_(vd)
+            v.copy_(v_to_lib(vd))
             self.pools.append((kd.cpu().numpy(), vd.cpu().numpy()))
             del kd, vd
         self.tokens = rng.integers(0, shape.vocab, size=batch).astype(np.int32)

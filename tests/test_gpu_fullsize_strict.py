@@ -28,7 +28,7 @@ import torch
 
 import oracle
 import pkv_inputs as inp
-from gpu_util import ATOL, RTOL, dev, assert_parity, oracle_config, k_from_lib, tie_aware_agree
+from gpu_util import ATOL, RTOL, dev, assert_parity, oracle_config, k_from_lib, v_from_lib, tie_aware_agree
 
 pytestmark = pytest.mark.gpu
 
@@ -115,15 +115,15 @@ def test_chained_layers_strict(lib, name, batch, prompt):
     for layer in range(shape.n_layers):
         h_in = hidden.cpu().numpy()
         k, v = rig.cache.layer(layer)
-        kp, vp = k_from_lib(k.cpu().numpy()), v.cpu().numpy()
+        kp, vp = k_from_lib(k.cpu().numpy()), v_from_lib(v.cpu().numpy())
         lib.decode_layer(rig.model, rig.cache, layer, hidden, bt_d, lens_d, rig.mc, ws)
         torch.cuda.synchronize()
         h_out = hidden.cpu().numpy()
-        gk, gv = k_from_lib(k.cpu().numpy()), v.cpu().numpy()
+        gk, gv = k_from_lib(k.cpu().numpy()), v_from_lib(v.cpu().numpy())
         rh = oracle.decode_layer(cfg, rig.host_layer(layer), h_in, kp, vp, rig.bt, rig.lens, acc=np.float32)
         err = assert_parity(h_out, rh, f"{name} layer {layer} hidden")
         assert_parity(gk[blk, :, slot, :], kp[blk, :, slot, :], f"{name} layer {layer} appended K")
-        assert_parity(gv[blk, :, :, slot], vp[blk, :, :, slot], f"{name} layer {layer} appended V")
+        assert_parity(gv[blk, :, slot, :], vp[blk, :, slot, :], f"{name} layer {layer} appended V")
         worst.append(err)
         print(f"{name} layer {layer}: max abs err {err:.4f}, |h| max {np.abs(rh.astype(np.float32)).max():.2f}",
               flush=True)
@@ -161,7 +161,7 @@ def test_teacher_forced_greedy_full15_graph(lib):
     first_gpu = rig.logits.cpu().numpy()[rows]
     pools = lambda: ([np.full((rig.nb, shape.n_kv_heads, 16, shape.head_dim), np.nan, np.float16)
                       for _ in range(shape.n_layers)],
-                     [np.full((rig.nb, shape.n_kv_heads, shape.head_dim, 16), np.nan, np.float16)
+                     [np.full((rig.nb, shape.n_kv_heads, 16, shape.head_dim), np.nan, np.float16)
                       for _ in range(shape.n_layers)])
     kps, vps = pools()      # the oracle's own cache
     kgs, vgs = pools()      # the GPU's cache, continued
@@ -170,7 +170,7 @@ def test_teacher_forced_greedy_full15_graph(lib):
     def gpu_blocks(layer, blocks):
         k, v = rig.cache.layer(layer)
         idx = dev(blocks.astype(np.int64))
-        return k_from_lib(k.index_select(0, idx).cpu().numpy()), v.index_select(0, idx).cpu().numpy()
+        return k_from_lib(k.index_select(0, idx).cpu().numpy()), v_from_lib(v.index_select(0, idx).cpu().numpy())
 
     prompt_blocks = np.unique(rig.bt[rows, : (prompt + 15) // 16])
     for layer in range(shape.n_layers):
@@ -210,10 +210,10 @@ def test_teacher_forced_greedy_full15_graph(lib):
                                        acc=np.float32)
         for layer in range(shape.n_layers):   # the GPU's appended K / V, then continue from them
             gk, gv = gpu_blocks(layer, blk)
-            gk, gv = gk[np.arange(n_rows), :, slot, :], gv[np.arange(n_rows), :, :, slot]
+            gk, gv = gk[np.arange(n_rows), :, slot, :], gv[np.arange(n_rows), :, slot, :]
             assert_parity(gk, kgs[layer][blk, :, slot, :], f"step {step} layer {layer} appended K")
-            assert_parity(gv, vgs[layer][blk, :, :, slot], f"step {step} layer {layer} appended V")
-            kgs[layer][blk, :, slot, :], vgs[layer][blk, :, :, slot] = gk, gv
+            assert_parity(gv, vgs[layer][blk, :, slot, :], f"step {step} layer {layer} appended V")
+            kgs[layer][blk, :, slot, :], vgs[layer][blk, :, slot, :] = gk, gv
         tok = gpu_tok.cpu().numpy()   # teacher forcing: every side continues from the GPU's tokens
         for key, r in (("own", rl_own), ("gpu", rl_gpu)):
             res[key]["shares"].append(_share_inside(g_logits, r))

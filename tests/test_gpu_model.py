@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import pkv_inputs as inp
-from gpu_util import dev, assert_parity, weights_to_device, oracle_config, k_to_lib, k_from_lib
+from gpu_util import dev, assert_parity, weights_to_device, oracle_config, k_to_lib, k_from_lib, v_to_lib, v_from_lib
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +26,7 @@ def _run_layer_gpu(pkv, shape, case, max_context=None):
     cache = pkv.KVCache(1, nb, shape.n_kv_heads, shape.head_dim)
     k, v = cache.layer(0)
     k.copy_(torch.from_numpy(k_to_lib(case["k_pool"])))
-    v.copy_(torch.from_numpy(case["v_pool"]))
+    v.copy_(torch.from_numpy(v_to_lib(case["v_pool"])))
     b = case["hidden"].shape[0]
     mc = max_context or int(case["ctx_lens"].max())
     bt = case["block_tables"]
@@ -36,7 +36,7 @@ def _run_layer_gpu(pkv, shape, case, max_context=None):
     ws = torch.empty(pkv.step_workspace_bytes(model, cache, b, mc), dtype=torch.uint8, device="cuda")
     pkv.decode_layer(model, cache, 0, hidden, dev(bt), dev(case["ctx_lens"]), mc, ws)
     torch.cuda.synchronize()
-    return hidden.cpu().numpy(), k_from_lib(k.cpu().numpy()), v.cpu().numpy()
+    return hidden.cpu().numpy(), k_from_lib(k.cpu().numpy()), v_from_lib(v.cpu().numpy())
 
 
 def _oracle_layer(shape, case):
@@ -69,9 +69,8 @@ def test_decode_layer_parity(lib, shape, batch, seed, hi):
     keep = ~changed
     assert np.array_equal(k[keep].view(np.uint16), case["k_pool"][keep].view(np.uint16))
     assert_parity(k[changed], rk[changed], "appended K")
-    vchanged = np.moveaxis(changed, 2, 3)
-    assert np.array_equal(v[~vchanged].view(np.uint16), case["v_pool"][~vchanged].view(np.uint16))
-    assert_parity(v[vchanged], rv[vchanged], "appended V")
+    assert np.array_equal(v[keep].view(np.uint16), case["v_pool"][keep].view(np.uint16))
+    assert_parity(v[changed], rv[changed], "appended V")
 
 
 def test_decode_layer_without_bias_and_unit_gains(lib):
@@ -103,7 +102,7 @@ class StepRig:
         self.hidden = torch.empty(batch, shape.hidden, dtype=torch.float16, device="cuda")
         self.kp = [np.full((self.nb, shape.n_kv_heads, 16, shape.head_dim), np.nan, np.float16)
                    for _ in range(shape.n_layers)]
-        self.vp = [np.full((self.nb, shape.n_kv_heads, shape.head_dim, 16), np.nan, np.float16)
+        self.vp = [np.full((self.nb, shape.n_kv_heads, 16, shape.head_dim), np.nan, np.float16)
                    for _ in range(shape.n_layers)]
         self.cfg = oracle_config(shape)
         self.d_bt = dev(self.bt)
@@ -202,7 +201,7 @@ def test_graph_set_buckets_with_inactive_rows(lib):
                      device="cuda")
     gs = lib.GraphSet(model, cache, buckets, tok_d, dev(bt), lens_d, mc, logits, ws)
     kp = [np.full((nb, shape.n_kv_heads, 16, shape.head_dim), np.nan, np.float16) for _ in range(shape.n_layers)]
-    vp = [np.full((nb, shape.n_kv_heads, shape.head_dim, 16), np.nan, np.float16) for _ in range(shape.n_layers)]
+    vp = [np.full((nb, shape.n_kv_heads, 16, shape.head_dim), np.nan, np.float16) for _ in range(shape.n_layers)]
     cfg = oracle_config(shape)
     out = torch.empty(8, dtype=torch.int32, device="cuda")
     for phase, n in ((0, 3), (1, 6)):
@@ -244,7 +243,7 @@ def test_layer_ops_in_order_equal_decode_layer(lib, shape, batch, seed, hi):
     cache = lib.KVCache(1, case["num_blocks"], shape.n_kv_heads, shape.head_dim)
     k, v = cache.layer(0)
     k.copy_(torch.from_numpy(k_to_lib(case["k_pool"])))
-    v.copy_(torch.from_numpy(case["v_pool"]))
+    v.copy_(torch.from_numpy(v_to_lib(case["v_pool"])))
     mc = int(case["ctx_lens"].max())
     hidden = dev(case["hidden"])
     ws = torch.zeros(lib.step_workspace_bytes(model, cache, batch, mc), dtype=torch.uint8, device="cuda")
@@ -254,6 +253,6 @@ def test_layer_ops_in_order_equal_decode_layer(lib, shape, batch, seed, hi):
     torch.cuda.synchronize()
     assert np.array_equal(hidden.cpu().numpy().view(np.uint16), h_ref.view(np.uint16))
     assert np.array_equal(k_from_lib(k.cpu().numpy()).view(np.uint16), k_ref.view(np.uint16))
-    assert np.array_equal(v.cpu().numpy().view(np.uint16), v_ref.view(np.uint16))
+    assert np.array_equal(v_from_lib(v.cpu().numpy()).view(np.uint16), v_ref.view(np.uint16))
     with pytest.raises(lib.PkvError, match="op must be"):
         lib.layer_op(model, cache, 0, 7, hidden, bt, lens, mc, ws)

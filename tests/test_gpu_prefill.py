@@ -33,11 +33,11 @@ def prefill_case(shape, new_lens, prior_lens, seed, spare_blocks=3):
     kp, vp = [], []
     for _ in range(shape.n_layers):
         k = np.full((nb, shape.n_kv_heads, BS, shape.head_dim), np.nan, np.float16)
-        v = np.full((nb, shape.n_kv_heads, shape.head_dim, BS), np.nan, np.float16)
+        v = np.full((nb, shape.n_kv_heads, BS, shape.head_dim), np.nan, np.float16)
         for s, p in enumerate(prior_lens):
             t = np.arange(p)
             k[bt[s][t // BS], :, t % BS, :] = rng.standard_normal((p, shape.n_kv_heads, shape.head_dim))
-            v[bt[s][t // BS], :, :, t % BS] = rng.standard_normal((p, shape.n_kv_heads, shape.head_dim))
+            v[bt[s][t // BS], :, t % BS, :] = rng.standard_normal((p, shape.n_kv_heads, shape.head_dim))
         kp.append(k)
         vp.append(v)
     tokens = rng.integers(0, shape.vocab, size=sum(new_lens)).astype(np.int32)
@@ -92,11 +92,9 @@ def check_cache(case, shape, gk, gv, rk, rv, seqs=None):
         if seqs is None:
             keep = ~written
             assert np.array_equal(gk[li][keep].view(np.uint16), case["k"][li][keep].view(np.uint16))
-            vkeep = np.moveaxis(keep, 2, 3)
-            assert np.array_equal(gv[li][vkeep].view(np.uint16), case["v"][li][vkeep].view(np.uint16))
+            assert np.array_equal(gv[li][keep].view(np.uint16), case["v"][li][keep].view(np.uint16))
         assert_parity(gk[li][written], rk[li][written], f"layer {li} appended K")
-        vw = np.moveaxis(written, 2, 3)
-        assert_parity(gv[li][vw], rv[li][vw], f"layer {li} appended V")
+        assert_parity(gv[li][written], rv[li][written], f"layer {li} appended V")
 
 
 @pytest.mark.parametrize("shape,new_lens,prior_lens,seed", [
@@ -199,7 +197,7 @@ def test_prefill_fp8_cache(lib):
     for s_ in range(3):
         t = np.arange(case["prior"][s_], case["prior"][s_] + case["starts"][s_ + 1] - case["starts"][s_])
         written[case["bt"][s_][t // BS], :, t % BS, :] = True
-    for got, ref, orig, sc, m in ((gk[0], rk[0], kq, ks, written), (gv[0], rv[0], vq, vs, np.moveaxis(written, 2, 3))):
+    for got, ref, orig, sc, m in ((gk[0], rk[0], kq, ks, written), (gv[0], rv[0], vq, vs, written)):
         assert np.array_equal(got[~m], orig[~m])
         dg = oracle.e4m3_decode(got[m]) * sc
         dr = oracle.e4m3_decode(ref[m]) * sc

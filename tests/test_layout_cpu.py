@@ -26,7 +26,7 @@ def test_k_tile_layout(dtype, d):
 @pytest.mark.parametrize("dtype", ["f16", "fp8"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_v_tile_layout(dtype, d):
-    v = np.ascontiguousarray(_pool(dtype, d).transpose(0, 1, 3, 2))   # [NB, Hkv, D, 16 tokens]
+    v = _pool(dtype, d)                       # [NB, Hkv, 16 tokens, D], as K
     lib = v_to_lib(v).reshape(2, 3, -1)
     for t in range(16):
         for dd in range(d):
@@ -34,5 +34,5 @@ def test_v_tile_layout(dtype, d):
                 off = (((dd // 64) * 4 + t // 4) * 16 + dd % 16) * 16 + ((dd // 16) % 4) * 4 + t % 4
             else:
                 off = dd * 16 + t
-            assert lib[0, 1, off] == v[0, 1, dd, t]
+            assert lib[0, 1, off] == v[0, 1, t, dd]
     assert np.array_equal(v_from_lib(v_to_lib(v)), v)

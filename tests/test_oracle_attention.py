@@ -25,7 +25,7 @@ def _scatter(k_tok, v_tok, n_blocks, rng=None, order=None):
     need = (c + BS - 1) // BS
     ids = order if order is not None else rng.permutation(n_blocks)[:need]
     kp = np.full((n_blocks, hkv, BS, d), np.nan, np.float16)
-    vp = np.full((n_blocks, hkv, d, BS), np.nan, np.float16)
+    vp = np.full((n_blocks, hkv, BS, d), np.nan, np.float16)
     row = np.full(need, -1, np.int32)
     row[:] = ids[:need]
     for t in range(c):

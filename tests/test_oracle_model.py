@@ -39,7 +39,7 @@ def _run_incremental(w, tokens_bt, rng, extra_blocks=3):
     perm = rng.permutation(nb)
     bt = perm[: b_n * need].reshape(b_n, need).astype(np.int32)
     kp = [np.full((nb, CFG.n_kv_heads, BS, CFG.head_dim), np.nan, np.float16) for _ in range(CFG.n_layers)]
-    vp = [np.full((nb, CFG.n_kv_heads, CFG.head_dim, BS), np.nan, np.float16) for _ in range(CFG.n_layers)]
+    vp = [np.full((nb, CFG.n_kv_heads, BS, CFG.head_dim), np.nan, np.float16) for _ in range(CFG.n_layers)]
     out = []
     for t in range(t_n):
         lens = np.full(b_n, t + 1, np.int32)
@@ -142,7 +142,7 @@ def test_argmax_lowest_index_on_ties():
 
 def _empty_pools(nb):
     kp = [np.full((nb, CFG.n_kv_heads, BS, CFG.head_dim), np.nan, np.float16) for _ in range(CFG.n_layers)]
-    vp = [np.full((nb, CFG.n_kv_heads, CFG.head_dim, BS), np.nan, np.float16) for _ in range(CFG.n_layers)]
+    vp = [np.full((nb, CFG.n_kv_heads, BS, CFG.head_dim), np.nan, np.float16) for _ in range(CFG.n_layers)]
     return kp, vp
 
 
@@ -174,7 +174,7 @@ def test_prefill_equals_causal_forward():
         for li in range(CFG.n_layers):
             np.testing.assert_allclose(kp[li][bt[s][t // BS], :, t % BS, :].astype(np.float64),
                                        ks[li].astype(np.float64), atol=2e-3, rtol=2e-3)
-            np.testing.assert_allclose(vp[li][bt[s][t // BS], :, :, t % BS].astype(np.float64),
+            np.testing.assert_allclose(vp[li][bt[s][t // BS], :, t % BS, :].astype(np.float64),
                                        vs[li].astype(np.float64), atol=2e-3, rtol=2e-3)
 
 
