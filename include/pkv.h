@@ -234,6 +234,21 @@ pkv_status pkv_model_create(const pkv_model_desc* desc, const void* embed,
                             const void* w_lm_head, pkv_model** out);
 void pkv_model_destroy(pkv_model* model);
 
+/* Model options (host only; take effect for steps enqueued or captured later):
+ *   PKV_OPT_PERSISTENT_BATCH1 (default 0): with 1, a decode step of batch 1
+ *   runs all layers in one persistent kernel (a grid of resident workgroups
+ *   walks the five fused ops of every layer with a grid-wide barrier between
+ *   them; the rvLLM post's optimisation history: fewer launches, cross-layer
+ *   fusion) when the model's shapes fit it (head_dim 128 and the batch-1
+ *   projection plans of the 1.5B / 7B-class shapes); otherwise, or with 0,
+ *   one kernel per fused op.  Both give the same bits.  Off by default because
+ *   on an MI355X it is the slower of the two (1.5B shape: 1.90 against
+ *   1.01 ms per step; 7B: 4.40 against 2.82 ms): its phases read the
+ *   activations with L2-bypassing loads and run at two workgroups per CU.
+ * PKV_E_ARG for an unknown option or value. */
+enum { PKV_OPT_PERSISTENT_BATCH1 = 0 };
+pkv_status pkv_model_set_option(pkv_model* model, int option, int value);
+
 /* Scratch bytes decode_layer / decode_step / graph_capture need (host only):
  * the per-step buffers of the fused layer (rvLLM post, section "퓨즈드 CUDA
  * 커널": q, the attention output and the SiLU*mul activation), the split-K

@@ -169,6 +169,11 @@ class Model:
                                      _p(weights["w_final_norm"]), _p(weights["w_lm_head"]), C.byref(h)))
         self.handle = h
 
+    def set_persistent_batch1(self, enable):
+        """Run batch-1 decode steps as one persistent kernel (default) or one
+        kernel per fused op (both give the same bits)."""
+        _check(_lib.pkv_model_set_option(self.handle, 0, 1 if enable else 0))
+
     def close(self, _destroy=_destroy):
         _destroy("pkv_model_destroy", self)
 

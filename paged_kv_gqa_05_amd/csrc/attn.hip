@@ -46,341 +46,14 @@
 //    conversion instruction (exact: every E4M3 value is an f16 value); the
 //    per-tensor K scale is folded into the score scale and the V scale into
 //    the output.
-#include "coherent.h"
-#include "pkv_internal.h"
+#include "attn_body.h"
 
 namespace pkv {
 namespace {
 
-typedef _Float16 h16;
-typedef h16 h16x8 __attribute__((ext_vector_type(8)));
-typedef h16 h16x4 __attribute__((ext_vector_type(4)));
-typedef h16 h16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLn2 = 0.69314718055994531f;
-constexpr float kLog2e = 1.44269504088896341f;
-// Partitions the merge reads per round trip.
-constexpr int kMergeBatch = 8;
-
-struct SplitParams {
-  const unsigned char* k_pool;
-  const unsigned char* v_pool;
-  const h16* q;
-  h16* out;
-  float* lse;
-  const int* bt;
-  const int* lens;
-  int* counters;   // [B][Hkv] partitions arrived (zero between calls)
-  float2* ws_ml;   // [B][Hq][P] (max, sum) per partition
-  float* ws_o;     // [B][Hq][P][D] unnormalised O per partition
-  int bt_stride;
-  int batch, hq, hkv, group, part, n_parts_max;
-  float scale_log2;  // softmax scale * log2(e) * K dequant scale
-  float v_scale;     // V dequant scale (1 for f16)
-};
-
-// Two E4M3 codes (low or high 16 bits of w) -> two f16, exactly.
-template <bool HI>
-__device__ __forceinline__ h16x2 e4m3x2_to_h16x2(int w) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
-}
-
-__device__ __forceinline__ h16x4 e4m3x4_to_h16x4(int w) {
-  const h16x2 a = e4m3x2_to_h16x2<false>(w), b = e4m3x2_to_h16x2<true>(w);
-  return h16x4{a[0], a[1], b[0], b[1]};
-}
-
-__device__ __forceinline__ h16x8 e4m3x8_to_h16x8(int lo, int hi) {
-  const h16x4 a = e4m3x4_to_h16x4(lo), b = e4m3x4_to_h16x4(hi);
-  return h16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// The 8-dim chunk that lane group q4 feeds at QK step s (D/32 steps).  f16 K
-// is stored as [D/8][16 tokens][8 dims]: step s reads chunks 4s..4s+3.  fp8 K
-// is stored as [D/16][16 tokens][16 dims]: one 16-byte load covers steps 2u and
-// 2u+1, i.e. chunks 8u + 2 q4 and 8u + 2 q4 + 1.
-template <bool FP8>
-__device__ __forceinline__ int q_chunk(int s, int q4) {
-  return FP8 ? 8 * (s >> 1) + 2 * q4 + (s & 1) : 4 * s + q4;
-}
-
-// Registers of one 16-token block for one lane (n = token of the K rows and
-// dim-in-group of the V rows, q4 = lane group).
-template <int D, bool FP8>
-struct Tile;
-
-template <int D>
-struct Tile<D, false> {
-  h16x8 k[D / 32];  // step s: token n, dims of chunk 4s + q4
-  h16x4 v[D / 16];  // V^T[dim 16j + n][tokens 4*q4 .. +4]
-  __device__ __forceinline__ void load_k(const SplitParams& p, int blk, int g, int lane) {
-    const size_t tile = (size_t)blk * p.hkv + g;
-    const h16* kp = reinterpret_cast<const h16*>(p.k_pool) + tile * kBlock * D + lane * 8;
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) k[s] = *reinterpret_cast<const h16x8*>(kp + s * 512);
-  }
-  __device__ __forceinline__ void load_v(const SplitParams& p, int blk, int g, int lane) {
-    const size_t tile = (size_t)blk * p.hkv + g;
-    const h16* vp = reinterpret_cast<const h16*>(p.v_pool) + tile * D * kBlock + (lane & 15) * kBlock +
-                    (lane >> 4) * 4;
-#pragma unroll
-    for (int j = 0; j < D / 16; ++j) v[j] = *reinterpret_cast<const h16x4*>(vp + j * 16 * kBlock);
-  }
-  __device__ __forceinline__ h16x8 kfrag(int s) const { return k[s]; }
-  __device__ __forceinline__ h16x4 vfrag(int j) const { return v[j]; }
-};
-
-template <int D>
-struct Tile<D, true> {
-  int4 k[D / 64];  // 16 codes: token n, dims 16 (4u + q4) .. +16 (steps 2u, 2u + 1)
-  int4 v[D / 64];  // 4 x 4 codes: V^T[dim 16j + n][tokens 4*q4 .. +4] for j = 4u .. 4u + 3
-  __device__ __forceinline__ void load_k(const SplitParams& p, int blk, int g, int lane) {
-    const size_t tile = (size_t)blk * p.hkv + g;
-    const unsigned char* kp = p.k_pool + tile * kBlock * D + lane * 16;
-#pragma unroll
-    for (int u = 0; u < D / 64; ++u) k[u] = *reinterpret_cast<const int4*>(kp + u * 1024);
-  }
-  __device__ __forceinline__ void load_v(const SplitParams& p, int blk, int g, int lane) {
-    const size_t tile = (size_t)blk * p.hkv + g;
-    const unsigned char* vp = p.v_pool + tile * D * kBlock + lane * 16;
-#pragma unroll
-    for (int u = 0; u < D / 64; ++u) v[u] = *reinterpret_cast<const int4*>(vp + u * 1024);
-  }
-  __device__ __forceinline__ h16x8 kfrag(int s) const {
-    const int4 w = k[s >> 1];
-    return (s & 1) ? e4m3x8_to_h16x8(w.z, w.w) : e4m3x8_to_h16x8(w.x, w.y);
-  }
-  __device__ __forceinline__ h16x4 vfrag(int j) const {
-    const int4 w = v[j >> 2];
-    const int r = j & 3;
-    return e4m3x4_to_h16x4(r == 0 ? w.x : r == 1 ? w.y : r == 2 ? w.z : w.w);
-  }
-};
-
-// Waves per SIMD each configuration is compiled for (register budget
-// 512 / n): 4 waves x NT <= 4 keeps three workgroups per CU resident, which
-// the plan's residency estimate relies on; the others hold one.
-template <int NT, int W>
-constexpr int attn_min_waves() {
-  return (W == 4 && NT <= 4) ? 3 : 1;
-}
-
 template <int D, bool FP8, int NT, int kWaves>
 __global__ void __launch_bounds__(64 * kWaves, (attn_min_waves<NT, kWaves>())) attn_kernel(SplitParams p) {
-  constexpr int kThreads = 64 * kWaves;
-  // padded LDS row (floats) for the combine of the four waves
-  constexpr int OSTR = D + 4;
-  __shared__ float s_o[kWaves][kMaxGroup][OSTR];
-  __shared__ float s_m[kWaves][kMaxGroup];
-  __shared__ float s_l[kWaves][kMaxGroup];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, q4 = lane >> 4;
-
-  // ---- this workgroup's (row, KV head, partition): blockIdx = (b * Hkv + g) * P + part
-  const int wg = blockIdx.x;
-  const int part_idx = wg % p.n_parts_max;
-  const int bg = wg / p.n_parts_max;
-  const int b = bg / p.hkv, g = bg - b * p.hkv;
-  const int tok0 = part_idx * p.part;
-  const int hbase = g * p.group;
-  // issued together, before the context length is known: the block-table
-  // entries of this wave's blocks (clamped inside the row) and the query rows
-  const int* btrow = p.bt + (size_t)b * p.bt_stride;
-  const int blk_l = btrow[min(tok0 / kBlock + wave + kWaves * min(lane, NT - 1), p.bt_stride - 1)];
-  h16x8 qf[D / 32];
-  {
-    const h16* qrow = p.q + ((size_t)b * p.hq + hbase + min(n, p.group - 1)) * D;
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) qf[s] = *reinterpret_cast<const h16x8*>(qrow + 8 * q_chunk<FP8>(s, q4));
-  }
-  const int c = p.lens[b];
-  if (tok0 >= c) {  // beyond the row's context (or an inactive row)
-    if (c == 0 && g == 0 && part_idx == 0) {
-      for (int idx = tid; idx < p.hq * D; idx += kThreads) p.out[(size_t)b * p.hq * D + idx] = (h16)0.f;
-      if (p.lse)
-        for (int h = tid; h < p.hq; h += kThreads) p.lse[(size_t)b * p.hq + h] = -INFINITY;
-    }
-    return;
-  }
-  if (n >= p.group) {
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) qf[s] = h16x8{0, 0, 0, 0, 0, 0, 0, 0};
-  }
-  const int np = (c + p.part - 1) / p.part;
-  const int tok_end = min(c, tok0 + p.part);
-  const int n_tiles = (tok_end - tok0 + kBlock - 1) / kBlock;
-  const int my_tiles = wave < n_tiles ? (n_tiles - wave + kWaves - 1) / kWaves : 0;  // <= NT
-
-  float m_w = -INFINITY, l_w = 0.f;  // this lane's head column (n), over the wave's tiles
-  f32x4 o[D / 16];
-#pragma unroll
-  for (int j = 0; j < D / 16; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (my_tiles > 0) {  // wave-uniform
-    // (1) every K and then every V block of this wave in flight at once (a
-    //     missing block re-reads the wave's last one, so the loads in flight
-    //     never depend on data and the compiler waits for exactly the ones it
-    //     uses); the scores start as soon as the K blocks land
-    Tile<D, FP8> tl[NT];
-    int blk[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) blk[t] = __shfl(blk_l, min(t, my_tiles - 1), 64);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) tl[t].load_k(p, blk[t], g, lane);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) tl[t].load_v(p, blk[t], g, lane);
-
-    // (2) scores S^T[token][head] of every block, in the log2 domain
-    float x[NT][4];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(tl[t].kfrag(s), qf[s], sacc, 0, 0, 0);
-      const int tb = tok0 + (wave + kWaves * t) * kBlock + 4 * q4;  // this lane's first token
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        x[t][rr] = (t < my_tiles && tb + rr < tok_end) ? sacc[rr] * p.scale_log2 : -INFINITY;
-    }
-    // (3) one max per head over the wave's tokens (in-lane, then the 4 lane groups)
-    float mt = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) mt = fmaxf(mt, fmaxf(fmaxf(x[t][0], x[t][1]), fmaxf(x[t][2], x[t][3])));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    m_w = mt;
-    // (4) P = exp2(S - m) and O^T += V^T P^T, no rescaling
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (t < my_tiles) {
-        float pr[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) pr[rr] = __builtin_amdgcn_exp2f(x[t][rr] - mt);
-        l_w += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        const h16x4 pf = h16x4{(h16)pr[0], (h16)pr[1], (h16)pr[2], (h16)pr[3]};
-        const int tb = tok0 + (wave + kWaves * t) * kBlock + 4 * q4;
-        if (tok0 + (wave + kWaves * t + 1) * kBlock > tok_end) {
-          // the row's last, partial block: slots past the context may hold
-          // anything (NaN included), so zero them before the product
-#pragma unroll
-          for (int j = 0; j < D / 16; ++j) {
-            h16x4 vf = tl[t].vfrag(j);
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-              if (tb + rr >= tok_end) vf[rr] = (h16)0.f;
-            o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, pf, o[j], 0, 0, 0);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < D / 16; ++j)
-            o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(tl[t].vfrag(j), pf, o[j], 0, 0, 0);
-        }
-      }
-    }
-  }
-
-  // ---- combine the four lane groups' sums, then the four waves
-  l_w += __shfl_xor(l_w, 16, 64);
-  l_w += __shfl_xor(l_w, 32, 64);
-#pragma unroll
-  for (int j = 0; j < D / 16; ++j)
-    *reinterpret_cast<f32x4*>(&s_o[wave][n][16 * j + 4 * q4]) = o[j];
-  if (q4 == 0) {
-    s_m[wave][n] = m_w;
-    s_l[wave][n] = l_w;
-  }
-  __syncthreads();
-
-  const size_t bh0 = (size_t)b * p.hq + hbase;
-  if (np == 1) {
-    for (int idx = tid; idx < p.group * D; idx += kThreads) {
-      const int h = idx / D, d = idx - h * D;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, s_m[w][h]);
-      float L = 0.f, O = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float e = __builtin_amdgcn_exp2f(s_m[w][h] - mx);  // 0 for a wave without tokens
-        L += s_l[w][h] * e;
-        O += s_o[w][h][d] * e;
-      }
-      p.out[(bh0 + h) * D + d] = (h16)(O * p.v_scale / L);
-      if (d == 0 && p.lse) p.lse[bh0 + h] = (mx + __log2f(L)) * kLn2;
-    }
-    return;
-  }
-
-  // ---- this partition's (max, sum, O) per head, four dims per thread
-  for (int idx = tid; idx < p.group * (D / 4); idx += kThreads) {
-    const int h = idx / (D / 4), d = 4 * (idx - h * (D / 4));
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, s_m[w][h]);
-    float L = 0.f;
-    f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float e = __builtin_amdgcn_exp2f(s_m[w][h] - mx);
-      L += s_l[w][h] * e;
-      O += *reinterpret_cast<const f32x4*>(&s_o[w][h][d]) * e;
-    }
-    const size_t slot = (bh0 + h) * p.n_parts_max + part_idx;
-    st_agent(p.ws_o + slot * D + d, O * p.v_scale);
-    if (d == 0) st_agent2(p.ws_ml + slot, make_float2(mx, L));
-  }
-  wait_vmcnt<0>();  // this thread's partial has reached the coherent level
-  __shared__ int s_last;
-  __syncthreads();
-  if (tid == 0)
-    s_last = __hip_atomic_fetch_add(p.counters + bg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
-  __syncthreads();
-  if (!s_last) return;
-
-  // ---- last partition of the row to finish: merge all np in partition order
-  if (tid == 0) __hip_atomic_store(p.counters + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (int idx = tid; idx < p.group * (D / 4); idx += kThreads) {
-    const int h = idx / (D / 4), d = 4 * (idx - h * (D / 4));
-    const size_t base = (bh0 + h) * p.n_parts_max;
-    float M = -INFINITY, L = 0.f;
-    f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int i0 = 0; i0 < np; i0 += kMergeBatch) {
-      // the (max, sum) and O of kMergeBatch partitions in flight together
-      float2 ml[kMergeBatch];
-      f32x4 po[kMergeBatch];
-#pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        const size_t slot = base + min(i0 + u, np - 1);
-        ml[u] = ld_agent2(p.ws_ml + slot);
-        po[u] = ld_agent(p.ws_o + slot * D + d);
-      }
-      float mn = M;
-#pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u)
-        if (i0 + u < np) mn = fmaxf(mn, ml[u].x);
-      const float r = __builtin_amdgcn_exp2f(M - mn);  // 0 on the first batch (M = -inf)
-      L *= r;
-      O *= r;
-#pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        if (i0 + u < np) {
-          const float e = __builtin_amdgcn_exp2f(ml[u].x - mn);
-          L += ml[u].y * e;
-          O += po[u] * e;
-        }
-      }
-      M = mn;
-    }
-    const float inv = 1.0f / L;
-    h16* o = p.out + (bh0 + h) * D + d;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) o[v] = (h16)(O[v] * inv);
-    if (d == 0 && p.lse) p.lse[bh0 + h] = (M + __log2f(L)) * kLn2;
-  }
+  attn_body<D, FP8, NT, kWaves, false>(p, blockIdx.x);
 }
 
 template <int D, bool FP8, int NT, int W>
@@ -428,7 +101,9 @@ AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int 
   auto wgs = [&](int w, int nt) { return rows * ceil_div(mc, 16 * nt * w); };
   (void)elt_bytes;
   int waves = 4, nt = 8;
-  if (mc > 512 && wgs(8, 8) <= 256) {
+  // (at most 16 rows: 4-wave partitions, which the persistent batch-1 step
+  // also runs; 8-wave ones would leave it)
+  if (mc > 512 && wgs(8, 8) <= 256 && rows > 16) {
     waves = 8;
   } else {
     if (wgs(4, 8) > 256 && wgs(4, 4) <= 768) nt = 4;
@@ -452,29 +127,7 @@ AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int 
 }
 
 hipError_t launch_paged_attention(const AttnArgs& a, const AttnPlan& plan, hipStream_t s) {
-  SplitParams sp{};
-  sp.k_pool = static_cast<const unsigned char*>(a.k_pool);
-  sp.v_pool = static_cast<const unsigned char*>(a.v_pool);
-  sp.q = static_cast<const h16*>(a.q);
-  sp.out = static_cast<h16*>(a.out);
-  sp.lse = a.lse;
-  sp.bt = a.bt;
-  sp.lens = a.lens;
-  sp.bt_stride = a.bt_stride;
-  sp.batch = a.batch;
-  sp.hq = a.hq;
-  sp.hkv = a.hkv;
-  sp.group = a.hq / a.hkv;
-  sp.part = plan.part;
-  sp.n_parts_max = plan.n_parts_max;
-  sp.scale_log2 = a.scale * kLog2e * (a.fp8 ? a.k_scale : 1.0f);
-  sp.v_scale = a.fp8 ? a.v_scale : 1.0f;
-  const size_t ml = align_up((size_t)a.batch * a.hq * plan.n_parts_max * sizeof(float2), 256);
-  char* ws = static_cast<char*>(a.ws);
-  const size_t cr = a.counter_region ? a.counter_region : plan.counter_bytes;
-  sp.counters = reinterpret_cast<int*>(ws);
-  sp.ws_ml = reinterpret_cast<float2*>(ws + cr);
-  sp.ws_o = reinterpret_cast<float*>(ws + cr + ml);
+  const SplitParams sp = make_split_params(a, plan);
   if (a.head_dim == 128) return a.fp8 ? launch_impl<128, true>(sp, plan, s) : launch_impl<128, false>(sp, plan, s);
   return a.fp8 ? launch_impl<64, true>(sp, plan, s) : launch_impl<64, false>(sp, plan, s);
 }

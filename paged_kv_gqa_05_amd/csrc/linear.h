@@ -1,6 +1,7 @@
 // Fused projection launchers shared by the decode layer and the LM head.
 #pragma once
 
+#include "coherent.h"
 #include "kvstore.h"
 #include "pkv_internal.h"
 
@@ -68,7 +69,9 @@ __device__ __forceinline__ float2 rope_cs(const RopeArgs& ra, const RopeRow& r, 
 }
 // Pair p of batch row m: y0, y1 are rows i and i + D/2 of a head with the
 // norm and the bias applied.  Rotates q and k heads at the row's position,
-// writes q, and stores the new token's k and v in the paged cache.
+// writes q, and stores the new token's k and v in the paged cache.  COH: q is
+// written with agent-scope stores (read by other XCDs in the same kernel).
+template <bool COH = false>
 __device__ __forceinline__ void rope_put(const RopeArgs& ra, const RopeRow& r, int m, int p, float y0, float y1,
                                          float2 cs) {
   const int half = ra.d >> 1;
@@ -78,8 +81,13 @@ __device__ __forceinline__ void rope_put(const RopeArgs& ra, const RopeRow& r, i
     const float o1 = y1 * cs.x + y0 * cs.y;
     if (head < ra.hq) {
       _Float16* q = ra.q_out + ((size_t)m * ra.hq + head) * ra.d;
-      q[i] = (_Float16)o0;
-      q[half + i] = (_Float16)o1;
+      if constexpr (COH) {
+        st_agent_h(q + i, (_Float16)o0);
+        st_agent_h(q + half + i, (_Float16)o1);
+      } else {
+        q[i] = (_Float16)o0;
+        q[half + i] = (_Float16)o1;
+      }
     } else if (r.c > 0) {
       const size_t tile = ((size_t)r.blk * ra.hkv + (head - ra.hq)) * 16 * ra.d;
       const int t = r.pos % 16;
@@ -99,16 +107,6 @@ __device__ __forceinline__ float2 rope_bias(const RopeArgs& ra, const _Float16* 
   const int half = ra.d >> 1;
   const int head = p / half, i = p - head * half;
   return make_float2((float)bias[head * ra.d + i], (float)bias[head * ra.d + half + i]);
-}
-
-// All three steps for one pair (y0, y1 with the norm applied, bias not yet).
-__device__ __forceinline__ void rope_store(const RopeArgs& ra, const _Float16* bias, int m, int p, float y0,
-                                           float y1) {
-  RopeRow r = rope_row_len(ra, m);
-  rope_row_blk(ra, m, r);
-  const float2 cs = rope_cs(ra, r, p);
-  const float2 b = rope_bias(ra, bias, p);
-  rope_put(ra, r, m, p, y0 + b.x, y1 + b.y, cs);
 }
 
 // Batches at or above this size use the MFMA GEMM; smaller ones the GEMV.
@@ -166,6 +164,36 @@ size_t linear_ws_bytes(int M, int n_out, int K, int epi);
 // GEMV below kMfmaMinBatch rows, MFMA GEMM above.  part_ws / counters:
 // scratch of linear_ws_bytes and kGemmMaxCounters zeroed ints.
 hipError_t launch_linear(const LinArgs& a, int epi, void* part_ws, int* counters, hipStream_t s);
+
+// The GEMV configuration (batch < 32) of an n_out x K projection: lanes per
+// output row and chunk steps per lane iteration (the batch-1 bucket).
+int gemv_lanes_per_row(int n_out, int K);
+void gemv_config(int n_out, int K, int* lanes_per_row, int* steps_per_iter);
+
+// ------------------------------------------------- persistent batch-1 layers
+
+// One layer's weight pointers, kept in device memory for the persistent kernel.
+struct PersistLayer {
+  const _Float16 *w_in, *w_qkv, *b_qkv, *w_o, *w_post, *w_gu, *w_down;
+};
+
+// Every layer of a batch-1 decode step in one persistent kernel (persist.hip).
+struct PersistArgs {
+  LinArgs qkv, o, gu, down;    // arguments of layer 0 (weights are replaced per layer)
+  AttnArgs attn;               // attention of layer 0 (pools and scales replaced per layer)
+  AttnPlan plan;
+  const PersistLayer* layers;  // device [n_layers]
+  size_t pool_stride;          // bytes from one layer's K pool to the next layer's
+  size_t v_off;                // bytes from a layer's K pool to its V pool
+  const float* k_scales;       // (host) [n_layers], fp8 caches only
+  const float* v_scales;
+  int n_layers;
+  unsigned* barrier;           // 2240 words zero before the launch (word 0 is set
+                               // if a barrier timed out)
+};
+// Whether the shapes fit the kernel's body variants (and the grid can be resident).
+bool persistent_config(const PersistArgs& a, int* cfg_hidden, int* cfg_gu);
+hipError_t launch_persistent_layers(const PersistArgs& a, hipStream_t s);
 
 // Zero n ints on the stream with a kernel (graph-capturable, no memset node).
 hipError_t launch_zero_i32(int* p, int n, hipStream_t s);

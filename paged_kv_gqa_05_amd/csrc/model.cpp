@@ -32,6 +32,8 @@ struct pkv_model {
   const void* w_final;
   const void* w_lm;
   void* rope;  // device float2 [max_positions][D/2]: (cos, sin)
+  void* layer_table = nullptr;  // device PersistLayer [num_layers] for the persistent batch-1 step
+  int persistent = 0;           // PKV_OPT_PERSISTENT_BATCH1
 };
 
 struct pkv_graph {
@@ -169,25 +171,20 @@ pkv_status check_step(const pkv_model* m, const pkv_cache* cache, const int32_t*
   return PKV_OK;
 }
 
-// One of the layer's five fused ops (PKV_OP_*).  pre (prefill only):
-// attention runs as the causal multi-token kernel over the new tokens'
-// sequences instead of one decode row per token.
-hipError_t run_layer_op(const pkv_model* m, pkv_cache* cache, int layer, int op, _Float16* h, const int32_t* bt,
-                        int bt_stride, const int32_t* lens, int batch, const StepBuffers& sb, const AttnPlan& plan,
-                        hipStream_t s, const PrefillAttnArgs* pre = nullptr) {
+// Arguments of fused op `op` (PKV_OP_QKV, _O, _GATE_UP, _DOWN) of a layer.
+LinArgs layer_lin_args(const pkv_model* m, const pkv_cache* cache, int layer, int op, _Float16* h,
+                       const int32_t* bt, int bt_stride, const int32_t* lens, int batch, const StepBuffers& sb) {
   const pkv_model_desc& d = m->d;
   const pkv_layer_weights& w = m->layers[layer];
   const int qkv_n = (d.num_q_heads + 2 * d.num_kv_heads) * d.head_dim;
   const int qd = d.num_q_heads * d.head_dim;
-  void* kp = cache->k_pool(layer);
-  void* vp = cache->v_pool(layer);
   const bool fp8 = cache->desc.dtype == PKV_KV_FP8_E4M3;
-  const float ks = fp8 ? cache->k_scales[layer] : 1.f, vs = fp8 ? cache->v_scales[layer] : 1.f;
   LinArgs a{};
   a.eps = d.rms_eps;
+  a.M = batch;
   switch (op) {
-    case PKV_OP_QKV: {  // RMSNorm + QKV (+ bias) + RoPE; q out, k and v of the new token into the cache
-      a.A = h; a.lda = d.hidden; a.K = d.hidden; a.M = batch;
+    case PKV_OP_QKV:  // RMSNorm + QKV (+ bias) + RoPE; q out, k and v of the new token into the cache
+      a.A = h; a.lda = d.hidden; a.K = d.hidden;
       a.W = static_cast<const _Float16*>(w.w_qkv);
       a.gain = static_cast<const _Float16*>(w.w_in); a.norm = 1;
       a.bias = static_cast<const _Float16*>(w.b_qkv);
@@ -195,45 +192,89 @@ hipError_t run_layer_op(const pkv_model* m, pkv_cache* cache, int layer, int op,
       a.rope.cos_sin = static_cast<const float2*>(m->rope);
       a.rope.lens = lens; a.rope.bt = bt; a.rope.bt_stride = bt_stride;
       a.rope.q_out = sb.q;
-      a.rope.k_pool = kp; a.rope.v_pool = vp;
+      a.rope.k_pool = cache->k_pool(layer); a.rope.v_pool = cache->v_pool(layer);
       a.rope.hq = d.num_q_heads; a.rope.hkv = d.num_kv_heads; a.rope.d = d.head_dim;
-      a.rope.fp8 = fp8; a.rope.k_scale = ks; a.rope.v_scale = vs;
-      return launch_linear(a, EPI_ROPE, sb.gemm_ws, sb.counters, s);
-    }
-    case PKV_OP_ATTN: {  // paged attention
-      if (pre) {
-        PrefillAttnArgs pa = *pre;
-        pa.k_pool = kp; pa.v_pool = vp; pa.q = sb.q; pa.out = sb.o;
-        pa.hq = d.num_q_heads; pa.hkv = d.num_kv_heads; pa.head_dim = d.head_dim; pa.fp8 = fp8;
-        pa.scale = 1.0f / std::sqrt((float)d.head_dim); pa.k_scale = ks; pa.v_scale = vs;
-        return launch_prefill_attention(pa, s);
-      }
-      AttnArgs at{};
-      at.k_pool = kp; at.v_pool = vp; at.q = sb.q; at.out = sb.o; at.lse = nullptr;
-      at.bt = bt; at.bt_stride = bt_stride; at.lens = lens; at.batch = batch;
-      at.hq = d.num_q_heads; at.hkv = d.num_kv_heads; at.head_dim = d.head_dim; at.fp8 = fp8;
-      at.scale = 1.0f / std::sqrt((float)d.head_dim); at.k_scale = ks; at.v_scale = vs; at.ws = sb.attn_ws;
-      return launch_paged_attention(at, plan, s);
-    }
+      a.rope.fp8 = fp8;
+      a.rope.k_scale = fp8 ? cache->k_scales[layer] : 1.f;
+      a.rope.v_scale = fp8 ? cache->v_scales[layer] : 1.f;
+      break;
     case PKV_OP_O:  // O projection + residual add
-      a.A = sb.o; a.lda = qd; a.K = qd; a.M = batch;
+      a.A = sb.o; a.lda = qd; a.K = qd;
       a.W = static_cast<const _Float16*>(w.w_o);
       a.out = h; a.ldo = d.hidden; a.n_out = d.hidden;
-      return launch_linear(a, EPI_RESID, sb.gemm_ws, sb.counters, s);
+      break;
     case PKV_OP_GATE_UP:  // RMSNorm + gate/up + SiLU*mul -> act
-      a.A = h; a.lda = d.hidden; a.K = d.hidden; a.M = batch;
+      a.A = h; a.lda = d.hidden; a.K = d.hidden;
       a.W = static_cast<const _Float16*>(w.w_gate_up);
       a.gain = static_cast<const _Float16*>(w.w_post); a.norm = 1;
       a.out = sb.act; a.ldo = d.ffn; a.n_out = d.ffn;
-      return launch_linear(a, EPI_SILU, sb.gemm_ws, sb.counters, s);
-    case PKV_OP_DOWN:  // down projection + residual add
-      a.A = sb.act; a.lda = d.ffn; a.K = d.ffn; a.M = batch;
+      break;
+    default:  // PKV_OP_DOWN: down projection + residual add
+      a.A = sb.act; a.lda = d.ffn; a.K = d.ffn;
       a.W = static_cast<const _Float16*>(w.w_down);
       a.out = h; a.ldo = d.hidden; a.n_out = d.hidden;
-      return launch_linear(a, EPI_RESID, sb.gemm_ws, sb.counters, s);
-    default:
-      return hipErrorInvalidValue;
+      break;
   }
+  return a;
+}
+
+AttnArgs layer_attn_args(const pkv_model* m, const pkv_cache* cache, int layer, const int32_t* bt, int bt_stride,
+                         const int32_t* lens, int batch, const StepBuffers& sb) {
+  const pkv_model_desc& d = m->d;
+  const bool fp8 = cache->desc.dtype == PKV_KV_FP8_E4M3;
+  AttnArgs at{};
+  at.k_pool = cache->k_pool(layer); at.v_pool = cache->v_pool(layer); at.q = sb.q; at.out = sb.o; at.lse = nullptr;
+  at.bt = bt; at.bt_stride = bt_stride; at.lens = lens; at.batch = batch;
+  at.hq = d.num_q_heads; at.hkv = d.num_kv_heads; at.head_dim = d.head_dim; at.fp8 = fp8;
+  at.scale = 1.0f / std::sqrt((float)d.head_dim);
+  at.k_scale = fp8 ? cache->k_scales[layer] : 1.f;
+  at.v_scale = fp8 ? cache->v_scales[layer] : 1.f;
+  at.ws = sb.attn_ws;
+  return at;
+}
+
+// One of the layer's five fused ops (PKV_OP_*).  pre (prefill only):
+// attention runs as the causal multi-token kernel over the new tokens'
+// sequences instead of one decode row per token.
+hipError_t run_layer_op(const pkv_model* m, pkv_cache* cache, int layer, int op, _Float16* h, const int32_t* bt,
+                        int bt_stride, const int32_t* lens, int batch, const StepBuffers& sb, const AttnPlan& plan,
+                        hipStream_t s, const PrefillAttnArgs* pre = nullptr) {
+  static const int kEpi[5] = {EPI_ROPE, -1, EPI_RESID, EPI_SILU, EPI_RESID};
+  if (op < PKV_OP_QKV || op > PKV_OP_DOWN) return hipErrorInvalidValue;
+  if (op != PKV_OP_ATTN)
+    return launch_linear(layer_lin_args(m, cache, layer, op, h, bt, bt_stride, lens, batch, sb), kEpi[op],
+                         sb.gemm_ws, sb.counters, s);
+  const AttnArgs at = layer_attn_args(m, cache, layer, bt, bt_stride, lens, batch, sb);
+  if (pre) {
+    PrefillAttnArgs pa = *pre;
+    pa.k_pool = at.k_pool; pa.v_pool = at.v_pool; pa.q = sb.q; pa.out = sb.o;
+    pa.hq = at.hq; pa.hkv = at.hkv; pa.head_dim = at.head_dim; pa.fp8 = at.fp8;
+    pa.scale = at.scale; pa.k_scale = at.k_scale; pa.v_scale = at.v_scale;
+    return launch_prefill_attention(pa, s);
+  }
+  return launch_paged_attention(at, plan, s);
+}
+
+// The batch-1 step's layers as one persistent kernel when the shapes fit its
+// variants and the model allows it (false: run the per-op kernels).
+bool persistent_args(const pkv_model* m, pkv_cache* cache, _Float16* h, const int32_t* bt, int bt_stride,
+                     const int32_t* lens, int batch, const StepBuffers& sb, const AttnPlan& plan, PersistArgs* pa) {
+  if (batch != 1 || !m->persistent || !m->layer_table) return false;
+  pa->qkv = layer_lin_args(m, cache, 0, PKV_OP_QKV, h, bt, bt_stride, lens, batch, sb);
+  pa->o = layer_lin_args(m, cache, 0, PKV_OP_O, h, bt, bt_stride, lens, batch, sb);
+  pa->gu = layer_lin_args(m, cache, 0, PKV_OP_GATE_UP, h, bt, bt_stride, lens, batch, sb);
+  pa->down = layer_lin_args(m, cache, 0, PKV_OP_DOWN, h, bt, bt_stride, lens, batch, sb);
+  pa->attn = layer_attn_args(m, cache, 0, bt, bt_stride, lens, batch, sb);
+  pa->plan = plan;
+  pa->layers = static_cast<const PersistLayer*>(m->layer_table);
+  pa->pool_stride = 2 * cache->pool_bytes;
+  pa->v_off = cache->pool_bytes;
+  pa->k_scales = cache->k_scales.empty() ? nullptr : cache->k_scales.data();
+  pa->v_scales = cache->v_scales.empty() ? nullptr : cache->v_scales.data();
+  pa->n_layers = m->d.num_layers;
+  pa->barrier = reinterpret_cast<unsigned*>(sb.counters);  // split-K counters: unused by the batch-1 GEMV
+  int c1 = 0, c2 = 0;
+  return persistent_config(*pa, &c1, &c2);
 }
 
 hipError_t run_layer(const pkv_model* m, pkv_cache* cache, int layer, _Float16* h, const int32_t* bt,
@@ -252,9 +293,15 @@ hipError_t run_step(const pkv_model* m, pkv_cache* cache, const int32_t* tokens,
   const pkv_model_desc& d = m->d;
   hipError_t e = launch_embed(m->embed, tokens, h, batch, d.hidden, sb.counters, sb.n_counters, s);
   if (e != hipSuccess) return e;
-  for (int l = 0; l < d.num_layers; ++l) {
-    e = run_layer(m, cache, l, h, bt, bt_stride, lens, batch, sb, plan, s);
+  PersistArgs pa{};
+  if (persistent_args(m, cache, h, bt, bt_stride, lens, batch, sb, plan, &pa)) {
+    e = launch_persistent_layers(pa, s);
     if (e != hipSuccess) return e;
+  } else {
+    for (int l = 0; l < d.num_layers; ++l) {
+      e = run_layer(m, cache, l, h, bt, bt_stride, lens, batch, sb, plan, s);
+      if (e != hipSuccess) return e;
+    }
   }
   LinArgs a{};
   a.eps = d.rms_eps;
@@ -318,6 +365,23 @@ pkv_status pkv_model_create(const pkv_model_desc* desc, const void* embed, const
     delete m;
     return hip_fail(e, "hipMemcpy(rope table)");
   }
+  // per-layer weight pointers for the persistent batch-1 step
+  std::vector<PersistLayer> lt(d.num_layers);
+  for (int l = 0; l < d.num_layers; ++l) {
+    const pkv_layer_weights& w = layers[l];
+    lt[l] = PersistLayer{static_cast<const _Float16*>(w.w_in), static_cast<const _Float16*>(w.w_qkv),
+                         static_cast<const _Float16*>(w.b_qkv), static_cast<const _Float16*>(w.w_o),
+                         static_cast<const _Float16*>(w.w_post), static_cast<const _Float16*>(w.w_gate_up),
+                         static_cast<const _Float16*>(w.w_down)};
+  }
+  e = hipMalloc(&m->layer_table, lt.size() * sizeof(PersistLayer));
+  if (e == hipSuccess) e = hipMemcpy(m->layer_table, lt.data(), lt.size() * sizeof(PersistLayer), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    if (m->layer_table) (void)hipFree(m->layer_table);
+    (void)hipFree(m->rope);
+    delete m;
+    return hip_fail(e, "layer table");
+  }
   *out = m;
   return PKV_OK;
 }
@@ -325,7 +389,16 @@ pkv_status pkv_model_create(const pkv_model_desc* desc, const void* embed, const
 void pkv_model_destroy(pkv_model* m) {
   if (!m) return;
   if (m->rope) (void)hipFree(m->rope);
+  if (m->layer_table) (void)hipFree(m->layer_table);
   delete m;
+}
+
+pkv_status pkv_model_set_option(pkv_model* m, int option, int value) {
+  if (!m) return fail(PKV_E_ARG, "model is NULL");
+  if (option != PKV_OPT_PERSISTENT_BATCH1) return fail(PKV_E_ARG, "unknown option");
+  if (value != 0 && value != 1) return fail(PKV_E_ARG, "value must be 0 or 1");
+  m->persistent = value;
+  return PKV_OK;
 }
 
 pkv_status pkv_step_workspace_bytes(const pkv_model* m, const pkv_cache* cache, int batch, int max_context,
