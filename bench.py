@@ -367,7 +367,7 @@ def time_sampling(pkv, torch, inp, batch, vocab, rounds, seed, mode):
             "logit_bytes": batch * vocab * 2}
 
 
-ATTN_SOURCES = ("attn.hip", "coherent.h", "pkv_internal.h")
+ATTN_SOURCES = ("attn.hip", "attn_body.h", "coherent.h", "pkv_internal.h")
 GEMM_SOURCES = ("gemm.hip", "linear.h", "linear.hip", "coherent.h", "kvstore.h", "pkv_internal.h")
 
 

@@ -94,8 +94,45 @@ def build_host_sanitized():
     return SAN_LIB
 
 
+# Measurement variants: the library with some sources compiled with extra
+# defines, linked with the other objects of build().  attn_qk_valu computes
+# the f16 attention scores with v_dot2 on the VALU instead of the 16x16x32
+# MFMA (libpkv_attn_qk_valu.so; select it with PKV_LIB_PATH), to time that
+# choice against the MFMA form.
+VARIANTS = {"attn_qk_valu": (("attn.hip", "persist.hip"), ["-DPKV_ATTN_QK_VALU"])}
+
+
+def build_variant(name):
+    files, defines = VARIANTS[name]
+    vobj = os.path.join(CSRC, "_obj_" + name)
+    os.makedirs(vobj, exist_ok=True)
+    objs = []
+    for src in sources():
+        base = os.path.basename(src)
+        if base in files:
+            obj = os.path.join(vobj, base + ".o")
+            cmd = [HIPCC, *FLAGS, *defines, "-x", "hip", "-c", src, "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed for {base} ({name}):\n" + r.stdout + r.stderr)
+        else:
+            obj = os.path.join(OBJ, base + ".o")
+            if not os.path.exists(obj):
+                raise RuntimeError(f"{obj} missing: run build() first")
+        objs.append(obj)
+    lib = os.path.join(HERE, f"libpkv_{name}.so")
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib + ".tmp", *objs],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(lib + ".tmp", lib)
+    return lib
+
+
 if __name__ == "__main__":
     if len(sys.argv) > 1 and sys.argv[1] == "--host-sanitized":
         print(build_host_sanitized())
+    elif len(sys.argv) > 2 and sys.argv[1] == "--variant":
+        print(build_variant(sys.argv[2]))
     else:
         print(build())

@@ -15,21 +15,26 @@
 //    workgroup waits one memory round trip before its KV loads.
 //  * Wave w of a partition owns its blocks w, w + W, ... (at most NT) and loads
 //    all of their K and V at once.  K blocks are stored in 16-byte chunks of
-//    8 dims x 16 tokens (fp8: 16 dims), so each K load instruction of a wave
-//    reads 1 KB of contiguous memory.  f16 V blocks are dim-major [D][16]
-//    (8-byte loads, 512 contiguous bytes per instruction); fp8 V blocks are
+//    8 dims x 16 tokens (fp8: 16 dims).  f16 V blocks are dim-major [D][16]
+//    (one 16-byte load gives a lane 8 tokens of one dim); fp8 V blocks are
 //    [D/64][4][16][4][4] (dim group, token quad, dim in group, dim step of
 //    16, token in quad), so one 16-byte load gives a lane its four
 //    token-quad fragments of dims n, n + 16, n + 32, n + 48 and a wave
 //    instruction reads 1 KB (1.16x faster than 4-byte loads at the long
 //    fp8 workload).
-//  * Scores: the K block feeds v_mfma_f32_16x16x32_f16 from registers as the A
+//  * Scores: K rows feed v_mfma_f32_16x16x32_f16 from registers as the A
 //    operand (token = MFMA row), the group's query rows (G <= 16, zero padded)
 //    are the B operand, giving S^T [token][head].  The dot product over D is
 //    taken in a permuted dim order (the same for q and K), which is what makes
-//    the K loads contiguous.  That C layout is exactly the B operand of
-//    v_mfma_f32_16x16x16f16 for O^T += V^T P^T, whose A operand comes straight
-//    from the V block registers: no LDS, no shuffles.
+//    the K loads contiguous.  f16 takes the wave's blocks in pairs and gives
+//    the two score products of a pair their K rows in a permuted token order,
+//    so that each lane's accumulators hold 8 consecutive tokens of one block:
+//    exactly the B operand of v_mfma_f32_16x16x32_f16 for O^T += V^T P^T,
+//    whose A operand is one 16-byte V load per lane (64 tile loads for a wave
+//    of 8 blocks, against 96 with 8-byte V loads and the 16x16x16 product).
+//    fp8 keeps one block per product: its accumulators are the B operand of
+//    v_mfma_f32_16x16x16f16, whose A operand comes from the V block's codes.
+//    No LDS and no shuffles between the two products either way.
 //  * Softmax per wave in two passes over registers: all scores first, one max
 //    per head, then P = exp2(S - max) and the PV products with no rescaling
 //    (an online softmax rescales the 32 output accumulators at every block,

@@ -179,70 +179,216 @@ __device__ __forceinline__ void attn_body(const SplitParams& p, const int wg) {
   const int n_tiles = (tok_end - tok0 + kBlock - 1) / kBlock;
   const int my_tiles = wave < n_tiles ? (n_tiles - wave + kWaves - 1) / kWaves : 0;  // <= NT
 
+#ifdef PKV_ATTN_QK_VALU
+  // measurement variant (build.py --variant attn_qk_valu): the f16 scores on
+  // the VALU, from the group's query rows in LDS
+  __shared__ h16 s_qv[16][D + 8];
+  __shared__ float s_sv[kWaves][2][16][17];
+  if (!FP8 && wave == 0) {
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) *reinterpret_cast<h16x8*>(&s_qv[n][8 * (4 * s + q4)]) = qf[s];
+  }
+  __syncthreads();
+#endif
   float m_w = -INFINITY, l_w = 0.f;  // this lane's head column (n), over the wave's tiles
   f32x4 o[D / 16];
 #pragma unroll
   for (int j = 0; j < D / 16; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (my_tiles > 0) {  // wave-uniform
-    // (1) every K and then every V block of this wave in flight at once (a
-    //     missing block re-reads the wave's last one, so the loads in flight
-    //     never depend on data and the compiler waits for exactly the ones it
-    //     uses); the scores start as soon as the K blocks land
-    Tile<D, FP8> tl[NT];
-    int blk[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) blk[t] = __shfl(blk_l, min(t, my_tiles - 1), 64);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) tl[t].load_k(p, blk[t], g, lane);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) tl[t].load_v(p, blk[t], g, lane);
+    if constexpr (FP8) {
+      // (1) every K and then every V block of this wave in flight at once (a
+      //     missing block re-reads the wave's last one, so the loads in flight
+      //     never depend on data and the compiler waits for exactly the ones it
+      //     uses); the scores start as soon as the K blocks land
+      Tile<D, FP8> tl[NT];
+      int blk[NT];
+  #pragma unroll
+      for (int t = 0; t < NT; ++t) blk[t] = __shfl(blk_l, min(t, my_tiles - 1), 64);
+  #pragma unroll
+      for (int t = 0; t < NT; ++t) tl[t].load_k(p, blk[t], g, lane);
+  #pragma unroll
+      for (int t = 0; t < NT; ++t) tl[t].load_v(p, blk[t], g, lane);
 
-    // (2) scores S^T[token][head] of every block, in the log2 domain
-    float x[NT][4];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(tl[t].kfrag(s), qf[s], sacc, 0, 0, 0);
-      const int tb = tok0 + (wave + kWaves * t) * kBlock + 4 * q4;  // this lane's first token
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        x[t][rr] = (t < my_tiles && tb + rr < tok_end) ? sacc[rr] * p.scale_log2 : -INFINITY;
-    }
-    // (3) one max per head over the wave's tokens (in-lane, then the 4 lane groups)
-    float mt = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) mt = fmaxf(mt, fmaxf(fmaxf(x[t][0], x[t][1]), fmaxf(x[t][2], x[t][3])));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    m_w = mt;
-    // (4) P = exp2(S - m) and O^T += V^T P^T, no rescaling
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (t < my_tiles) {
-        float pr[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) pr[rr] = __builtin_amdgcn_exp2f(x[t][rr] - mt);
-        l_w += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        const h16x4 pf = h16x4{(h16)pr[0], (h16)pr[1], (h16)pr[2], (h16)pr[3]};
-        const int tb = tok0 + (wave + kWaves * t) * kBlock + 4 * q4;
-        if (tok0 + (wave + kWaves * t + 1) * kBlock > tok_end) {
-          // the row's last, partial block: slots past the context may hold
-          // anything (NaN included), so zero them before the product
-#pragma unroll
-          for (int j = 0; j < D / 16; ++j) {
-            h16x4 vf = tl[t].vfrag(j);
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-              if (tb + rr >= tok_end) vf[rr] = (h16)0.f;
-            o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, pf, o[j], 0, 0, 0);
+      // (2) scores S^T[token][head] of every block, in the log2 domain
+      float x[NT][4];
+  #pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int s = 0; s < D / 32; ++s)
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(tl[t].kfrag(s), qf[s], sacc, 0, 0, 0);
+        const int tb = tok0 + (wave + kWaves * t) * kBlock + 4 * q4;  // this lane's first token
+  #pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          x[t][rr] = (t < my_tiles && tb + rr < tok_end) ? sacc[rr] * p.scale_log2 : -INFINITY;
+      }
+      // (3) one max per head over the wave's tokens (in-lane, then the 4 lane groups)
+      float mt = -INFINITY;
+  #pragma unroll
+      for (int t = 0; t < NT; ++t) mt = fmaxf(mt, fmaxf(fmaxf(x[t][0], x[t][1]), fmaxf(x[t][2], x[t][3])));
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      m_w = mt;
+      // (4) P = exp2(S - m) and O^T += V^T P^T, no rescaling
+  #pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t < my_tiles) {
+          float pr[4];
+  #pragma unroll
+          for (int rr = 0; rr < 4; ++rr) pr[rr] = __builtin_amdgcn_exp2f(x[t][rr] - mt);
+          l_w += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+          const h16x4 pf = h16x4{(h16)pr[0], (h16)pr[1], (h16)pr[2], (h16)pr[3]};
+          const int tb = tok0 + (wave + kWaves * t) * kBlock + 4 * q4;
+          if (tok0 + (wave + kWaves * t + 1) * kBlock > tok_end) {
+            // the row's last, partial block: slots past the context may hold
+            // anything (NaN included), so zero them before the product
+  #pragma unroll
+            for (int j = 0; j < D / 16; ++j) {
+              h16x4 vf = tl[t].vfrag(j);
+  #pragma unroll
+              for (int rr = 0; rr < 4; ++rr)
+                if (tb + rr >= tok_end) vf[rr] = (h16)0.f;
+              o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, pf, o[j], 0, 0, 0);
+            }
+          } else {
+  #pragma unroll
+            for (int j = 0; j < D / 16; ++j)
+              o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(tl[t].vfrag(j), pf, o[j], 0, 0, 0);
           }
-        } else {
+        }
+      }
+    } else {
+      // f16: the wave's blocks in pairs (X, Y) = (t, t + 1).  The two score
+      //     products of a pair take their 16 K rows in a permuted token order:
+      //     row 4G + i of product A is token 8G + i of the pair (tokens 0-15
+      //     of X, then 16-31 of Y) and row 4G + i of product B is token
+      //     8G + 4 + i.  Lane group G then holds the scores of 8 consecutive
+      //     tokens of one block, which is the k range it feeds as the B
+      //     operand of v_mfma_f32_16x16x32_f16 for O^T += V^T P^T; the A
+      //     operand is one 16-byte load of the dim-major V block per lane and
+      //     16 dims.  No shuffles, and half the V load instructions of the
+      //     16x16x16 product: a wave of 8 blocks issues 64 tile loads.
+      constexpr int NP = NT / 2;
+      int blk[NT];
 #pragma unroll
-          for (int j = 0; j < D / 16; ++j)
-            o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(tl[t].vfrag(j), pf, o[j], 0, 0, 0);
+      for (int t = 0; t < NT; ++t) blk[t] = __shfl(blk_l, min(t, my_tiles - 1), 64);
+      const int rsel = n >> 3;                          // K row n: from Y (1) or X (0)
+      const int rslot = 8 * ((n >> 2) & 1) + (n & 3);  // its slot in product A (B: + 4)
+      const int vsel = q4 >> 1;                         // this lane's 8 tokens: Y (1) or X (0)
+      const int vslot = 8 * (q4 & 1);                   // their first slot
+      const h16* kpool = reinterpret_cast<const h16*>(p.k_pool);
+      const h16* vpool = reinterpret_cast<const h16*>(p.v_pool);
+      h16x8 ka[NP][D / 32], kb[NP][D / 32], vv[NP][D / 16];
+#pragma unroll
+      for (int pr = 0; pr < NP; ++pr) {
+        const h16* kt = kpool + ((size_t)blk[2 * pr + rsel] * p.hkv + g) * kBlock * D + rslot * 8;
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+          ka[pr][s] = *reinterpret_cast<const h16x8*>(kt + (4 * s + q4) * kBlock * 8);
+          kb[pr][s] = *reinterpret_cast<const h16x8*>(kt + (4 * s + q4) * kBlock * 8 + 32);
+        }
+      }
+#pragma unroll
+      for (int pr = 0; pr < NP; ++pr) {
+        const h16* vt = vpool + ((size_t)blk[2 * pr + vsel] * p.hkv + g) * D * kBlock + n * kBlock + vslot;
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) vv[pr][j] = *reinterpret_cast<const h16x8*>(vt + j * 16 * kBlock);
+      }
+      // scores of the lane's 8 tokens per pair (slots vslot .. vslot + 7 of
+      // block 2 pr + vsel), log2 domain
+      float xa[NP][4], xb[NP][4];
+#pragma unroll
+      for (int pr = 0; pr < NP; ++pr) {
+#ifdef PKV_ATTN_QK_VALU
+        // each lane: v_dot2 over its 32 dims of K rows n (products A and B)
+        // for every head, summed over the 4 lane groups, then moved through
+        // LDS into the accumulator layout of the MFMA form
+        f32x4 sa, sb;
+        for (int h = 0; h < p.group; ++h) {
+          float da = 0.f, db = 0.f;
+#pragma unroll
+          for (int s = 0; s < D / 32; ++s) {
+            const h16x8 qh = *reinterpret_cast<const h16x8*>(&s_qv[h][8 * (4 * s + q4)]);
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              da = __builtin_amdgcn_fdot2(h16x2{ka[pr][s][e], ka[pr][s][e + 1]}, h16x2{qh[e], qh[e + 1]}, da, false);
+              db = __builtin_amdgcn_fdot2(h16x2{kb[pr][s][e], kb[pr][s][e + 1]}, h16x2{qh[e], qh[e + 1]}, db, false);
+            }
+          }
+          da += __shfl_xor(da, 16, 64);
+          da += __shfl_xor(da, 32, 64);
+          db += __shfl_xor(db, 16, 64);
+          db += __shfl_xor(db, 32, 64);
+          if (q4 == 0) {
+            s_sv[wave][0][n][h] = da;
+            s_sv[wave][1][n][h] = db;
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sa[i] = n < p.group ? s_sv[wave][0][4 * q4 + i][n] : 0.f;
+          sb[i] = n < p.group ? s_sv[wave][1][4 * q4 + i][n] : 0.f;
+        }
+        __builtin_amdgcn_wave_barrier();
+#else
+        f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+          sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[pr][s], qf[s], sa, 0, 0, 0);
+          sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[pr][s], qf[s], sb, 0, 0, 0);
+        }
+#endif
+        const int t = 2 * pr + vsel;
+        const int tb = tok0 + (wave + kWaves * t) * kBlock + vslot;
+        const bool tv = t < my_tiles;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xa[pr][i] = (tv && tb + i < tok_end) ? sa[i] * p.scale_log2 : -INFINITY;
+          xb[pr][i] = (tv && tb + 4 + i < tok_end) ? sb[i] * p.scale_log2 : -INFINITY;
+        }
+      }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int pr = 0; pr < NP; ++pr)
+        mt = fmaxf(mt, fmaxf(fmaxf(fmaxf(xa[pr][0], xa[pr][1]), fmaxf(xa[pr][2], xa[pr][3])),
+                             fmaxf(fmaxf(xb[pr][0], xb[pr][1]), fmaxf(xb[pr][2], xb[pr][3]))));
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      m_w = mt;
+#pragma unroll
+      for (int pr = 0; pr < NP; ++pr) {
+        if (2 * pr < my_tiles) {
+          float pa[4], pb[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pa[i] = __builtin_amdgcn_exp2f(xa[pr][i] - mt);
+            pb[i] = __builtin_amdgcn_exp2f(xb[pr][i] - mt);
+          }
+          l_w += ((pa[0] + pa[1]) + (pa[2] + pa[3])) + ((pb[0] + pb[1]) + (pb[2] + pb[3]));
+          const h16x8 pf = h16x8{(h16)pa[0], (h16)pa[1], (h16)pa[2], (h16)pa[3],
+                                 (h16)pb[0], (h16)pb[1], (h16)pb[2], (h16)pb[3]};
+          if (2 * pr + 1 < my_tiles && tok0 + (wave + kWaves * (2 * pr + 1) + 1) * kBlock <= tok_end) {
+#pragma unroll
+            for (int j = 0; j < D / 16; ++j)
+              o[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vv[pr][j], pf, o[j], 0, 0, 0);
+          } else {
+            // the wave's last pair: a block past the wave's tiles (a re-read)
+            // or slots past the context may hold anything (NaN included), so
+            // zero them before the product
+            const int t = 2 * pr + vsel;
+            const int tb = tok0 + (wave + kWaves * t) * kBlock + vslot;
+#pragma unroll
+            for (int j = 0; j < D / 16; ++j) {
+              h16x8 vf = vv[pr][j];
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (!(t < my_tiles && tb + e < tok_end)) vf[e] = (h16)0.f;
+              o[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, o[j], 0, 0, 0);
+            }
+          }
         }
       }
     }
