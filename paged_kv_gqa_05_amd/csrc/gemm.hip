@@ -74,6 +74,9 @@ __device__ __forceinline__ void load_to_lds(const void* g, const _Float16* lds) 
 // wait for every outstanding global load).
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
+// Wait for this wave's LDS reads (lgkmcnt 0), leaving vector-memory loads in flight.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
 template <int MT, int NT, int NS, int EPI, bool NORM, int WM, int WN>
 struct Cfg {
   static constexpr bool PAIR = epi_pair(EPI);
@@ -88,6 +91,18 @@ struct Cfg {
   static_assert(ROWS % (8 * WV) == 0 && FM >= 1 && FN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "tile shape");
   static_assert(!PAIR || (FN % 2 == 0), "paired tiles need an even fragment count");
   static_assert(NS >= 2 && (NS - 2) * LPW < 64, "stages");
+  // Registers of one stage's fragments and of the accumulators (per lane).
+  // Two fragment sets are kept (PIPE, see the main loop) when they fit, with
+  // 64 registers for the rest, in a wave's share of its SIMD's 512 at the
+  // number of workgroups per CU that the LDS allows: more registers then cost
+  // no resident workgroup.
+  static constexpr int FRAG_REGS = (2 * FM + 2 * FN + (NORM ? 2 : 0)) * 4;
+  static constexpr int ACC_REGS = FM * FN * 4;
+  static constexpr int LDS_BYTES = NS * STAGE * 2 + MT * 4 + 64;
+  static constexpr int WG_LDS = (160 * 1024) / LDS_BYTES;
+  static constexpr int WG_PER_CU = WG_LDS < 1 ? 1 : (WG_LDS > 32 / WV ? 32 / WV : WG_LDS);
+  static constexpr int REG_BUDGET = 512 / ((WG_PER_CU * WV + 3) / 4);  // per wave, waves per SIMD rounded up
+  static constexpr bool PIPE = 2 * FRAG_REGS + ACC_REGS + 64 <= REG_BUDGET;
 };
 
 // Wait until at most `pending` stages (of LPW loads each) are still in flight;
@@ -206,38 +221,52 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmParams p) {
     wrow_t[j] = MT + t + fr;
   }
 
-  auto compute = [&](int it) {
+  // The fragments of one stage for this lane (both 32-wide k steps, and with
+  // the norm the gain chunks), read from LDS ...
+  struct Frag {
+    h16x8 af[2][FM], wf[2][FN], g[2];
+  };
+  auto read_frags = [&](int it, Frag& f) {
     const h16* sb = smem + (it % NS) * C::STAGE;
-    const int kbase = (kc0 + it) * BK;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int c = 4 * s + fg;  // logical 16-byte chunk of this lane
-      const bool kin = kbase + 8 * c < p.K;
-      h16x8 af[FM], wf[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int r = arow[i];
-        af[i] = *reinterpret_cast<const h16x8*>(sb + r * BK + ((c ^ (r & 7)) * 8));
-        if (!kin) af[i] = h16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        f.af[s][i] = *reinterpret_cast<const h16x8*>(sb + r * BK + ((c ^ (r & 7)) * 8));
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int r = wrow_t[j];
-        wf[j] = *reinterpret_cast<const h16x8*>(sb + r * BK + ((c ^ (r & 7)) * 8));
+        f.wf[s][j] = *reinterpret_cast<const h16x8*>(sb + r * BK + ((c ^ (r & 7)) * 8));
+      }
+      if constexpr (NORM) f.g[s] = *reinterpret_cast<const h16x8*>(sb + C::GAIN_OFF + wave * BK + 8 * c);
+    }
+  };
+  // ... and their products (chunks past K are zero; with the norm, sum(h^2)
+  // of the raw activations, then the gain applied)
+  auto mma = [&](int it, Frag& f) {
+    const int kbase = (kc0 + it) * BK;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int c = 4 * s + fg;
+      if (kbase + 8 * c >= p.K) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) f.af[s][i] = h16x8{0, 0, 0, 0, 0, 0, 0, 0};
       }
       if constexpr (NORM) {
-        const h16x8 g = *reinterpret_cast<const h16x8*>(sb + C::GAIN_OFF + wave * BK + 8 * c);
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          ss[i] = dot8(af[i], af[i], ss[i]);
-          af[i] = af[i] * g;
+          ss[i] = dot8(f.af[s][i], f.af[s][i], ss[i]);
+          f.af[s][i] = f.af[s][i] * f.g[s];
         }
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], wf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.af[s][i], f.wf[s][j], acc[i][j], 0, 0, 0);
     }
   };
 
@@ -245,12 +274,77 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmParams p) {
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < n_iter) issue(s);
-  for (int it = 0; it < n_iter; ++it) {
-    const int pending = min(n_iter - 1, it + NS - 2) - it;
-    wait_stage<NS - 2, C::LPW>(pending);
-    barrier_only();
-    if (it + NS - 1 < n_iter) issue(it + NS - 1);
-    compute(it);
+  if constexpr (C::PIPE) {
+    // With one or two waves per SIMD nothing hides a wave's LDS read latency,
+    // so the fragments of stage it are read while the products of stage
+    // it - 1 run (two fragment sets in registers).  Before the barrier that
+    // lets a stage's slot be refilled, each wave waits for its own reads of
+    // that slot.  Same products in the same order as reading and multiplying
+    // one stage at a time.
+    Frag fa, fb;
+    auto step = [&](int it, Frag& cur, Frag& prev) {
+      const int pending = min(n_iter - 1, it + NS - 2) - it;
+      wait_stage<NS - 2, C::LPW>(pending);
+      wait_lds();
+      barrier_only();
+      if (it + NS - 1 < n_iter) issue(it + NS - 1);
+      read_frags(it, cur);
+      if (it > 0) mma(it - 1, prev);
+    };
+    int it = 0;
+    for (; it + 1 < n_iter; it += 2) {
+      step(it, fa, fb);
+      step(it + 1, fb, fa);
+    }
+    if (it < n_iter) {
+      step(it, fa, fb);
+      mma(it, fa);
+    } else {
+      mma(it - 1, fb);
+    }
+  } else {
+    // one 32-wide k step at a time: half the fragment registers
+    auto compute = [&](int it) {
+      const h16* sb = smem + (it % NS) * C::STAGE;
+      const int kbase = (kc0 + it) * BK;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int c = 4 * s + fg;
+        const bool kin = kbase + 8 * c < p.K;
+        h16x8 af[FM], wf[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int r = arow[i];
+          af[i] = *reinterpret_cast<const h16x8*>(sb + r * BK + ((c ^ (r & 7)) * 8));
+          if (!kin) af[i] = h16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int r = wrow_t[j];
+          wf[j] = *reinterpret_cast<const h16x8*>(sb + r * BK + ((c ^ (r & 7)) * 8));
+        }
+        if constexpr (NORM) {
+          const h16x8 g = *reinterpret_cast<const h16x8*>(sb + C::GAIN_OFF + wave * BK + 8 * c);
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            ss[i] = dot8(af[i], af[i], ss[i]);
+            af[i] = af[i] * g;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], wf[j], acc[i][j], 0, 0, 0);
+      }
+    };
+    for (int it = 0; it < n_iter; ++it) {
+      const int pending = min(n_iter - 1, it + NS - 2) - it;
+      wait_stage<NS - 2, C::LPW>(pending);
+      barrier_only();
+      if (it + NS - 1 < n_iter) issue(it + NS - 1);
+      compute(it);
+    }
   }
 
   // ---- sum(h^2) per activation row: reduce the four k-groups of a row
