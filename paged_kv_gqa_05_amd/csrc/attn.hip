@@ -45,7 +45,10 @@
 //    device-coherent stores and counts its arrival on a per-(row, KV head)
 //    counter; the workgroup that arrives last merges all partitions of the
 //    row in partition order (so the result does not depend on arrival order),
-//    writes the output and resets the counter to zero.  One kernel, no merge
+//    writes the output and resets the counter to zero.  When the whole grid
+//    is resident at once (8-wave plans), the row's first partition instead
+//    keeps its own partial on chip, waits for the others' arrivals and
+//    merges (falling back to publishing after a bounded wait).  One kernel, no merge
 //    launch; the counters are zero before and after every call.
 //  * FP8 E4M3 codes are converted to f16 in registers with the gfx950
 //    conversion instruction (exact: every E4M3 value is an f16 value); the

@@ -19,6 +19,9 @@ constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLog2e = 1.44269504088896341f;
 // Partitions the merge reads per round trip.
 constexpr int kMergeBatch = 8;
+// How long the first partition of a row waits for the others' arrivals before
+// it publishes its own partial instead (100 us of the 100 MHz wall clock).
+constexpr unsigned long long kMergePollTicks = 10000;
 
 struct SplitParams {
   const unsigned char* k_pool;
@@ -33,6 +36,8 @@ struct SplitParams {
   float* ws_o;     // [B][Hq][P][D] unnormalised O per partition
   int bt_stride;
   int batch, hq, hkv, group, part, n_parts_max;
+  int merge_poll;    // every workgroup of the call is resident at once: the first
+                     // partition of a row waits for the others and merges
   float scale_log2;  // softmax scale * log2(e) * K dequant scale
   float v_scale;     // V dequant scale (1 for f16)
 };
@@ -427,7 +432,17 @@ __device__ __forceinline__ void attn_body(const SplitParams& p, const int wg) {
     return;
   }
 
-  // ---- this partition's (max, sum, O) per head, four dims per thread
+  // ---- this partition's (max, sum, O) per head, four dims per thread.
+  // When every workgroup of the call is resident at once (and a thread holds
+  // one (head, 4 dims) item), the row's first partition, a full one and so
+  // the last to finish as a rule, keeps its own partial on chip, waits for
+  // the others to arrive and merges: two memory round trips (publishing its
+  // partial, counting its arrival) leave the critical path.  Otherwise, or
+  // if that wait runs past its limit, every partition publishes and the last
+  // to arrive merges.  Both merge the same values in partition order.
+  const bool poll = p.merge_poll && part_idx == 0 && p.group * (D / 4) <= kThreads;  // uniform
+  float2 own_ml = make_float2(-INFINITY, 0.f);
+  f32x4 own_o = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int idx = tid; idx < p.group * (D / 4); idx += kThreads) {
     const int h = idx / (D / 4), d = 4 * (idx - h * (D / 4));
     float mx = -INFINITY;
@@ -441,17 +456,47 @@ __device__ __forceinline__ void attn_body(const SplitParams& p, const int wg) {
       L += s_l[w][h] * e;
       O += *reinterpret_cast<const f32x4*>(&s_o[w][h][d]) * e;
     }
-    const size_t slot = (bh0 + h) * p.n_parts_max + part_idx;
-    st_agent(p.ws_o + slot * D + d, O * p.v_scale);
-    if (d == 0) st_agent2(p.ws_ml + slot, make_float2(mx, L));
+    own_ml = make_float2(mx, L);
+    own_o = O * p.v_scale;
+    if (!poll) {
+      const size_t slot = (bh0 + h) * p.n_parts_max + part_idx;
+      st_agent(p.ws_o + slot * D + d, own_o);
+      if (d == 0) st_agent2(p.ws_ml + slot, own_ml);
+    }
   }
-  wait_vmcnt<0>();  // this thread's partial has reached the coherent level
   __shared__ int s_last;
-  __syncthreads();
-  if (tid == 0)
-    s_last = __hip_atomic_fetch_add(p.counters + bg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
-  __syncthreads();
-  if (!s_last) return;
+  bool polled = false;
+  if (poll) {
+    if (tid == 0) {
+      const unsigned long long t0 = wall_clock64();
+      int ok = 0;
+      for (;;) {
+        if (__hip_atomic_load(p.counters + bg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= np - 1) {
+          ok = 1;
+          break;
+        }
+        if (wall_clock64() - t0 > kMergePollTicks) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      s_last = ok;
+    }
+    __syncthreads();
+    polled = s_last;
+    if (!polled && tid < p.group * (D / 4)) {  // past the limit: publish like the others
+      const int h = tid / (D / 4), d = 4 * (tid - h * (D / 4));
+      const size_t slot = (bh0 + h) * p.n_parts_max + part_idx;
+      st_agent(p.ws_o + slot * D + d, own_o);
+      if (d == 0) st_agent2(p.ws_ml + slot, own_ml);
+    }
+  }
+  if (!polled) {
+    wait_vmcnt<0>();  // this thread's partial has reached the coherent level
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(p.counters + bg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
+    __syncthreads();
+    if (!s_last) return;
+  }
 
   // ---- last partition of the row to finish: merge all np in partition order
   if (tid == 0) __hip_atomic_store(p.counters + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -469,6 +514,10 @@ __device__ __forceinline__ void attn_body(const SplitParams& p, const int wg) {
         const size_t slot = base + min(i0 + u, np - 1);
         ml[u] = ld_agent2(p.ws_ml + slot);
         po[u] = ld_agent(p.ws_o + slot * D + d);
+      }
+      if (polled && i0 == 0) {  // partition 0 is this workgroup's own, never published
+        ml[0] = own_ml;
+        po[0] = own_o;
       }
       float mn = M;
 #pragma unroll
@@ -516,6 +565,8 @@ inline SplitParams make_split_params(const AttnArgs& a, const AttnPlan& plan) {
   sp.group = a.hq / a.hkv;
   sp.part = plan.part;
   sp.n_parts_max = plan.n_parts_max;
+  // the 8-wave plans keep the whole grid within one workgroup per CU
+  sp.merge_poll = plan.waves == 8 ? 1 : 0;
   sp.scale_log2 = a.scale * kLog2e * (a.fp8 ? a.k_scale : 1.0f);
   sp.v_scale = a.fp8 ? a.v_scale : 1.0f;
   const size_t ml = align_up((size_t)a.batch * a.hq * plan.n_parts_max * sizeof(float2), 256);
