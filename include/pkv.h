@@ -191,6 +191,16 @@ pkv_status pkv_paged_attn_decode_noalloc(const pkv_cache* cache, int layer, cons
                                          const int32_t* context_lens, int batch, int num_q_heads,
                                          int max_context, float scale, pkv_stream_t stream);
 
+/* Testing hook for the decode attention's merge (host only, process-wide,
+ * takes effect for kernels enqueued or captured later).  Under the 8-wave
+ * plans the first partition of a multi-partition row waits up to `ticks` of
+ * the 100 MHz device wall clock for the row's other partitions and then
+ * merges them with its own partial kept on chip; past the limit it publishes
+ * its partial and the last partition to arrive merges.  The default is 10000
+ * (100 us); 0 makes it publish at once (the fallback path, for tests).  Both
+ * paths give the same bits.  Always PKV_OK. */
+pkv_status pkv_debug_attn_merge_wait(unsigned long long ticks);
+
 /* --------------------------------------------------------------------- model */
 
 typedef struct {

@@ -132,6 +132,13 @@ def paged_attn_decode(cache, layer, q, out, block_tables, context_lens, max_cont
                                       _stream(stream)))
 
 
+def debug_attn_merge_wait(ticks):
+    """Testing hook (process-wide): how long, in 100 MHz wall-clock ticks, the
+    first partition of a multi-partition row waits for the others before it
+    publishes its partial (default 10000; 0 publishes at once)."""
+    _check(_lib.pkv_debug_attn_merge_wait(int(ticks)))
+
+
 def paged_attn_decode_noalloc(cache, layer, q, out, block_tables, context_lens, max_context, scale, lse=None,
                               stream=None):
     """paged_attn_decode with the library's static per-GPU scratch instead of a
@@ -170,8 +177,8 @@ class Model:
         self.handle = h
 
     def set_persistent_batch1(self, enable):
-        """Run batch-1 decode steps as one persistent kernel (default) or one
-        kernel per fused op (both give the same bits)."""
+        """Run batch-1 decode steps as one persistent kernel or one kernel per
+        fused op (the default; both give the same bits)."""
         _check(_lib.pkv_model_set_option(self.handle, 0, 1 if enable else 0))
 
     def close(self, _destroy=_destroy):

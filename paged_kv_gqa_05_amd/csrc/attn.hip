@@ -85,6 +85,8 @@ hipError_t launch_impl(const SplitParams& sp, const AttnPlan& plan, hipStream_t 
 
 }  // namespace
 
+unsigned long long attn_merge_wait_ticks = 10000;  // 100 us at the 100 MHz wall clock
+
 AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int max_context) {
   AttnPlan p{};
   // A workgroup of W waves takes one partition of 16 NT W tokens; every wave
@@ -141,3 +143,8 @@ hipError_t launch_paged_attention(const AttnArgs& a, const AttnPlan& plan, hipSt
 }
 
 }  // namespace pkv
+
+extern "C" pkv_status pkv_debug_attn_merge_wait(unsigned long long ticks) {
+  pkv::attn_merge_wait_ticks = ticks;
+  return PKV_OK;
+}

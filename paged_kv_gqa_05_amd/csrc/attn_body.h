@@ -19,9 +19,6 @@ constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLog2e = 1.44269504088896341f;
 // Partitions the merge reads per round trip.
 constexpr int kMergeBatch = 8;
-// How long the first partition of a row waits for the others' arrivals before
-// it publishes its own partial instead (100 us of the 100 MHz wall clock).
-constexpr unsigned long long kMergePollTicks = 10000;
 
 struct SplitParams {
   const unsigned char* k_pool;
@@ -38,6 +35,7 @@ struct SplitParams {
   int batch, hq, hkv, group, part, n_parts_max;
   int merge_poll;    // every workgroup of the call is resident at once: the first
                      // partition of a row waits for the others and merges
+  unsigned long long poll_ticks;  // its wait limit (wall-clock ticks; 0: publish at once)
   float scale_log2;  // softmax scale * log2(e) * K dequant scale
   float v_scale;     // V dequant scale (1 for f16)
 };
@@ -470,12 +468,12 @@ __device__ __forceinline__ void attn_body(const SplitParams& p, const int wg) {
     if (tid == 0) {
       const unsigned long long t0 = wall_clock64();
       int ok = 0;
-      for (;;) {
+      while (p.poll_ticks > 0) {
         if (__hip_atomic_load(p.counters + bg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= np - 1) {
           ok = 1;
           break;
         }
-        if (wall_clock64() - t0 > kMergePollTicks) break;
+        if (wall_clock64() - t0 > p.poll_ticks) break;
         __builtin_amdgcn_s_sleep(1);
       }
       s_last = ok;
@@ -567,6 +565,7 @@ inline SplitParams make_split_params(const AttnArgs& a, const AttnPlan& plan) {
   sp.n_parts_max = plan.n_parts_max;
   // the 8-wave plans keep the whole grid within one workgroup per CU
   sp.merge_poll = plan.waves == 8 ? 1 : 0;
+  sp.poll_ticks = attn_merge_wait_ticks;
   sp.scale_log2 = a.scale * kLog2e * (a.fp8 ? a.k_scale : 1.0f);
   sp.v_scale = a.fp8 ? a.v_scale : 1.0f;
   const size_t ml = align_up((size_t)a.batch * a.hq * plan.n_parts_max * sizeof(float2), 256);

@@ -55,6 +55,9 @@ struct AttnPlan {
   size_t ws_bytes;  // workspace bytes (counters + partials of multi-partition rows)
 };
 AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int max_context);
+// Wall-clock ticks the first partition of a row waits for the others before
+// it publishes its partial (pkv_debug_attn_merge_wait; 0 = publish at once).
+extern unsigned long long attn_merge_wait_ticks;
 
 // A standalone attention workspace (pkv_paged_attn_decode) of W bytes keeps
 // its arrival counters in a leading region whose size depends on W alone

@@ -184,6 +184,32 @@ def test_workspace_small_batch_then_large_batch(lib):
         assert not ws[:region].any().item()
 
 
+def test_merge_by_first_partition_equals_last_arriver_merge(lib):
+    """attn15 runs the 8-wave plan (about half its rows in two partitions).
+    There the first partition of a row keeps its partial on chip, waits for
+    the others and merges; with a zero wait it publishes at once and the last
+    partition to arrive merges instead (the fallback path).  Both give the
+    same bits (output and log-sum-exp), match the oracle and leave the
+    counter region zero."""
+    case = inp.workload_case(inp.ATTN15)
+    cache = load_case_into_cache(lib, case)
+    ws = lib.attn_workspace(cache, 64, 12, case.max_context)
+    region = _counter_region(ws.numel())
+    runs = []
+    try:
+        for ticks in (10000, 0, 10000, 0):
+            lib.debug_attn_merge_wait(ticks)
+            runs.append(run_attention(lib, case, cache=cache, ws=ws))
+            assert not ws[:region].any().item(), f"counters left set (wait {ticks})"
+    finally:
+        lib.debug_attn_merge_wait(10000)
+    ref, _ = oracle_attention(case)
+    assert_parity(runs[0][0], ref, "merge by the first partition")
+    for out, lse in runs[1:]:
+        assert np.array_equal(out.view(np.uint16), runs[0][0].view(np.uint16))
+        assert np.array_equal(lse.view(np.uint32), runs[0][1].view(np.uint32))
+
+
 def test_inactive_rows(lib):
     case = inp.attention_case(4, 4, 2, 64, 1, 40, seed=14, ctx_lens=[0, 5, 0, 33])
     out, lse = run_attention(lib, case)
