@@ -283,6 +283,21 @@ pkv_status pkv_decode_layer(const pkv_model* model, pkv_cache* cache, int layer,
                             const int32_t* context_lens, int batch, int max_context,
                             void* workspace, size_t workspace_bytes, pkv_stream_t stream);
 
+/* The same layer in the (x, residual) form of the fused "Add + RMSNorm"
+ * kernels (rvLLM post, section "퓨즈드 CUDA 커널": the residual add of a
+ * sub-block's output happens inside the next fused op):
+ *   h = f16(residual + x)   (correctly rounded)
+ *   the layer above on h up to h1 = h + W_o o
+ *   residual = h1;  x = f16(W_down (silu(g) * u))   (not yet added)
+ * x: f16 [batch][H], in: the previous layer's x (the embedding rows for
+ * layer 0), out: this layer's MLP output.  residual: f16 [batch][H], in/out
+ * (zero for layer 0).  Distinct buffers (PKV_E_ARG otherwise).  The final
+ * hidden state after the last layer is f16(residual + x).  Workspace, cache
+ * and metadata as for pkv_decode_layer. */
+pkv_status pkv_decode_layer_xr(const pkv_model* model, pkv_cache* cache, int layer, void* x, void* residual,
+                               const int32_t* block_tables, int bt_stride, const int32_t* context_lens,
+                               int batch, int max_context, void* ws, size_t ws_bytes, pkv_stream_t stream);
+
 /* One of the five fused ops of a decoder layer (rvLLM post, section
  * "퓨즈드 CUDA 커널"), run alone; in the order below they are exactly
  * pkv_decode_layer (bit for bit), passing q, the attention output and the

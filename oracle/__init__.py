@@ -46,6 +46,7 @@ from .decoder import (
     paged_attention_batch,
     kv_append,
     decode_layer,
+    decode_layer_xr,
     decode_step,
     greedy_argmax,
     causal_forward,
@@ -56,5 +57,5 @@ __all__ = [
     "e4m3_decode", "e4m3_encode", "e4m3_quantize", "e4m3_table", "apply_penalties", "candidates", "draw",
     "exp_f32", "sample", "sample_penalized", "sample_row", "weight_fixed", "ModelConfig", "rmsnorm", "silu", "rope",
     "rope_angles", "paged_attention", "paged_attention_batch", "kv_append",
-    "decode_layer", "decode_step", "greedy_argmax", "causal_forward", "prefill",
+    "decode_layer", "decode_layer_xr", "decode_step", "greedy_argmax", "causal_forward", "prefill",
 ]

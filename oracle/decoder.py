@@ -233,14 +233,10 @@ def _linear(x, w, acc, bias=None):
     return y
 
 
-def decode_layer(cfg, lw, h, k_pool, v_pool, block_tables, ctx_lens, acc=np.float64, k_scale=None,
-                 v_scale=None):
-    """One decoder layer for a batch of single-token rows.
-
-    h: [B, H] f16 hidden state; the pools are this layer's and are updated in
-    place by the append (E4M3 pools with this layer's k_scale / v_scale).
-    Returns the new hidden state [B, H] f16.
-    """
+def _layer(cfg, lw, h, k_pool, v_pool, block_tables, ctx_lens, acc, k_scale, v_scale):
+    """The layer up to its last product: returns h1 = f16(h + W_o o) (the
+    hidden state after the attention sub-block) and W_d (silu(g) * u) in
+    `acc` precision, not rounded."""
     hq, hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     b_n = h.shape[0]
     lens = np.asarray(ctx_lens, dtype=np.int64)
@@ -266,8 +262,36 @@ def decode_layer(cfg, lw, h, k_pool, v_pool, block_tables, ctx_lens, acc=np.floa
     m = rmsnorm(h1, lw["w_post"], cfg.rms_eps, acc)
     gu = _linear(m, lw["w_gate_up"], acc)
     act = silu(gu[:, : cfg.ffn], acc) * gu[:, cfg.ffn:]
-    h2 = (np.asarray(h1, dtype=acc) + _linear(act, lw["w_down"], acc)).astype(F16)
-    return h2
+    return h1, _linear(act, lw["w_down"], acc)
+
+
+def decode_layer(cfg, lw, h, k_pool, v_pool, block_tables, ctx_lens, acc=np.float64, k_scale=None,
+                 v_scale=None):
+    """One decoder layer for a batch of single-token rows.
+
+    h: [B, H] f16 hidden state; the pools are this layer's and are updated in
+    place by the append (E4M3 pools with this layer's k_scale / v_scale).
+    Returns the new hidden state [B, H] f16.
+    """
+    h1, down = _layer(cfg, lw, h, k_pool, v_pool, block_tables, ctx_lens, acc, k_scale, v_scale)
+    return (np.asarray(h1, dtype=acc) + down).astype(F16)
+
+
+def decode_layer_xr(cfg, lw, x, r, k_pool, v_pool, block_tables, ctx_lens, acc=np.float64, k_scale=None,
+                    v_scale=None):
+    """The same layer in the (x, residual) form of the fused "Add + RMSNorm"
+    kernels (rvLLM post, section "퓨즈드 CUDA 커널": the add joins the previous
+    sub-block's output to the residual stream inside the next fused op).
+
+    x: [B, H] f16 output of the previous MLP (the embedding for layer 0), r:
+    [B, H] f16 residual stream (zero for layer 0).  The layer adds x to r
+    (h = f16(r + x)), runs as decode_layer on h up to the down projection, and
+    returns (x', r') = (f16(W_d (silu(g) * u)), h1): the new MLP output, not
+    yet added, and the residual stream after the attention sub-block.
+    """
+    h = (np.asarray(r, dtype=acc) + np.asarray(x, dtype=acc)).astype(F16)
+    h1, down = _layer(cfg, lw, h, k_pool, v_pool, block_tables, ctx_lens, acc, k_scale, v_scale)
+    return down.astype(F16), h1
 
 
 def decode_step(cfg, weights, k_pools, v_pools, tokens, block_tables, ctx_lens,

@@ -201,6 +201,18 @@ def decode_layer(model, cache, layer, hidden, block_tables, context_lens, max_co
                                  _p(workspace), workspace.numel(), _stream(stream)))
 
 
+def decode_layer_xr(model, cache, layer, x, residual, block_tables, context_lens, max_context, workspace,
+                    stream=None):
+    """The layer in (x, residual) form: residual = f16(residual + x), the
+    layer up to the attention sub-block's residual add (left in residual),
+    x = the MLP output (not yet added)."""
+    _need(x, torch.float16, "x")
+    _need(residual, torch.float16, "residual")
+    _check(_lib.pkv_decode_layer_xr(model.handle, cache.handle, layer, _p(x), _p(residual), _p(block_tables),
+                                    block_tables.shape[1], _p(context_lens), x.shape[0], max_context,
+                                    _p(workspace), workspace.numel(), _stream(stream)))
+
+
 OP_QKV, OP_ATTN, OP_O, OP_GATE_UP, OP_DOWN = range(5)
 
 

@@ -52,6 +52,8 @@ SIGNATURES = {
     "pkv_step_workspace_bytes": (c_status, [vp, vp, C.c_int, C.c_int, C.POINTER(size_t)]),
     "pkv_decode_layer": (c_status, [vp, vp, C.c_int, vp, i32p, C.c_int, i32p, C.c_int, C.c_int,
                                     vp, size_t, vp]),
+    "pkv_decode_layer_xr": (c_status, [vp, vp, C.c_int, vp, vp, i32p, C.c_int, i32p, C.c_int, C.c_int,
+                                       vp, size_t, vp]),
     "pkv_layer_op": (c_status, [vp, vp, C.c_int, C.c_int, vp, i32p, C.c_int, i32p, C.c_int, C.c_int,
                                 vp, size_t, vp]),
     "pkv_decode_step": (c_status, [vp, vp, i32p, i32p, C.c_int, i32p, C.c_int, C.c_int, vp, vp,

@@ -428,6 +428,28 @@ pkv_status pkv_decode_layer(const pkv_model* m, pkv_cache* cache, int layer, voi
   return PKV_OK;
 }
 
+pkv_status pkv_decode_layer_xr(const pkv_model* m, pkv_cache* cache, int layer, void* x, void* residual,
+                               const int32_t* bt, int bt_stride, const int32_t* lens, int batch,
+                               int max_context, void* ws, size_t ws_bytes, pkv_stream_t stream) {
+  StepBuffers sb{};
+  AttnPlan plan{};
+  pkv_status st = check_step(m, cache, bt, bt_stride, lens, batch, max_context, ws, ws_bytes, &sb, &plan);
+  if (st != PKV_OK) return st;
+  if (!x || !residual) return fail(PKV_E_ARG, "x or residual is NULL");
+  if (x == residual) return fail(PKV_E_ARG, "x and residual must be different buffers");
+  if (layer < 0 || layer >= m->d.num_layers || layer >= cache->desc.num_layers)
+    return fail(PKV_E_ARG, "layer out of range");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  _Float16* h = static_cast<_Float16*>(residual);
+  PKV_HIP(launch_add_clear(residual, x, (size_t)batch * m->d.hidden, sb.counters, sb.n_counters, s));
+  for (int op = PKV_OP_QKV; op <= PKV_OP_GATE_UP; ++op)
+    PKV_HIP(run_layer_op(m, cache, layer, op, h, bt, bt_stride, lens, batch, sb, plan, s));
+  LinArgs a = layer_lin_args(m, cache, layer, PKV_OP_DOWN, h, bt, bt_stride, lens, batch, sb);
+  a.out = x;  // zeroed above: the residual epilogue leaves f16(W_down act) in x
+  PKV_HIP(launch_linear(a, EPI_RESID, sb.gemm_ws, sb.counters, s));
+  return PKV_OK;
+}
+
 pkv_status pkv_layer_op(const pkv_model* m, pkv_cache* cache, int layer, int op, void* hidden,
                         const int32_t* bt, int bt_stride, const int32_t* lens, int batch, int max_context,
                         void* ws, size_t ws_bytes, pkv_stream_t stream) {

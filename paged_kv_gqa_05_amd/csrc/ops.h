@@ -45,5 +45,7 @@ hipError_t launch_prefill_attention(const PrefillAttnArgs& a, hipStream_t s);
 
 hipError_t launch_argmax(const void* logits, int batch, int vocab, int32_t* tokens, const int32_t* lens,
                          hipStream_t s);
+// r = f16(r + x), then x = 0, over n f16 elements; zeroes zero_n ints at zero_p.
+hipError_t launch_add_clear(void* r, void* x, size_t n, int* zero_p, int zero_n, hipStream_t s);
 
 }  // namespace pkv

@@ -1,5 +1,7 @@
 // Small per-step kernels: embedding gather, greedy argmax and the per-token
 // rows of a prefill.
+#include <algorithm>
+
 #include "ops.h"
 
 namespace pkv {
@@ -16,6 +18,21 @@ __global__ void embed_kernel(const h16* __restrict__ table, const int32_t* __res
   h16* dst = h + (size_t)b * hidden;
   for (int i = threadIdx.x * 8; i < hidden; i += blockDim.x * 8)
     *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(src + i);
+}
+
+// The first residual add of the (x, residual) layer form: r = f16(r + x) in
+// fp32 (the exact sum of two f16 values rounded once more to f16 is the
+// correctly rounded f16 sum), then x = 0 (the down projection adds its
+// output to it); also zeroes zero_n ints at zero_p (the step's counters).
+__global__ void add_clear_kernel(h16* __restrict__ r, h16* __restrict__ x, size_t n, int* __restrict__ zero_p,
+                                 int zero_n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (size_t i = t; i < (size_t)zero_n; i += stride) zero_p[i] = 0;
+  for (size_t i = t; i < n; i += stride) {
+    r[i] = (h16)((float)r[i] + (float)x[i]);
+    x[i] = (h16)0.f;
+  }
 }
 
 // Lowest index of the largest value per row (-1 for a row whose context
@@ -122,6 +139,14 @@ hipError_t launch_embed(const void* table, const int32_t* tokens, void* h, int b
                         int* zero_p, int zero_n, hipStream_t s) {
   hipLaunchKernelGGL(embed_kernel, dim3(batch), dim3(256), 0, s, static_cast<const h16*>(table), tokens,
                      static_cast<h16*>(h), hidden, zero_p, zero_n);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_clear(void* r, void* x, size_t n, int* zero_p, int zero_n, hipStream_t s) {
+  const size_t need = (std::max(n, (size_t)zero_n) + 255) / 256;
+  const int grid = (int)std::min<size_t>(std::max<size_t>(need, 1), 1024);
+  hipLaunchKernelGGL(add_clear_kernel, dim3(grid), dim3(256), 0, s, static_cast<h16*>(r), static_cast<h16*>(x), n,
+                     zero_p, zero_n);
   return hipGetLastError();
 }
 

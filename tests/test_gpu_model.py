@@ -19,6 +19,23 @@ def _layer_case(shape, batch, seed, lo=1, hi=64):
     return inp.tiny_layer_case(seed=seed, batch=batch, ctx_lo=lo, ctx_hi=hi, shape=shape)
 
 
+def _layer_rig(pkv, shape, case, max_context=None):
+    """Model, cache (case pools loaded), tables, lengths, max context and workspace."""
+    w = weights_to_device(case["weights"])
+    model = pkv.Model(shape, w, max_positions=4096)
+    cache = pkv.KVCache(1, case["num_blocks"], shape.n_kv_heads, shape.head_dim)
+    k, v = cache.layer(0)
+    k.copy_(torch.from_numpy(k_to_lib(case["k_pool"])))
+    v.copy_(torch.from_numpy(v_to_lib(case["v_pool"])))
+    b = case["hidden"].shape[0]
+    mc = max_context or int(case["ctx_lens"].max())
+    bt = case["block_tables"]
+    if bt.shape[1] * 16 < mc:
+        bt = np.concatenate([bt, np.full((b, (mc + 15) // 16 - bt.shape[1]), -1, np.int32)], axis=1)
+    ws = torch.empty(pkv.step_workspace_bytes(model, cache, b, mc), dtype=torch.uint8, device="cuda")
+    return model, cache, dev(bt), dev(case["ctx_lens"]), mc, ws, w
+
+
 def _run_layer_gpu(pkv, shape, case, max_context=None):
     w = weights_to_device(case["weights"])
     model = pkv.Model(shape, w, max_positions=4096)
@@ -71,6 +88,59 @@ def test_decode_layer_parity(lib, shape, batch, seed, hi):
     assert_parity(k[changed], rk[changed], "appended K")
     assert np.array_equal(v[keep].view(np.uint16), case["v_pool"][keep].view(np.uint16))
     assert_parity(v[changed], rv[changed], "appended V")
+
+
+@pytest.mark.parametrize("shape,batch,seed,hi", [
+    (inp.TINY, 4, 1301, 64),       # GEMV path
+    (MID, 3, 1302, 300),           # D = 128, several partitions
+    (MID, 70, 1303, 200),          # MFMA path
+    (WIDE, 2, 1304, 100),          # down projection over a whole workgroup per row
+])
+def test_decode_layer_xr_parity(lib, shape, batch, seed, hi):
+    """The (x, residual) form: residual after the attention sub-block and the
+    MLP output (not yet added) against the oracle's, each within the bar, and
+    the cache's appended slots as for the plain layer."""
+    case = _layer_case(shape, batch, seed, hi=hi)
+    rng = np.random.default_rng(seed + 5)
+    x = (rng.standard_normal(case["hidden"].shape) * 0.5).astype(np.float16)
+    r = case["hidden"]
+    model, cache, bt, lens, mc, ws, _w = _layer_rig(lib, shape, case)
+    xd, rd = dev(x), dev(r)
+    lib.decode_layer_xr(model, cache, 0, xd, rd, bt, lens, mc, ws)
+    torch.cuda.synchronize()
+    kp, vp = case["k_pool"].copy(), case["v_pool"].copy()
+    ox, orr = oracle.decode_layer_xr(oracle_config(shape, 1), case["weights"]["layers"][0], x, r, kp, vp,
+                                     case["block_tables"], case["ctx_lens"])
+    assert_parity(rd.cpu().numpy(), orr, "residual after the attention sub-block")
+    assert_parity(xd.cpu().numpy(), ox, "MLP output")
+    k, v = cache.layer(0)
+    changed = np.zeros(kp.shape, bool)
+    for b, c in enumerate(case["ctx_lens"]):
+        changed[case["block_tables"][b][(c - 1) // 16], :, (c - 1) % 16, :] = True
+    assert_parity(k_from_lib(k.cpu().numpy())[changed], kp[changed], "appended K")
+    assert_parity(v_from_lib(v.cpu().numpy())[changed], vp[changed], "appended V")
+
+
+def test_decode_layer_xr_chain_equals_plain_chain(lib):
+    """Two layers in (x, residual) form from (embedding-like x, zero residual)
+    end at f16(residual + x), which matches two plain layers on h = x within
+    the bar; x and residual must be distinct buffers."""
+    shape = MID
+    case = _layer_case(shape, 6, 1311, hi=200)
+    model, cache, bt, lens, mc, ws, _w = _layer_rig(lib, shape, case)
+    x = dev(case["hidden"])
+    r = torch.zeros_like(x)
+    for _ in range(2):
+        lib.decode_layer_xr(model, cache, 0, x, r, bt, lens, mc, ws)
+    final = (r.float() + x.float()).half().cpu().numpy()
+    model2, cache2, bt2, lens2, mc2, ws2, _w2 = _layer_rig(lib, shape, case)
+    h = dev(case["hidden"])
+    for _ in range(2):
+        lib.decode_layer(model2, cache2, 0, h, bt2, lens2, mc2, ws2)
+    torch.cuda.synchronize()
+    assert_parity(final, h.cpu().numpy(), "two layers, (x, residual) form against plain")
+    with pytest.raises(lib.PkvError):
+        lib.decode_layer_xr(model, cache, 0, x, x, bt, lens, mc, ws)
 
 
 def test_decode_layer_without_bias_and_unit_gains(lib):

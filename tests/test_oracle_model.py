@@ -8,6 +8,10 @@
 * rows are independent (batch composition does not change a row);
 * the append writes exactly the slot at pos = ctx - 1 and nothing else;
 * greedy argmax takes the lowest index on ties;
+* the (x, residual) form of the layer: with W_o = 0 its residual is exactly
+  the f16 sum r + x, with W_d = 0 its x' is exactly zero and its residual the
+  plain layer's output on h = f16(r + x), and in general f16(r' + x') is the
+  plain layer's output up to the one extra rounding of x';
 * prefill of several prompts at once == the textbook causal forward of each
   prompt (last logits and every cached K and V), and prefill in two chunks ==
   prefill in one == token-by-token decode.
@@ -18,7 +22,7 @@ import numpy as np
 import torch
 import torch.nn.functional as F
 
-from oracle import ModelConfig, decode_step, causal_forward, decode_layer, greedy_argmax, prefill
+from oracle import ModelConfig, decode_step, causal_forward, decode_layer, decode_layer_xr, greedy_argmax, prefill
 import pkv_inputs as inp
 
 SHAPE = inp.Shape(hidden=128, n_q_heads=4, n_kv_heads=2, head_dim=32, ffn=160, vocab=300, n_layers=2)
@@ -206,3 +210,40 @@ def test_prefill_in_chunks_equals_one_chunk_and_decode():
                                        atol=2e-3, rtol=2e-3)
             np.testing.assert_allclose(kp3[li][bt3[b][t // BS], :, t % BS, :].astype(np.float64), a,
                                        atol=2e-3, rtol=2e-3)
+
+
+def test_layer_xr_form_pins():
+    shape = inp.Shape(128, 4, 2, 32, 96, 64, 1)
+    cfg = ModelConfig(128, 4, 2, 32, 96, 64, 1)
+    case = inp.tiny_layer_case(seed=57, batch=5, ctx_lo=1, ctx_hi=40, shape=shape)
+    rng = np.random.default_rng(58)
+    x = (rng.standard_normal(case["hidden"].shape) * 0.5).astype(np.float16)
+    r = case["hidden"]
+    h = (r.astype(np.float64) + x.astype(np.float64)).astype(np.float16)
+    lw = case["weights"]["layers"][0]
+
+    def run(lw, form):
+        kp, vp = case["k_pool"].copy(), case["v_pool"].copy()
+        if form == "xr":
+            return decode_layer_xr(cfg, lw, x, r, kp, vp, case["block_tables"], case["ctx_lens"]), kp
+        return decode_layer(cfg, lw, h, kp, vp, case["block_tables"], case["ctx_lens"]), kp
+
+    # W_o = 0: the attention sub-block adds nothing, r' is the input sum itself
+    (x1, r1), _ = run(dict(lw, w_o=np.zeros_like(lw["w_o"])), "xr")
+    assert np.array_equal(r1.view(np.uint16), h.view(np.uint16))
+    # W_d = 0: x' is zero and r' is the plain layer's output on h
+    lw0 = dict(lw, w_down=np.zeros_like(lw["w_down"]))
+    (x2, r2), k_xr = run(lw0, "xr")
+    h2, k_plain = run(lw0, "plain")
+    assert not np.any(x2.astype(np.float32)) and np.array_equal(r2.view(np.uint16), h2.view(np.uint16))
+    assert np.array_equal(np.nan_to_num(k_xr), np.nan_to_num(k_plain))
+    # in general: r' + x' (one more f16 rounding of x') is the plain layer's output
+    (x3, r3), _ = run(lw, "xr")
+    h3, _ = run(lw, "plain")
+    s = (r3.astype(np.float64) + x3.astype(np.float64)).astype(np.float16)
+    # f16(x') is off by half an ulp of x', and each final rounding by half an
+    # ulp of the sum (x' can be larger than the sum when r' and x' cancel)
+    ulp = lambda a: np.spacing(np.abs(a).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(s.astype(np.float64) - h3.astype(np.float64)) <= ulp(h3) + 0.5 * ulp(x3) + 1e-7)
+    assert np.any(x3.astype(np.float32))
+
