@@ -144,7 +144,12 @@ pkv_status pkv_kv_append(pkv_cache* cache, int layer, const void* k, const void*
  * counters sit in a leading region whose size depends on W only (W / 64 in
  * whole 256-byte units, at least 256 bytes), the partial results after it; a
  * call fits W when its batch x Hkv counters fit that region and its partials
- * fit behind it, which every W >= the returned size guarantees. */
+ * fit behind it, which every W >= the returned size guarantees.
+ * PKV_E_ARG for NULL arguments, sizes below 1 or Hq not a multiple of Hkv;
+ * PKV_E_UNSUPPORTED for more than 16 query heads per KV head, max_context
+ * above 262144, or batch x Hkv x ceil(max_context / 128) above 2^30 (the
+ * attention's grid bound; the same limit holds for every call that plans
+ * the decode attention). */
 pkv_status pkv_attn_workspace_bytes(const pkv_cache* cache, int batch, int num_q_heads,
                                     int max_context, size_t* bytes);
 
@@ -265,7 +270,9 @@ pkv_status pkv_model_set_option(pkv_model* model, int option, int value);
  * partial tiles of the projections and the attention partials.  Contents
  * need no initialisation (the step zeroes its arrival counters in its first
  * kernel, the memset removal of the post's optimisation history).
- * PKV_E_ARG for NULL arguments or sizes below 1. */
+ * PKV_E_ARG for NULL arguments or sizes below 1; PKV_E_UNSUPPORTED for
+ * max_context above 262144 or batch x Hkv x ceil(max_context / 128) above
+ * 2^30. */
 pkv_status pkv_step_workspace_bytes(const pkv_model* model, const pkv_cache* cache, int batch,
                                     int max_context, size_t* bytes);
 

@@ -142,6 +142,8 @@ pkv_status pkv_attn_workspace_bytes(const pkv_cache* cache, int batch, int num_q
   const int hkv = cache->desc.num_kv_heads;
   if (num_q_heads < hkv || num_q_heads % hkv) return fail(PKV_E_ARG, "num_q_heads must be a multiple of num_kv_heads");
   if (num_q_heads / hkv > kMaxGroup) return fail(PKV_E_UNSUPPORTED, "more than 16 query heads per KV head");
+  if (max_context > kAttnMaxContext) return fail(PKV_E_UNSUPPORTED, "max_context above 262144");
+  if (!attn_grid_fits(batch, hkv, max_context)) return fail(PKV_E_UNSUPPORTED, "batch x KV heads x partitions of max_context above 2^30 workgroups");
   *bytes = attn_standalone_bytes(attn_plan(batch, num_q_heads, hkv, cache->desc.head_dim, cache->elt(), max_context));
   return PKV_OK;
 }

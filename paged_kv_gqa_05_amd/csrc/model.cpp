@@ -162,6 +162,7 @@ pkv_status check_step(const pkv_model* m, const pkv_cache* cache, const int32_t*
     return fail(PKV_E_ARG, "max_context must be in [1, max_positions]");
   if (max_context > kAttnMaxContext) return fail(PKV_E_UNSUPPORTED, "max_context above 262144");
   if (bt_stride < ceil_div(max_context, kBlock)) return fail(PKV_E_ARG, "bt_stride < ceil(max_context / 16)");
+  if (!attn_grid_fits(batch, cd.num_kv_heads, max_context)) return fail(PKV_E_UNSUPPORTED, "batch x KV heads x partitions of max_context above 2^30 workgroups");
   *plan = attn_plan(batch, m->d.num_q_heads, m->d.num_kv_heads, m->d.head_dim, cache_elt(cd), max_context);
   const StepBuffers need = carve(m, batch, *plan, nullptr);
   if (!ws || ws_bytes < need.total)
@@ -406,6 +407,8 @@ pkv_status pkv_step_workspace_bytes(const pkv_model* m, const pkv_cache* cache, 
   if (!m || !cache || !bytes) return fail(PKV_E_ARG, "NULL argument");
   if (batch < 1 || max_context < 1) return fail(PKV_E_ARG, "batch and max_context must be >= 1");
   const pkv_cache_desc& cd = cache->desc;
+  if (max_context > kAttnMaxContext) return fail(PKV_E_UNSUPPORTED, "max_context above 262144");
+  if (!attn_grid_fits(batch, cd.num_kv_heads, max_context)) return fail(PKV_E_UNSUPPORTED, "batch x KV heads x partitions of max_context above 2^30 workgroups");
   const AttnPlan plan =
       attn_plan(batch, m->d.num_q_heads, m->d.num_kv_heads, m->d.head_dim, cache_elt(cd), max_context);
   *bytes = carve(m, batch, plan, nullptr).total;

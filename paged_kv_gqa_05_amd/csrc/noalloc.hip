@@ -59,6 +59,7 @@ extern "C" pkv_status pkv_paged_attn_decode_noalloc(const pkv_cache* cache, int 
   if (max_context < 1) return fail(PKV_E_ARG, "max_context must be >= 1");
   if (max_context > kAttnMaxContext) return fail(PKV_E_UNSUPPORTED, "max_context above 262144");
   if (bt_stride < ceil_div(max_context, kBlock)) return fail(PKV_E_ARG, "bt_stride < ceil(max_context / 16)");
+  if (!attn_grid_fits(batch, cache->desc.num_kv_heads, max_context)) return fail(PKV_E_UNSUPPORTED, "batch x KV heads x partitions of max_context above 2^30 workgroups");
   if (!q || !out) return fail(PKV_E_ARG, "q / out is NULL");
   const pkv_cache_desc& d = cache->desc;
   if (num_q_heads < d.num_kv_heads || num_q_heads % d.num_kv_heads)

@@ -43,6 +43,13 @@ pkv_status hip_fail(hipError_t e, const char* what);
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Calls whose attention could need more than 2^30 workgroups (batch x Hkv x
+// the partitions of max_context at the smallest partition, 128 tokens) are
+// refused, so that grid sizes and workgroup indices stay within int.
+inline bool attn_grid_fits(int batch, int hkv, int max_context) {
+  return (long long)batch * hkv * ceil_div(max_context, 128) <= (1LL << 30);
+}
+
 // ---------------------------------------------------------------- attention
 struct AttnPlan {
   int waves;        // waves per workgroup (4 or 8)

@@ -53,6 +53,11 @@ def test_cache_bytes_and_layout():
     assert lib.pkv_attn_workspace_bytes(h, 64, 12, 2048, C.byref(ws)) == 0 and ws.value > 0
     assert lib.pkv_attn_workspace_bytes(h, 64, 7, 2048, C.byref(ws)) == 1        # 7 % 2 != 0
     assert lib.pkv_attn_workspace_bytes(h, 64, 34, 2048, C.byref(ws)) == 2       # 17 per group
+    # the attention grid bound: batch x Hkv x ceil(max_context / 128) <= 2^30
+    assert lib.pkv_attn_workspace_bytes(h, (1 << 30) // (2 * 2048), 12, 262144, C.byref(ws)) == 0
+    assert lib.pkv_attn_workspace_bytes(h, (1 << 30) // (2 * 2048) + 1, 12, 262144, C.byref(ws)) == 2
+    assert b"2^30" in lib.pkv_last_error()
+    assert lib.pkv_attn_workspace_bytes(h, 64, 12, 262145, C.byref(ws)) == 2
     lib.pkv_kv_cache_destroy(h)
 
 
