@@ -346,8 +346,14 @@ def prefill(cfg, weights, k_pools, v_pools, tokens, seq_starts, prior_lens, bloc
 
 
 def greedy_argmax(logits):
-    """Greedy token: index of the largest f16 logit, lowest index on ties."""
-    return np.argmax(np.asarray(logits), axis=-1).astype(np.int32)
+    """Greedy token per row (reading R10): the lowest index among the largest
+    f16 logits, a NaN never winning (so -inf beats NaN); 0 for a row of NaNs
+    only."""
+    x = np.asarray(logits, dtype=np.float64)
+    nan = np.isnan(x)
+    xm = np.where(nan, -np.inf, x)
+    hit = (xm == xm.max(axis=-1, keepdims=True)) & ~nan
+    return np.where(hit.any(axis=-1), np.argmax(hit, axis=-1), 0).astype(np.int32)
 
 
 # ---------------------------------------------------------------- full sequence

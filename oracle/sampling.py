@@ -14,7 +14,8 @@ taken here, step by step:
          x = x / r if x > 0 else x * r      (repetition penalty r; 1 = off)
          x = (x - f * c) - p                (frequency f, presence p; 0 = off)
      and the result is rounded to f16, like the logits it replaces.
-  1. temperature <= 0: the greedy token (lowest index of the largest logit).
+  1. temperature <= 0: the greedy token (lowest index among the largest
+     logits, a NaN never winning; 0 for a row of NaNs only).
   2. Each finite logit x gets an integer weight W(x) = floor(2^40 E(y)) with
      y = (x - m) * (1 / T) in float32 (m = the largest finite logit) and E the
      float32 exponential of ``exp_f32`` below, so every mass and every
@@ -141,8 +142,12 @@ def sample_row(logits, temperature, top_k, top_p, u):
     """The sampled token id for one row of f16 logits (steps 1-5)."""
     x = _key_order(logits)
     if not (float(temperature) > 0.0):
-        finite = np.where(np.isnan(x), -np.inf, x)
-        return int(np.flatnonzero(finite == finite.max())[0])
+        # the greedy token: lowest index among the largest logits, a NaN never
+        # winning (-inf beats NaN); 0 when every logit is NaN
+        valid = ~np.isnan(x)
+        if not valid.any():
+            return 0
+        return int(np.flatnonzero(valid & (x == x[valid].max()))[0])
     ids, w = candidates(logits, temperature, top_k, top_p)
     if ids.size == 0:
         return 0

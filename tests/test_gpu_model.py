@@ -217,10 +217,21 @@ def test_argmax_kernel(lib, vocab):
     lg[3, 100] = np.nan
     lg[4, vocab - 1] = 40.0                # the row's very last logit
     lg[5, [vocab - 1, vocab - 9]] = 35.0   # a tie inside the last vector and the one before
-    out = torch.empty(7, dtype=torch.int32, device="cuda")
+    # NaN never wins: -inf beats a leading NaN, a row of NaNs gives 0, +inf wins
+    extra = np.full((4, vocab), -np.inf, np.float16)
+    extra[0, 0] = np.nan
+    extra[1, :] = np.nan
+    extra[2, :] = rng.standard_normal(vocab).astype(np.float16)
+    extra[2, [0, vocab // 2]] = np.nan
+    extra[2, vocab - 2] = np.inf
+    extra[3, [1, 2]] = np.nan
+    lg = np.concatenate([lg, extra])
+    out = torch.empty(lg.shape[0], dtype=torch.int32, device="cuda")
     lib.argmax(dev(lg), out)
     torch.cuda.synchronize()
-    assert out.cpu().numpy().tolist() == oracle.greedy_argmax(np.nan_to_num(lg, nan=-np.inf)).tolist()
+    want = oracle.greedy_argmax(lg)
+    assert want[7:].tolist() == [1, 0, vocab - 2, 0]
+    assert out.cpu().numpy().tolist() == want.tolist()
 
 
 def test_graph_replay_matches_eager_and_sees_new_metadata(lib):

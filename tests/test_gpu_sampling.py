@@ -67,6 +67,41 @@ def test_sample_without_lens_and_uniform_edges(lib):
             assert got[b] == ids[np.nonzero(w > 0)[0][0]], b
 
 
+def test_sample_degenerate_rows(lib):
+    """Rows with no finite logit (token 0 when sampling), NaN before -inf at
+    temperature 0 (the -inf wins), a +inf logit (never kept when sampling,
+    the greedy winner), all-equal logits (ties kept at both thresholds) and a
+    single finite logit among -inf: the sampled token equals the oracle's."""
+    V = 1000
+    rng = np.random.default_rng(31)
+    rows, params = [], []
+    def add(row, t, k, p, u):
+        rows.append(np.asarray(row, np.float16))
+        params.append((t, k, p, u))
+    ninf = np.full(V, -np.inf)
+    nan = np.full(V, np.nan)
+    lead_nan = ninf.copy(); lead_nan[0] = np.nan
+    pinf = rng.standard_normal(V); pinf[[3, 400]] = np.inf; pinf[7] = np.nan
+    one = ninf.copy(); one[500] = 1.25
+    flat = np.full(V, 1.5)
+    for t in (0.0, 0.7):
+        add(ninf, t, -1, 1.0, 0.3)
+        add(nan, t, 5, 0.9, 0.3)
+        add(lead_nan, t, -1, 0.5, 0.6)
+        add(pinf, t, -1, 1.0, 0.4)
+        add(pinf, t, 10, 0.8, 0.9)
+        add(one, t, 5, 0.2, 0.99)
+        add(flat, t, 3, 0.5, 0.73)
+        add(flat, t, -1, 0.0, 0.11)
+    lg = np.stack(rows)
+    t, k, p, u = (np.array(c, dt) for c, dt in zip(zip(*params), (np.float32, np.int32, np.float32, np.float32)))
+    case = inp.SamplingCase(lg, t, k, p, u, np.ones(len(rows), np.int32))
+    got = run_sample(lib, case)
+    want = oracle_tokens(case)
+    assert want[:3].tolist() == [0, 0, 1] and want[8:11].tolist() == [0, 0, 0]
+    assert np.array_equal(got, want), list(zip(got.tolist(), want.tolist()))
+
+
 def test_sample_distribution_matches_softmax(lib):
     """One small row repeated with evenly spaced uniforms: the token counts
     follow softmax(z) restricted to the top-k / top-p set."""

@@ -20,7 +20,27 @@ def test_temperature_zero_is_greedy():
     lg[1, [7, 200]] = 20.0            # tie: lowest index
     lg[2, 50] = np.nan
     got = sample(lg, [0.0] * 5, [-1] * 5, [1.0] * 5, [0.3] * 5)
-    assert got.tolist() == greedy_argmax(np.nan_to_num(lg, nan=-np.inf)).tolist()
+    assert got.tolist() == greedy_argmax(lg).tolist()
+
+
+# Reading R10 by hand: the lowest index among the largest logits, a NaN never
+# winning (so -inf beats NaN), token 0 for a row of NaNs only.
+GREEDY_CORNERS = [
+    ([np.nan, -np.inf, -np.inf], 1),
+    ([np.nan, np.nan, np.nan], 0),
+    ([-np.inf, np.nan, -np.inf], 0),
+    ([1.0, np.nan, 3.0, 3.0], 2),
+    ([np.nan, np.inf, 5.0, np.inf], 1),
+    ([-0.0, 0.0, np.nan], 0),
+    ([np.nan, -2.0, -1.0, -1.0], 2),
+]
+
+
+@pytest.mark.parametrize("row,tok", GREEDY_CORNERS)
+def test_greedy_corners_by_hand(row, tok):
+    lg = np.array(row, np.float16)
+    assert int(greedy_argmax(lg[None])[0]) == tok
+    assert sample_row(lg, 0.0, -1, 1.0, 0.5) == tok
 
 
 @pytest.mark.parametrize("u", [0.0, 0.4, 0.999])
