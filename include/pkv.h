@@ -328,7 +328,9 @@ pkv_status pkv_layer_op(const pkv_model* model, pkv_cache* cache, int layer, int
                         int max_context, void* workspace, size_t workspace_bytes, pkv_stream_t stream);
 
 /* One decode step: h = embed[token_ids[b]], every layer, then
- * logits = W_lm RMSNorm(h) * w_final_norm.  token_ids int32 [batch];
+ * logits = W_lm RMSNorm(h) * w_final_norm.  token_ids int32 [batch]; an id
+ * outside [0, V) (such as the -1 pkv_argmax gives an inactive row) embeds as
+ * a zero row and is never read from the table (the same in pkv_prefill);
  * logits f16 [batch][V]; hidden_out (nullable) f16 [batch][H] gets the final
  * pre-norm hidden state.  Appends each row's token to the cache at
  * pos = context_lens[b] - 1 in every layer (f16 or fp8 caches, as

@@ -48,6 +48,7 @@ from .decoder import (
     decode_layer,
     decode_layer_xr,
     decode_step,
+    embed_rows,
     greedy_argmax,
     causal_forward,
     prefill,
@@ -57,5 +58,5 @@ __all__ = [
     "e4m3_decode", "e4m3_encode", "e4m3_quantize", "e4m3_table", "apply_penalties", "candidates", "draw",
     "exp_f32", "sample", "sample_penalized", "sample_row", "weight_fixed", "ModelConfig", "rmsnorm", "silu", "rope",
     "rope_angles", "paged_attention", "paged_attention_batch", "kv_append",
-    "decode_layer", "decode_layer_xr", "decode_step", "greedy_argmax", "causal_forward", "prefill",
+    "decode_layer", "decode_layer_xr", "decode_step", "embed_rows", "greedy_argmax", "causal_forward", "prefill",
 ]

@@ -294,6 +294,18 @@ def decode_layer_xr(cfg, lw, x, r, k_pool, v_pool, block_tables, ctx_lens, acc=n
     return down.astype(F16), h1
 
 
+def embed_rows(embed, tokens):
+    """The embedding rows of the tokens, f16 [B, H] (reading R25): a token id
+    outside [0, V), such as the -1 the greedy argmax gives an inactive row,
+    embeds as a zero row."""
+    e = np.asarray(embed)
+    t = np.asarray(tokens, dtype=np.int64)
+    ok = (t >= 0) & (t < e.shape[0])
+    h = e[np.where(ok, t, 0)].astype(F16)
+    h[~ok] = 0
+    return h
+
+
 def decode_step(cfg, weights, k_pools, v_pools, tokens, block_tables, ctx_lens,
                 acc=np.float64, k_scales=None, v_scales=None):
     """Embedding -> every layer -> final RMSNorm -> LM head.
@@ -303,7 +315,7 @@ def decode_step(cfg, weights, k_pools, v_pools, tokens, block_tables, ctx_lens,
     place (E4M3 pools take per-layer k_scales / v_scales).  Returns
     (logits [B, V] f16, final hidden [B, H] f16).
     """
-    h = np.asarray(weights["embed"])[np.asarray(tokens, dtype=np.int64)].astype(F16)
+    h = embed_rows(weights["embed"], tokens)
     for li, lw in enumerate(weights["layers"]):
         ks = None if k_scales is None else k_scales[li]
         vs = None if v_scales is None else v_scales[li]
@@ -335,7 +347,7 @@ def prefill(cfg, weights, k_pools, v_pools, tokens, seq_starts, prior_lens, bloc
     j = np.arange(starts[-1]) - starts[seq_of]
     lens = (np.asarray(prior_lens, dtype=np.int64)[seq_of] + j + 1).astype(np.int32)
     rows_bt = np.asarray(block_tables)[seq_of]
-    h = np.asarray(weights["embed"])[np.asarray(tokens, dtype=np.int64)].astype(F16)
+    h = embed_rows(weights["embed"], tokens)
     for li, lw in enumerate(weights["layers"]):
         ks = None if k_scales is None else k_scales[li]
         vs = None if v_scales is None else v_scales[li]
@@ -371,7 +383,7 @@ def causal_forward(cfg, weights, tokens, acc=np.float64):
     tok = np.asarray(tokens, dtype=np.int64)
     t_n = tok.shape[0]
     pos = np.arange(t_n)
-    h = np.asarray(weights["embed"])[tok].astype(F16)
+    h = embed_rows(weights["embed"], tok)
     ks, vs = [], []
     mask = np.tril(np.ones((t_n, t_n), dtype=bool))
     for lw in weights["layers"]:

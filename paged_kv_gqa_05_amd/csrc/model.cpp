@@ -292,7 +292,7 @@ hipError_t run_step(const pkv_model* m, pkv_cache* cache, const int32_t* tokens,
                     int bt_stride, const int32_t* lens, int batch, void* logits, _Float16* h,
                     const StepBuffers& sb, const AttnPlan& plan, hipStream_t s) {
   const pkv_model_desc& d = m->d;
-  hipError_t e = launch_embed(m->embed, tokens, h, batch, d.hidden, sb.counters, sb.n_counters, s);
+  hipError_t e = launch_embed(m->embed, d.vocab, tokens, h, batch, d.hidden, sb.counters, sb.n_counters, s);
   if (e != hipSuccess) return e;
   PersistArgs pa{};
   if (persistent_args(m, cache, h, bt, bt_stride, lens, batch, sb, plan, &pa)) {
@@ -526,7 +526,7 @@ pkv_status pkv_prefill(const pkv_model* m, pkv_cache* cache, const int32_t* toke
   const hipStream_t s = static_cast<hipStream_t>(stream);
   PKV_HIP(launch_prefill_rows(seq_starts, prior_lens, bt, bt_stride, n_seqs, n_tokens, pb.stride_tok, max_context,
                               pb.lens_tok, pb.bt_tok, pb.last_idx, s));
-  PKV_HIP(launch_embed(m->embed, tokens, sb.h, n_tokens, d.hidden, sb.counters, sb.n_counters, s));
+  PKV_HIP(launch_embed(m->embed, d.vocab, tokens, sb.h, n_tokens, d.hidden, sb.counters, sb.n_counters, s));
   PrefillAttnArgs pre{};
   pre.seq_starts = seq_starts; pre.prior_lens = prior_lens; pre.bt = bt; pre.bt_stride = bt_stride;
   pre.items = pb.items; pre.n_items = pb.n_items; pre.max_items = pb.max_items;
@@ -535,7 +535,7 @@ pkv_status pkv_prefill(const pkv_model* m, pkv_cache* cache, const int32_t* toke
   for (int l = 0; l < d.num_layers; ++l)
     PKV_HIP(run_layer(m, cache, l, sb.h, pb.bt_tok, pb.stride_tok, pb.lens_tok, n_tokens, sb, plan, s, &pre));
   // the last new token of every sequence -> final RMSNorm -> LM head
-  PKV_HIP(launch_embed(sb.h, pb.last_idx, pb.h_last, n_seqs, d.hidden, sb.counters, sb.n_counters, s));
+  PKV_HIP(launch_embed(sb.h, n_tokens, pb.last_idx, pb.h_last, n_seqs, d.hidden, sb.counters, sb.n_counters, s));
   LinArgs a{};
   a.eps = d.rms_eps;
   a.A = pb.h_last; a.lda = d.hidden; a.K = d.hidden; a.M = n_seqs;

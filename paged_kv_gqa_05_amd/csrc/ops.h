@@ -4,7 +4,9 @@
 
 namespace pkv {
 
-hipError_t launch_embed(const void* table, const int32_t* tokens, void* h, int batch, int hidden,
+// h[b] = table[tokens[b]] for b < batch (a zero row for an id outside
+// [0, table_rows)); also zeroes zero_n ints at zero_p.
+hipError_t launch_embed(const void* table, int table_rows, const int32_t* tokens, void* h, int batch, int hidden,
                         int* zero_p, int zero_n, hipStream_t s);
 // With counts (int32 [batch][vocab]): penalties applied in place to
 // penalized_logits (the same buffer as logits) first, and each active row's

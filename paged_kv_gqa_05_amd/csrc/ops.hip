@@ -10,12 +10,17 @@ namespace {
 typedef _Float16 h16;
 
 // Also zeroes zero_n ints at zero_p (the split-K arrival counters of the step).
-__global__ void embed_kernel(const h16* __restrict__ table, const int32_t* __restrict__ tokens,
+__global__ void embed_kernel(const h16* __restrict__ table, int rows, const int32_t* __restrict__ tokens,
                              h16* __restrict__ h, int hidden, int* __restrict__ zero_p, int zero_n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < zero_n; i += gridDim.x * blockDim.x) zero_p[i] = 0;
   const int b = blockIdx.x;
-  const h16* src = table + (size_t)tokens[b] * hidden;
+  const int tok = tokens[b];
   h16* dst = h + (size_t)b * hidden;
+  if (tok < 0 || tok >= rows) {  // outside the table (the argmax's -1 of an inactive row): a zero row
+    for (int i = threadIdx.x * 8; i < hidden; i += blockDim.x * 8) *reinterpret_cast<uint4*>(dst + i) = uint4{0, 0, 0, 0};
+    return;
+  }
+  const h16* src = table + (size_t)tok * hidden;
   for (int i = threadIdx.x * 8; i < hidden; i += blockDim.x * 8)
     *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(src + i);
 }
@@ -135,9 +140,9 @@ hipError_t launch_prefill_rows(const int32_t* seq_starts, const int32_t* prior_l
   return hipGetLastError();
 }
 
-hipError_t launch_embed(const void* table, const int32_t* tokens, void* h, int batch, int hidden,
+hipError_t launch_embed(const void* table, int table_rows, const int32_t* tokens, void* h, int batch, int hidden,
                         int* zero_p, int zero_n, hipStream_t s) {
-  hipLaunchKernelGGL(embed_kernel, dim3(batch), dim3(256), 0, s, static_cast<const h16*>(table), tokens,
+  hipLaunchKernelGGL(embed_kernel, dim3(batch), dim3(256), 0, s, static_cast<const h16*>(table), table_rows, tokens,
                      static_cast<h16*>(h), hidden, zero_p, zero_n);
   return hipGetLastError();
 }

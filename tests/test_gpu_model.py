@@ -206,6 +206,20 @@ def test_decode_step_parity_and_greedy(lib, batch):
     assert agree / total >= 0.99
 
 
+def test_decode_step_out_of_range_tokens_embed_as_zero(lib):
+    """Token ids outside [0, V) (the -1 the argmax gives an inactive row, the
+    vocabulary size itself, a large negative id) embed as zero rows on both
+    sides (reading R25); the other rows are unaffected."""
+    rig = StepRig(lib, MID, 5, seed=2011, prompt_len=4, max_context=32)
+    for t in range(3):
+        tok = rig.prompts[:, t].astype(np.int32).copy()
+        tok[1], tok[3], tok[4] = -1, MID.vocab + t, -(1 << 20)
+        lg, hd = rig.gpu_step(tok)
+        rl, rh = rig.oracle_step(tok)
+        assert_parity(lg, rl, f"logits step {t}")
+        assert_parity(hd, rh, f"hidden step {t}")
+
+
 @pytest.mark.parametrize("vocab", [151936, 152064, 163840, 163848, 1000, 999])
 def test_argmax_kernel(lib, vocab):
     # vocab 163840 fills exactly one round of loads per thread, 163848 needs a

@@ -22,7 +22,7 @@ import numpy as np
 import torch
 import torch.nn.functional as F
 
-from oracle import ModelConfig, decode_step, causal_forward, decode_layer, decode_layer_xr, greedy_argmax, prefill
+from oracle import ModelConfig, decode_step, causal_forward, decode_layer, decode_layer_xr, embed_rows, greedy_argmax, prefill
 import pkv_inputs as inp
 
 SHAPE = inp.Shape(hidden=128, n_q_heads=4, n_kv_heads=2, head_dim=32, ffn=160, vocab=300, n_layers=2)
@@ -137,6 +137,14 @@ def test_layer_append_touches_only_its_slot():
             expect[case["block_tables"][b][(c - 1) // BS], :, (c - 1) % BS, :] = True
     assert np.array_equal(changed_k, expect)
     assert not np.any(np.isnan(kp[expect]))
+
+
+def test_embed_rows_out_of_range_ids_are_zero_rows():
+    """Reading R25 by hand: ids outside [0, V) embed as zero rows."""
+    table = np.arange(12, dtype=np.float16).reshape(4, 3)  # V = 4, H = 3
+    got = embed_rows(table, [-1, 0, 4, 2, 3, -7])
+    want = np.array([[0, 0, 0], [0, 1, 2], [0, 0, 0], [6, 7, 8], [9, 10, 11], [0, 0, 0]], np.float16)
+    assert got.dtype == np.float16 and np.array_equal(got, want)
 
 
 def test_argmax_lowest_index_on_ties():
