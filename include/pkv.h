@@ -54,6 +54,15 @@
  *   covers positions [0, context_lens[b]).  context_lens[b] == 0 marks an
  *   inactive row (no append; attention output 0).  Block-table entries at
  *   index >= ceil(context_lens[b] / BS) are never read.
+ *   Caller errors in this device metadata (pkv_validate_metadata reports
+ *   them on the host) never make a kernel access memory outside the pool,
+ *   the tables or the workspace: a block id outside [0, num_blocks) among
+ *   the entries a call uses is read as block 0 and an append to it is
+ *   dropped; a context length above the call's max_context is taken as
+ *   max_context by the attention, and its append is dropped when its slot
+ *   lies past the row's table; a token id outside [0, V) embeds as a zero
+ *   row.  Such rows' results are unspecified; the call's other rows are
+ *   unaffected.
  *
  * Query heads: head h reads KV head h / (Hq / Hkv) (contiguous groups);
  * Hq / Hkv <= 16.

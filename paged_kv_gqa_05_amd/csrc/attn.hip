@@ -126,6 +126,7 @@ AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int 
   }
   p.waves = waves;
   p.nt = nt;
+  p.max_context = mc;
   p.part = 16 * nt * waves;
   p.n_parts_max = ceil_div(mc, p.part);
   p.grid = batch * hkv * p.n_parts_max;

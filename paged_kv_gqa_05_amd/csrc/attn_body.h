@@ -33,6 +33,8 @@ struct SplitParams {
   float* ws_o;     // [B][Hq][P][D] unnormalised O per partition
   int bt_stride;
   int batch, hq, hkv, group, part, n_parts_max;
+  int num_blocks;    // blocks in the pool: a block id outside [0, num_blocks) is read as block 0
+  int max_context;   // a longer context length is taken as max_context
   int merge_poll;    // every workgroup of the call is resident at once: the first
                      // partition of a row waits for the others and merges
   unsigned long long poll_ticks;  // its wait limit (wall-clock ticks; 0: publish at once)
@@ -152,7 +154,9 @@ __device__ __forceinline__ void attn_body(const SplitParams& p, const int wg) {
   // issued together, before the context length is known: the block-table
   // entries of this wave's blocks (clamped inside the row) and the query rows
   const int* btrow = p.bt + (size_t)b * p.bt_stride;
-  const int blk_l = btrow[min(tok0 / kBlock + wave + kWaves * min(lane, NT - 1), p.bt_stride - 1)];
+  // (a block id outside the pool, a caller error, reads block 0 instead)
+  const int blk_raw = btrow[min(tok0 / kBlock + wave + kWaves * min(lane, NT - 1), p.bt_stride - 1)];
+  const int blk_l = (unsigned)blk_raw < (unsigned)p.num_blocks ? blk_raw : 0;
   h16x8 qf[D / 32];
   {
     const h16* qrow = p.q + ((size_t)b * p.hq + hbase + min(n, p.group - 1)) * D;
@@ -161,7 +165,7 @@ __device__ __forceinline__ void attn_body(const SplitParams& p, const int wg) {
       qf[s] = COH ? ld_agent_h8(qrow + 8 * q_chunk<FP8>(s, q4))
                   : *reinterpret_cast<const h16x8*>(qrow + 8 * q_chunk<FP8>(s, q4));
   }
-  const int c = p.lens[b];
+  const int c = min(max(p.lens[b], 0), p.max_context);  // (out-of-range lengths clamped)
   if (tok0 >= c) {  // beyond the row's context (or an inactive row)
     if (c == 0 && g == 0 && part_idx == 0) {
       for (int idx = tid; idx < p.hq * D; idx += kThreads) {
@@ -563,6 +567,8 @@ inline SplitParams make_split_params(const AttnArgs& a, const AttnPlan& plan) {
   sp.group = a.hq / a.hkv;
   sp.part = plan.part;
   sp.n_parts_max = plan.n_parts_max;
+  sp.num_blocks = a.num_blocks;
+  sp.max_context = plan.max_context;
   // the 8-wave plans keep the whole grid within one workgroup per CU
   sp.merge_poll = plan.waves == 8 ? 1 : 0;
   sp.poll_ticks = attn_merge_wait_ticks;

@@ -129,7 +129,7 @@ pkv_status pkv_kv_append(pkv_cache* cache, int layer, const void* k, const void*
   PKV_HIP(launch_kv_append(cache->k_pool(layer), cache->v_pool(layer), k, v, block_tables, bt_stride,
                            context_lens, batch, cache->desc.num_kv_heads, cache->desc.head_dim, fp8,
                            fp8 ? cache->k_scales[layer] : 1.f, fp8 ? cache->v_scales[layer] : 1.f,
-                           static_cast<hipStream_t>(stream)));
+                           cache->desc.num_blocks, static_cast<hipStream_t>(stream)));
   return PKV_OK;
 }
 
@@ -178,6 +178,7 @@ pkv_status pkv_paged_attn_decode(const pkv_cache* cache, int layer, const void* 
   a.hq = num_q_heads;
   a.hkv = d.num_kv_heads;
   a.head_dim = d.head_dim;
+  a.num_blocks = d.num_blocks;
   a.fp8 = d.dtype == PKV_KV_FP8_E4M3;
   a.scale = scale;
   a.k_scale = a.fp8 ? cache->k_scales[layer] : 1.f;

@@ -14,12 +14,16 @@ __global__ void kv_append_kernel(void* __restrict__ kpool, void* __restrict__ vp
                                  const _Float16* __restrict__ k, const _Float16* __restrict__ v,
                                  const int32_t* __restrict__ bt, int bt_stride,
                                  const int32_t* __restrict__ lens, int hkv, int head_dim, int fp8,
-                                 float k_scale, float v_scale) {
+                                 float k_scale, float v_scale, int num_blocks) {
   const int b = blockIdx.x;
   const int c = lens[b];
   if (c <= 0) return;
   const int pos = c - 1;
+  // a length beyond the block table or a block id outside the pool (caller
+  // errors) stores nothing rather than writing outside the pool
+  if (pos / kBlock >= bt_stride) return;
   const int blk = bt[(size_t)b * bt_stride + pos / kBlock];
+  if ((unsigned)blk >= (unsigned)num_blocks) return;
   const int slot = pos % kBlock;
   for (int idx = threadIdx.x; idx < hkv * head_dim; idx += blockDim.x) {
     const int g = idx / head_dim, d = idx - g * head_dim;
@@ -33,10 +37,11 @@ __global__ void kv_append_kernel(void* __restrict__ kpool, void* __restrict__ vp
 
 hipError_t launch_kv_append(void* k_pool, void* v_pool, const void* k, const void* v,
                             const int32_t* bt, int bt_stride, const int32_t* lens, int batch,
-                            int hkv, int head_dim, bool fp8, float k_scale, float v_scale, hipStream_t s) {
+                            int hkv, int head_dim, bool fp8, float k_scale, float v_scale, int num_blocks,
+                            hipStream_t s) {
   hipLaunchKernelGGL(kv_append_kernel, dim3(batch), dim3(256), 0, s, k_pool, v_pool,
                      static_cast<const _Float16*>(k), static_cast<const _Float16*>(v), bt, bt_stride, lens,
-                     hkv, head_dim, fp8 ? 1 : 0, k_scale, v_scale);
+                     hkv, head_dim, fp8 ? 1 : 0, k_scale, v_scale, num_blocks);
   return hipGetLastError();
 }
 

@@ -33,6 +33,8 @@ struct RopeArgs {
   int hq, hkv, d;
   int fp8;                // E4M3 cache: store codes of f16(x) / scale
   float k_scale, v_scale;
+  int num_blocks;         // blocks in the pool: an id outside [0, num_blocks) is never written
+  int max_pos;            // rows of cos_sin
 };
 
 // Weight rows of output pair p.
@@ -51,21 +53,25 @@ __device__ __forceinline__ int pair_row(int epi_rope, int n_out, int head_dim, i
 // trip): the row's context length, then its position's block id and the
 // (cos, sin) of each pair, then stores only.
 struct RopeRow {
-  int c, pos, blk;
+  int c, pos, blk;  // blk -1: nothing stored (inactive row, or no valid slot)
 };
 __device__ __forceinline__ RopeRow rope_row_len(const RopeArgs& ra, int m) {
   RopeRow r;
   r.c = ra.lens[m];
   r.pos = r.c > 0 ? r.c - 1 : 0;
-  r.blk = 0;
+  r.blk = -1;
   return r;
 }
+// A length beyond the block table or a block id outside the pool (caller
+// errors) stores nothing rather than writing outside the pool.
 __device__ __forceinline__ void rope_row_blk(const RopeArgs& ra, int m, RopeRow& r) {
-  r.blk = r.c > 0 ? ra.bt[(size_t)m * ra.bt_stride + r.pos / 16] : 0;
+  const int e = r.pos / 16;
+  const int blk = (r.c > 0 && e < ra.bt_stride) ? ra.bt[(size_t)m * ra.bt_stride + e] : -1;
+  r.blk = (unsigned)blk < (unsigned)ra.num_blocks ? blk : -1;
 }
 __device__ __forceinline__ float2 rope_cs(const RopeArgs& ra, const RopeRow& r, int p) {
   const int half = ra.d >> 1;
-  return ra.cos_sin[(size_t)r.pos * half + p % half];
+  return ra.cos_sin[(size_t)min(r.pos, ra.max_pos - 1) * half + p % half];
 }
 // Pair p of batch row m: y0, y1 are rows i and i + D/2 of a head with the
 // norm and the bias applied.  Rotates q and k heads at the row's position,
@@ -88,13 +94,13 @@ __device__ __forceinline__ void rope_put(const RopeArgs& ra, const RopeRow& r, i
         q[i] = (_Float16)o0;
         q[half + i] = (_Float16)o1;
       }
-    } else if (r.c > 0) {
+    } else if (r.blk >= 0) {
       const size_t tile = ((size_t)r.blk * ra.hkv + (head - ra.hq)) * 16 * ra.d;
       const int t = r.pos % 16;
       kv_store(ra.k_pool, tile + k_tile_off(ra.fp8, t, i), ra.fp8, ra.k_scale, o0);
       kv_store(ra.k_pool, tile + k_tile_off(ra.fp8, t, half + i), ra.fp8, ra.k_scale, o1);
     }
-  } else if (r.c > 0) {
+  } else if (r.blk >= 0) {
     const size_t tile = ((size_t)r.blk * ra.hkv + (head - ra.hq - ra.hkv)) * 16 * ra.d;
     const int t = r.pos % 16;
     kv_store(ra.v_pool, tile + v_tile_off(ra.fp8, t, i), ra.fp8, ra.v_scale, y0);

@@ -198,6 +198,8 @@ LinArgs layer_lin_args(const pkv_model* m, const pkv_cache* cache, int layer, in
       a.rope.fp8 = fp8;
       a.rope.k_scale = fp8 ? cache->k_scales[layer] : 1.f;
       a.rope.v_scale = fp8 ? cache->v_scales[layer] : 1.f;
+      a.rope.num_blocks = cache->desc.num_blocks;
+      a.rope.max_pos = d.max_positions;
       break;
     case PKV_OP_O:  // O projection + residual add
       a.A = sb.o; a.lda = qd; a.K = qd;
@@ -227,6 +229,7 @@ AttnArgs layer_attn_args(const pkv_model* m, const pkv_cache* cache, int layer, 
   at.k_pool = cache->k_pool(layer); at.v_pool = cache->v_pool(layer); at.q = sb.q; at.out = sb.o; at.lse = nullptr;
   at.bt = bt; at.bt_stride = bt_stride; at.lens = lens; at.batch = batch;
   at.hq = d.num_q_heads; at.hkv = d.num_kv_heads; at.head_dim = d.head_dim; at.fp8 = fp8;
+  at.num_blocks = cache->desc.num_blocks;
   at.scale = 1.0f / std::sqrt((float)d.head_dim);
   at.k_scale = fp8 ? cache->k_scales[layer] : 1.f;
   at.v_scale = fp8 ? cache->v_scales[layer] : 1.f;
@@ -251,6 +254,7 @@ hipError_t run_layer_op(const pkv_model* m, pkv_cache* cache, int layer, int op,
     pa.k_pool = at.k_pool; pa.v_pool = at.v_pool; pa.q = sb.q; pa.out = sb.o;
     pa.hq = at.hq; pa.hkv = at.hkv; pa.head_dim = at.head_dim; pa.fp8 = at.fp8;
     pa.scale = at.scale; pa.k_scale = at.k_scale; pa.v_scale = at.v_scale;
+    pa.num_blocks = at.num_blocks;
     return launch_prefill_attention(pa, s);
   }
   return launch_paged_attention(at, plan, s);

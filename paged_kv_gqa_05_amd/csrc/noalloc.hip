@@ -102,6 +102,7 @@ extern "C" pkv_status pkv_paged_attn_decode_noalloc(const pkv_cache* cache, int 
   a.hq = num_q_heads;
   a.hkv = d.num_kv_heads;
   a.head_dim = d.head_dim;
+  a.num_blocks = d.num_blocks;
   a.fp8 = d.dtype == PKV_KV_FP8_E4M3;
   a.scale = scale;
   a.k_scale = a.fp8 ? cache->k_scales[layer] : 1.f;

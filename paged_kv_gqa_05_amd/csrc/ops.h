@@ -35,6 +35,7 @@ struct PrefillAttnArgs {
   int32_t* n_items;
   int max_items;
   int n_seqs, n_tokens, hq, hkv, head_dim, max_context;
+  int num_blocks;  // blocks in the pool (ids outside it are read as block 0)
   bool fp8;
   float scale, k_scale, v_scale;
 };

@@ -57,6 +57,7 @@ struct AttnPlan {
   int part;         // tokens per partition (16 nt waves)
   int n_parts_max;  // partitions per (row, kv head) for max_context
   int grid;         // workgroups of the attention kernel
+  int max_context;  // the call's max_context (longer context lengths are taken as it)
   size_t counter_bytes;  // leading workspace bytes: [B][Hkv] int arrival counters,
                          // zero before the first call, left zero by every call
   size_t ws_bytes;  // workspace bytes (counters + partials of multi-partition rows)
@@ -101,6 +102,7 @@ struct AttnArgs {
   int bt_stride;
   const int32_t* lens;
   int batch, hq, hkv, head_dim;
+  int num_blocks;     // blocks in the pool (ids outside it are read as block 0)
   bool fp8;
   float scale;        // softmax scale
   float k_scale, v_scale;
@@ -112,6 +114,7 @@ hipError_t launch_paged_attention(const AttnArgs& a, const AttnPlan& p, hipStrea
 // ------------------------------------------------------------------ KV ops
 hipError_t launch_kv_append(void* k_pool, void* v_pool, const void* k, const void* v,
                             const int32_t* bt, int bt_stride, const int32_t* lens, int batch,
-                            int hkv, int head_dim, bool fp8, float k_scale, float v_scale, hipStream_t s);
+                            int hkv, int head_dim, bool fp8, float k_scale, float v_scale, int num_blocks,
+                            hipStream_t s);
 
 }  // namespace pkv

@@ -53,6 +53,7 @@ struct Params {
   const int2* items;
   const int32_t* n_items;
   int n_tokens, hq, hkv, group, max_context;
+  int num_blocks;    // blocks in the pool: a block id outside [0, num_blocks) is read as block 0
   float scale_log2;  // softmax scale * log2(e) * K dequant scale
   float v_scale;     // V dequant scale (1 for f16)
 };
@@ -211,7 +212,10 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(Params p) {
   for (int pg0 = 0; pg0 < n_pages; pg0 += NP) {
     Page<D, FP8> pg[NP];
 #pragma unroll
-    for (int t = 0; t < NP; ++t) pg[t].load(p, btrow[min(pg0 + t, n_pages - 1)], g, lane);
+    for (int t = 0; t < NP; ++t) {
+      const int blk = btrow[min(pg0 + t, n_pages - 1)];
+      pg[t].load(p, (unsigned)blk < (unsigned)p.num_blocks ? blk : 0, g, lane);
+    }
     // scores of the group's pages, log2 domain, causal mask per column
     float x[NP][4];
     float mt = -INFINITY;
@@ -318,6 +322,7 @@ hipError_t launch_prefill_attention(const PrefillAttnArgs& a, hipStream_t s) {
   p.hkv = a.hkv;
   p.group = group;
   p.max_context = a.max_context;
+  p.num_blocks = a.num_blocks;
   p.scale_log2 = a.scale * kLog2e * (a.fp8 ? a.k_scale : 1.0f);
   p.v_scale = a.fp8 ? a.v_scale : 1.0f;
   if (a.head_dim == 64) return a.fp8 ? launch_d<64, true>(p, a.max_items, s) : launch_d<64, false>(p, a.max_items, s);
