@@ -555,7 +555,7 @@ def main():
                          "kernel for scaling rocprof FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
 
