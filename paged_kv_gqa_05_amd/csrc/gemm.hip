@@ -135,10 +135,20 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(GemmParams p) {
   const int n_kc = (p.K + BK - 1) / BK;
   int mt, nt, sp = 0, splits = 1, kc_per = n_kc;
   if (li < p.full_per_xcd) {  // a whole tile
-    const int t = xcd * p.full_per_xcd + li;
-    if (t >= p.nt_full * p.n_mt) return;
-    mt = t % p.n_mt;
-    nt = t / p.n_mt;
+    if (p.blk_m > 0) {
+      // blocks of 32 tiles (blk_m along M), dealt round-robin to the XCDs:
+      // the 32 workgroups an XCD runs at once share their activation and
+      // weight rows through its L2
+      const int k = 8 * (li >> 5) + xcd, w = li & 31;
+      mt = (k % p.nbm) * p.blk_m + w % p.blk_m;
+      nt = (k / p.nbm) * (32 / p.blk_m) + w / p.blk_m;
+      if (mt >= p.n_mt || nt >= p.nt_full) return;
+    } else {
+      const int t = xcd * p.full_per_xcd + li;
+      if (t >= p.nt_full * p.n_mt) return;
+      mt = t % p.n_mt;
+      nt = t / p.n_mt;
+    }
   } else {  // a K range of a split tile
     const int u = xcd * p.per_xcd + (li - p.full_per_xcd);
     if (u >= p.split_items) return;
@@ -777,6 +787,19 @@ hipError_t launch_gemm(const LinArgs& a, int epi, const GemmPlan& pl, void* part
   gp.n_mt = pl.n_mt; gp.n_nt = pl.n_nt; gp.nt_full = pl.nt_full;
   gp.splits = pl.splits; gp.kc_per_split = pl.kc_per_split;
   gp.full_per_xcd = ceil_div(pl.nt_full * pl.n_mt, 8);
+  // grids of many rounds of whole tiles (prefill): blocks of 32 tiles, 4 x 8
+  // (8 x 4 for tiles wider than tall), so that an XCD's concurrent
+  // workgroups share both operands through its L2
+  if (pl.splits == 1 && pl.nt_full * pl.n_mt >= 4 * kCUs) {
+    gp.blk_m = pl.mt < pl.nt ? 8 : 4;
+    if (pl.n_mt >= gp.blk_m && pl.nt_full >= 32 / gp.blk_m) {
+      gp.nbm = ceil_div(pl.n_mt, gp.blk_m);
+      const int blocks = gp.nbm * ceil_div(pl.nt_full, 32 / gp.blk_m);
+      gp.full_per_xcd = ceil_div(blocks, 8) * 32;
+    } else {
+      gp.blk_m = 0;
+    }
+  }
   gp.split_items = pl.splits > 1 ? (pl.n_nt - pl.nt_full) * pl.n_mt * pl.splits : 0;
   gp.per_xcd = ceil_div(gp.split_items, 8);
   gp.counters = counters;

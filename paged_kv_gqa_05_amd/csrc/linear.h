@@ -157,6 +157,7 @@ struct GemmParams {
   float eps;
   int n_mt, n_nt, nt_full, splits, kc_per_split;
   int full_per_xcd, per_xcd, split_items;  // workgroups per XCD: whole tiles, then split parts
+  int blk_m, nbm;   // > 0: whole tiles in blocks of blk_m x (32 / blk_m) tiles, nbm blocks along M
   RopeArgs rope;
 };
 
