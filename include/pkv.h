@@ -434,7 +434,9 @@ pkv_status pkv_sample_penalized(void* logits, int batch, int vocab, const float*
  * graph: before each replay the caller rewrites the CONTENTS of token_ids,
  * block_tables and context_lens (ordered on the replay stream, rvLLM post
  * section "CUDA 그래프 리플레이").  Nothing is allocated inside the captured
- * region. */
+ * region.  The model, the cache and every buffer passed here must outlive the
+ * graph: a replay uses them as captured (options such as
+ * PKV_OPT_PERSISTENT_BATCH1 are read at capture time). */
 pkv_status pkv_graph_capture(const pkv_model* model, pkv_cache* cache, const int32_t* token_ids,
                              const int32_t* block_tables, int bt_stride,
                              const int32_t* context_lens, int batch, int max_context,
