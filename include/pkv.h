@@ -215,6 +215,17 @@ pkv_status pkv_paged_attn_decode_noalloc(const pkv_cache* cache, int layer, cons
  * paths give the same bits.  Always PKV_OK. */
 pkv_status pkv_debug_attn_merge_wait(unsigned long long ticks);
 
+/* Testing hook for the decode attention's work-list form (host only,
+ * process-wide, default 1).  A call with long rows (8 or more 512-token
+ * partitions at max_context) whose partitions would span several rounds of
+ * the device runs in work-list form: a grid of resident workgroups takes
+ * only the partitions inside each row's context, longest rows first, so no
+ * workgroup is spent on partitions past a shorter row's context and the rows
+ * with the most partials to merge merge early.  With 0 such calls run the
+ * direct grid of the same partitions.  Both forms give the same bits.
+ * Always PKV_OK. */
+pkv_status pkv_debug_attn_worklist(int enable);
+
 /* --------------------------------------------------------------------- model */
 
 typedef struct {

@@ -139,6 +139,12 @@ def debug_attn_merge_wait(ticks):
     _check(_lib.pkv_debug_attn_merge_wait(int(ticks)))
 
 
+def debug_attn_worklist(enable):
+    """Testing hook (process-wide): whether attention calls of several rounds of
+    workgroups run in work-list form (default True) or as the direct grid."""
+    _check(_lib.pkv_debug_attn_worklist(int(enable)))
+
+
 def paged_attn_decode_noalloc(cache, layer, q, out, block_tables, context_lens, max_context, scale, lse=None,
                               stream=None):
     """paged_attn_decode with the library's static per-GPU scratch instead of a

@@ -49,6 +49,7 @@ SIGNATURES = {
     "pkv_model_destroy": (None, [vp]),
     "pkv_model_set_option": (c_status, [vp, C.c_int, C.c_int]),
     "pkv_debug_attn_merge_wait": (c_status, [C.c_ulonglong]),
+    "pkv_debug_attn_worklist": (c_status, [C.c_int]),
     "pkv_step_workspace_bytes": (c_status, [vp, vp, C.c_int, C.c_int, C.POINTER(size_t)]),
     "pkv_decode_layer": (c_status, [vp, vp, C.c_int, vp, i32p, C.c_int, i32p, C.c_int, C.c_int,
                                     vp, size_t, vp]),

@@ -98,8 +98,11 @@ def build_host_sanitized():
 # defines, linked with the other objects of build().  attn_qk_valu computes
 # the f16 attention scores with v_dot2 on the VALU instead of the 16x16x32
 # MFMA (libpkv_attn_qk_valu.so; select it with PKV_LIB_PATH), to time that
-# choice against the MFMA form.
-VARIANTS = {"attn_qk_valu": (("attn.hip", "persist.hip"), ["-DPKV_ATTN_QK_VALU"])}
+# choice against the MFMA form.  attn_stamps records wall-clock stamps per
+# attention workgroup or work-list item (start, context known, partition
+# computed, end; read back with pkv_debug_attn_stamps), for timelines.
+VARIANTS = {"attn_qk_valu": (("attn.hip", "persist.hip"), ["-DPKV_ATTN_QK_VALU"]),
+            "attn_stamps": (("attn.hip",), ["-DPKV_ATTN_STAMPS"])}
 
 
 def build_variant(name):

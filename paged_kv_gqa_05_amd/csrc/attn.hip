@@ -54,6 +54,8 @@
 //    conversion instruction (exact: every E4M3 value is an f16 value); the
 //    per-tensor K scale is folded into the score scale and the V scale into
 //    the output.
+#include <algorithm>
+
 #include "attn_body.h"
 
 namespace pkv {
@@ -64,13 +66,57 @@ __global__ void __launch_bounds__(64 * kWaves, (attn_min_waves<NT, kWaves>())) a
   attn_body<D, FP8, NT, kWaves, false>(p, blockIdx.x);
 }
 
+// The work-list form (4 waves), a kernel of its own: its item loop needs more
+// registers than the direct form, whose residency must not change.
+template <int D, bool FP8, int NT, int W>
+__global__ void __launch_bounds__(64 * W) attn_wl_kernel(SplitParams p) {
+  attn_worklist<D, FP8, NT, W>(p);
+}
+
+// Workgroups of one configuration that the device holds at once (occupancy
+// query, cached per device).
+template <int D, bool FP8, int NT, int W>
+int resident_workgroups() {
+  static int cache[16] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 0;
+  if (cache[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_wl_kernel<D, FP8, NT, W>, 64 * W, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cache[dev] = per_cu * cus > 0 ? per_cu * cus : -1;
+  }
+  return cache[dev];
+}
+
 template <int D, bool FP8, int NT, int W>
 void launch_cfg(const SplitParams& sp, const AttnPlan& plan, hipStream_t s) {
   hipLaunchKernelGGL((attn_kernel<D, FP8, NT, W>), dim3(plan.grid), dim3(64 * W), 0, s, sp);
 }
 
+// The work-list form: as many workgroups as the device holds at once (any
+// other count gives the same result).
+template <int D, bool FP8, int W>
+void launch_worklist(SplitParams sp, const AttnPlan& plan, hipStream_t s) {
+  sp.worklist = 1;
+  const int resident = resident_workgroups<D, FP8, 8, W>();
+  const int grid = resident > 0 ? std::min(resident, plan.grid) : plan.grid;
+  hipLaunchKernelGGL((attn_wl_kernel<D, FP8, 8, W>), dim3(grid), dim3(64 * W), 0, s, sp);
+}
+
 template <int D, bool FP8>
 hipError_t launch_impl(const SplitParams& sp, const AttnPlan& plan, hipStream_t s) {
+  if (plan.worklist && attn_worklist_enabled) {
+    if constexpr (FP8) {
+      if (plan.waves == 8) {
+        launch_worklist<D, FP8, 8>(sp, plan, s);
+        return hipGetLastError();
+      }
+    }
+    launch_worklist<D, FP8, 4>(sp, plan, s);
+    return hipGetLastError();
+  }
   if (plan.waves == 8) {
     launch_cfg<D, FP8, 8, 8>(sp, plan, s);
   } else {
@@ -86,6 +132,7 @@ hipError_t launch_impl(const SplitParams& sp, const AttnPlan& plan, hipStream_t 
 }  // namespace
 
 unsigned long long attn_merge_wait_ticks = 10000;  // 100 us at the 100 MHz wall clock
+int attn_worklist_enabled = 1;
 
 AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int max_context) {
   AttnPlan p{};
@@ -109,7 +156,6 @@ AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int 
   const int mc = max_context > 0 ? max_context : 1;
   const long rows = (long)batch * hkv;
   auto wgs = [&](int w, int nt) { return rows * ceil_div(mc, 16 * nt * w); };
-  (void)elt_bytes;
   int waves = 4, nt = 8;
   // (at most 16 rows: 4-wave partitions, which the persistent batch-1 step
   // also runs; 8-wave ones would leave it)
@@ -124,13 +170,28 @@ AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int 
     const int per_wave = ceil_div(ceil_div(mc, 16), 4);
     while (nt > 4 && per_wave <= nt / 2) nt /= 2;
   }
+  // Long rows (8 or more 512-token partitions at max_context) over a grid of
+  // several rounds: the work-list form (attn_worklist), with 1024-token items
+  // for fp8 (8 waves x 8 blocks; f16 would spill at that size).  fp8long
+  // (32 rows x 4 KV heads, contexts 1106..30229): 103.3-103.6 us direct,
+  // 100.9 with 512-token items, 96.6-96.9 with 1024-token items.  Calls of a
+  // few partitions per row keep the direct grid (7B heads, batch 128,
+  // contexts 512-540: 47.0 us either way).
+  int worklist = 0;
+  if (batch <= kWorklistMaxRows && rows > 16 && waves == 4 && nt == 8 && ceil_div(mc, 512) >= 8 &&
+      wgs(4, 8) > 512) {
+    worklist = 1;
+    if (elt_bytes == 1) waves = 8;
+  }
+  p.worklist = worklist;
   p.waves = waves;
   p.nt = nt;
   p.max_context = mc;
   p.part = 16 * nt * waves;
   p.n_parts_max = ceil_div(mc, p.part);
   p.grid = batch * hkv * p.n_parts_max;
-  p.counter_bytes = align_up((size_t)batch * hkv * sizeof(int), 256);
+  // (the work-list form's item counter and exit count follow the arrival counters)
+  p.counter_bytes = align_up(((size_t)batch * hkv + 2) * sizeof(int), 256);
   const size_t ml = align_up((size_t)batch * hq * p.n_parts_max * sizeof(float2), 256);
   const size_t o = align_up((size_t)batch * hq * p.n_parts_max * head_dim * sizeof(float), 256);
   p.ws_bytes = p.counter_bytes + (p.n_parts_max > 1 ? ml + o : 0);
@@ -144,6 +205,20 @@ hipError_t launch_paged_attention(const AttnArgs& a, const AttnPlan& plan, hipSt
 }
 
 }  // namespace pkv
+
+#ifdef PKV_ATTN_STAMPS
+extern "C" int pkv_debug_attn_stamps(void* host, size_t bytes) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(pkv::g_attn_stamps), bytes, 0, hipMemcpyDeviceToHost);
+}
+extern "C" int pkv_debug_attn_stamps_clear(const void* zeros, size_t bytes) {
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(pkv::g_attn_stamps), zeros, bytes, 0, hipMemcpyHostToDevice);
+}
+#endif
+
+extern "C" pkv_status pkv_debug_attn_worklist(int enable) {
+  pkv::attn_worklist_enabled = enable;
+  return PKV_OK;
+}
 
 extern "C" pkv_status pkv_debug_attn_merge_wait(unsigned long long ticks) {
   pkv::attn_merge_wait_ticks = ticks;

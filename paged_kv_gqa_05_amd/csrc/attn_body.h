@@ -20,6 +20,21 @@ constexpr float kLog2e = 1.44269504088896341f;
 // Partitions the merge reads per round trip.
 constexpr int kMergeBatch = 8;
 
+#ifdef PKV_ATTN_STAMPS
+// measurement variant: wall-clock stamps per workgroup (start, context known,
+// partition computed, end) and what it did
+constexpr int kStampWgs = 16384;
+static __device__ unsigned long long g_attn_stamps[kStampWgs * 6];
+#define ATTN_STAMP(k) \
+  do { if (threadIdx.x == 0 && wg < kStampWgs) { if ((k) == 1) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); \
+       g_attn_stamps[wg * 6 + (k)] = wall_clock64(); } } while (0)
+#define ATTN_STAMP_INFO(v) \
+  do { if (threadIdx.x == 0 && wg < kStampWgs) { g_attn_stamps[wg * 6 + 4] = (v); g_attn_stamps[wg * 6 + 5] = __smid(); } } while (0)
+#else
+#define ATTN_STAMP(k) do {} while (0)
+#define ATTN_STAMP_INFO(v) do {} while (0)
+#endif
+
 struct SplitParams {
   const unsigned char* k_pool;
   const unsigned char* v_pool;
@@ -35,6 +50,8 @@ struct SplitParams {
   int batch, hq, hkv, group, part, n_parts_max;
   int num_blocks;    // blocks in the pool: a block id outside [0, num_blocks) is read as block 0
   int max_context;   // a longer context length is taken as max_context
+  int worklist;      // work-list mode (attn_worklist): the grid takes the call's
+                     // (row, KV head, partition) items longest rows first
   int merge_poll;    // every workgroup of the call is resident at once: the first
                      // partition of a row waits for the others and merges
   unsigned long long poll_ticks;  // its wait limit (wall-clock ticks; 0: publish at once)
@@ -128,13 +145,16 @@ constexpr int attn_min_waves() {
   return (W == 4 && NT <= 4) ? 3 : 1;
 }
 
-// The kernel body as a device function of the workgroup index, so that a
-// persistent kernel can run it (COH: q read and the output written with
-// agent-scope accesses; every exit is uniform over the workgroup, and the
-// caller separates two calls with a workgroup barrier).
+// The work of one (row b, KV head g, partition part_idx) item, as a device
+// function, so that the kernel, its work-list mode and a persistent kernel can
+// run it (COH: q read and the output written with agent-scope accesses; every
+// exit is uniform over the workgroup, and the caller separates two items with
+// a workgroup barrier).  wg names the item in measurement builds only.
 template <int D, bool FP8, int NT, int kWaves, bool COH>
-__device__ __forceinline__ void attn_body(const SplitParams& p, const int wg) {
+__device__ __forceinline__ void attn_item(const SplitParams& p, const int wg, const int b, const int g,
+                                          const int part_idx) {
   constexpr int kThreads = 64 * kWaves;
+  ATTN_STAMP(0);
   // padded LDS row (floats) for the combine of the four waves
   constexpr int OSTR = D + 4;
   __shared__ float s_o[kWaves][kMaxGroup][OSTR];
@@ -145,10 +165,7 @@ __device__ __forceinline__ void attn_body(const SplitParams& p, const int wg) {
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, q4 = lane >> 4;
 
-  // ---- this workgroup's (row, KV head, partition): wg = (b * Hkv + g) * P + part
-  const int part_idx = wg % p.n_parts_max;
-  const int bg = wg / p.n_parts_max;
-  const int b = bg / p.hkv, g = bg - b * p.hkv;
+  const int bg = b * p.hkv + g;
   const int tok0 = part_idx * p.part;
   const int hbase = g * p.group;
   // issued together, before the context length is known: the block-table
@@ -166,7 +183,10 @@ __device__ __forceinline__ void attn_body(const SplitParams& p, const int wg) {
                   : *reinterpret_cast<const h16x8*>(qrow + 8 * q_chunk<FP8>(s, q4));
   }
   const int c = min(max(p.lens[b], 0), p.max_context);  // (out-of-range lengths clamped)
+  ATTN_STAMP(1);
   if (tok0 >= c) {  // beyond the row's context (or an inactive row)
+    ATTN_STAMP(3);
+    ATTN_STAMP_INFO(0);
     if (c == 0 && g == 0 && part_idx == 0) {
       for (int idx = tid; idx < p.hq * D; idx += kThreads) {
         if constexpr (COH) st_agent_h(p.out + (size_t)b * p.hq * D + idx, (h16)0.f);
@@ -412,6 +432,7 @@ __device__ __forceinline__ void attn_body(const SplitParams& p, const int wg) {
     s_l[wave][n] = l_w;
   }
   __syncthreads();
+  ATTN_STAMP(2);
 
   const size_t bh0 = (size_t)b * p.hq + hbase;
   if (np == 1) {
@@ -431,6 +452,8 @@ __device__ __forceinline__ void attn_body(const SplitParams& p, const int wg) {
       else p.out[(bh0 + h) * D + d] = (h16)(O * p.v_scale / L);
       if (d == 0 && p.lse) p.lse[bh0 + h] = (mx + __log2f(L)) * kLn2;
     }
+    ATTN_STAMP(3);
+    ATTN_STAMP_INFO(1);
     return;
   }
 
@@ -497,7 +520,11 @@ __device__ __forceinline__ void attn_body(const SplitParams& p, const int wg) {
     if (tid == 0)
       s_last = __hip_atomic_fetch_add(p.counters + bg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
     __syncthreads();
-    if (!s_last) return;
+    if (!s_last) {
+      ATTN_STAMP(3);
+      ATTN_STAMP_INFO(2 + 16 * np);
+      return;
+    }
   }
 
   // ---- last partition of the row to finish: merge all np in partition order
@@ -547,6 +574,91 @@ __device__ __forceinline__ void attn_body(const SplitParams& p, const int wg) {
     }
     if (d == 0 && p.lse) p.lse[bh0 + h] = (M + __log2f(L)) * kLn2;
   }
+  ATTN_STAMP(3);
+  ATTN_STAMP_INFO((polled ? 4 : 3) + 16 * np);
+}
+
+// The item of workgroup wg in the direct mapping: wg = (b * Hkv + g) * P + part.
+template <int D, bool FP8, int NT, int kWaves, bool COH>
+__device__ __forceinline__ void attn_body(const SplitParams& p, const int wg) {
+  const int part_idx = wg % p.n_parts_max;
+  const int bg = wg / p.n_parts_max;
+  const int b = bg / p.hkv;
+  attn_item<D, FP8, NT, kWaves, COH>(p, wg, b, bg - b * p.hkv, part_idx);
+}
+
+// Work-list mode, for calls whose direct grid (every row's partitions counted
+// at max_context) spans several rounds of resident workgroups.  The direct
+// grid then spends a slot and a memory round trip on every partition past a
+// shorter row's context, and the rows dispatched last finish with their
+// merges at the very end.  Here a grid of resident workgroups reads the
+// context lengths once, orders the rows by their partition count (longest
+// first, ties by row), numbers the real items in that order (a row's items
+// KV head by KV head, partitions in order within a head), and takes items
+// from a shared counter: the long rows, whose merges read the most partials,
+// run and merge first, short rows fill the end, and a workgroup that merges
+// simply takes fewer items.  Every item is computed exactly as in the direct
+// mapping.  An inactive row (length 0) is one item per KV head, which writes
+// its zero output.  The counter and an exit count follow the arrival
+// counters; the last workgroup to leave sets both back to zero.
+constexpr int kWorklistMaxRows = 256;
+
+template <int D, bool FP8, int NT, int kWaves>
+__device__ __forceinline__ void attn_worklist(const SplitParams& p) {
+  constexpr int kThreads = 64 * kWaves;
+  __shared__ int s_np[kWorklistMaxRows];     // items of row r per KV head
+  __shared__ int s_first[kWorklistMaxRows];  // first item of the row of rank k
+  __shared__ int s_row[kWorklistMaxRows];    // the row of rank k
+  __shared__ int s_total, s_item;
+  const int tid = threadIdx.x;
+  const int B = p.batch;
+  int* work = p.counters + B * p.hkv;  // next item; then the exit count
+  int next = 0;
+  if (tid == 0) next = __hip_atomic_fetch_add(work, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int r = tid; r < B; r += kThreads) {
+    const int c = min(max(p.lens[r], 0), p.max_context);
+    s_np[r] = c > 0 ? (c + p.part - 1) / p.part : 1;
+  }
+  __syncthreads();
+  for (int r = tid; r < B; r += kThreads) {
+    const int nr = s_np[r];
+    int rank = 0, before = 0;
+    for (int j = 0; j < B; ++j) {
+      const int nj = s_np[j];
+      const bool ahead = nj > nr || (nj == nr && j < r);
+      rank += ahead ? 1 : 0;
+      before += ahead ? nj : 0;
+    }
+    s_row[rank] = r;
+    s_first[rank] = before * p.hkv;
+    if (rank == B - 1) s_total = (before + nr) * p.hkv;
+  }
+  if (tid == 0) s_item = next;
+  __syncthreads();
+  const int total = s_total;
+  int item = s_item;
+  while (item < total) {
+    if (tid == 0) next = __hip_atomic_fetch_add(work, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int lo = 0, hi = B - 1;  // the last rank whose first item is <= item
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_first[mid] <= item) lo = mid;
+      else hi = mid - 1;
+    }
+    const int r = s_row[lo], nr = s_np[r], j = item - s_first[lo];
+    const int g = j / nr;
+    attn_item<D, FP8, NT, kWaves, false>(p, item, r, g, j - g * nr);
+    __syncthreads();  // the item's LDS is free again
+    if (tid == 0) s_item = next;
+    __syncthreads();
+    item = s_item;
+  }
+  if (tid == 0 &&
+      __hip_atomic_fetch_add(work + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1) {
+    // every workgroup has taken its last item: reset for the next call
+    __hip_atomic_store(work, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(work + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // Kernel arguments from the call's arguments and plan (workspace: counters,
@@ -570,7 +682,8 @@ inline SplitParams make_split_params(const AttnArgs& a, const AttnPlan& plan) {
   sp.num_blocks = a.num_blocks;
   sp.max_context = plan.max_context;
   // the 8-wave plans keep the whole grid within one workgroup per CU
-  sp.merge_poll = plan.waves == 8 ? 1 : 0;
+  sp.merge_poll = plan.waves == 8 && !plan.worklist ? 1 : 0;
+  sp.worklist = 0;  // set by the work-list launch
   sp.poll_ticks = attn_merge_wait_ticks;
   sp.scale_log2 = a.scale * kLog2e * (a.fp8 ? a.k_scale : 1.0f);
   sp.v_scale = a.fp8 ? a.v_scale : 1.0f;

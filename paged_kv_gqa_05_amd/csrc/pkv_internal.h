@@ -58,14 +58,19 @@ struct AttnPlan {
   int n_parts_max;  // partitions per (row, kv head) for max_context
   int grid;         // workgroups of the attention kernel
   int max_context;  // the call's max_context (longer context lengths are taken as it)
-  size_t counter_bytes;  // leading workspace bytes: [B][Hkv] int arrival counters,
-                         // zero before the first call, left zero by every call
+  int worklist;     // long rows over a grid of several rounds: the work-list form
+  size_t counter_bytes;  // leading workspace bytes: [B][Hkv] int arrival counters and
+                         // the work-list item and exit counts, zero before the first
+                         // call, left zero by every call
   size_t ws_bytes;  // workspace bytes (counters + partials of multi-partition rows)
 };
 AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int max_context);
 // Wall-clock ticks the first partition of a row waits for the others before
 // it publishes its partial (pkv_debug_attn_merge_wait; 0 = publish at once).
 extern unsigned long long attn_merge_wait_ticks;
+// Whether plans of the work-list form run it (pkv_debug_attn_worklist;
+// default 1) or the direct grid of the same partitions.
+extern int attn_worklist_enabled;
 
 // A standalone attention workspace (pkv_paged_attn_decode) of W bytes keeps
 // its arrival counters in a leading region whose size depends on W alone

@@ -210,6 +210,38 @@ def test_merge_by_first_partition_equals_last_arriver_merge(lib):
         assert np.array_equal(lse.view(np.uint32), runs[0][1].view(np.uint32))
 
 
+@pytest.mark.parametrize("kv_dtype", ["f16", "fp8"])
+def test_worklist_form_equals_direct_grid(lib, kv_dtype):
+    """40 rows x 4 KV heads with log-uniform contexts up to 8192 (and three
+    inactive rows) need more workgroups than the device holds at once, so
+    the call runs in work-list form (only the partitions inside each row's
+    context, longest rows first).  The direct grid of every partition (hook
+    off) gives the same bits, both match the oracle, and the counter region
+    (arrival counters, item and exit counts) is zero after every call."""
+    rng = np.random.default_rng(31)
+    lens = inp.context_lengths(rng, 40, 1, 8192, "loguniform")
+    lens[[3, 17, 38]] = 0
+    lens[5] = 8192
+    case = inp.attention_case(40, 28, 4, 128, 1, 8192, seed=32, kv_dtype=kv_dtype, ctx_lens=lens)
+    cache = load_case_into_cache(lib, case)
+    ws = lib.attn_workspace(cache, 40, 28, case.max_context)
+    region = _counter_region(ws.numel())
+    runs = []
+    try:
+        for enable in (True, False, True):
+            lib.debug_attn_worklist(enable)
+            runs.append(run_attention(lib, case, cache=cache, ws=ws))
+            assert not ws[:region].any().item(), f"counters left set (work list {enable})"
+    finally:
+        lib.debug_attn_worklist(True)
+    ref, ref_lse = oracle_attention(case)
+    assert_parity(runs[0][0], ref, f"work-list form ({kv_dtype})")
+    assert np.all(runs[0][0][[3, 17, 38]] == 0) and np.all(np.isneginf(runs[0][1][[3, 17, 38]]))
+    for out, lse in runs[1:]:
+        assert np.array_equal(out.view(np.uint16), runs[0][0].view(np.uint16))
+        assert np.array_equal(lse.view(np.uint32), runs[0][1].view(np.uint32))
+
+
 def test_inactive_rows(lib):
     case = inp.attention_case(4, 4, 2, 64, 1, 40, seed=14, ctx_lens=[0, 5, 0, 33])
     out, lse = run_attention(lib, case)
