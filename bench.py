@@ -330,10 +330,32 @@ def time_attention(pkv, torch, w, n_pools, rounds, seed):
     other = 2 * q.numel() * 2 + bt.nbytes + lens.nbytes
     nbytes = kv_bytes + other
     cache.close()
+    del cache, q, out, ws
+    torch.cuda.empty_cache()
+    # the streaming-read reference: one plain read of the same byte count per
+    # call, over as many rotated buffers, timed the same way
+    sr_bytes = (nbytes + 15) // 16 * 16
+    bufs = torch.zeros(n_pools, sr_bytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for i in range(n_pools):
+        pkv.stream_read(bufs[i], sink)
+    with no_gc():
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(rounds):
+            for i in range(n_pools):
+                pkv.stream_read(bufs[i], sink)
+        e1.record()
+        torch.cuda.synchronize()
+    sr_ms = e0.elapsed_time(e1) / (rounds * n_pools)
+    del bufs
+    torch.cuda.empty_cache()
     return {"batch": w.batch, "heads": f"{w.n_q_heads}/{w.n_kv_heads}", "head_dim": w.head_dim,
             "kv_dtype": w.kv_dtype, "sum_context": int(lens.sum()), "bytes_per_call": nbytes,
             "us_per_call": ms * 1e3, "GBs": nbytes / (ms * 1e-3) / 1e9,
-            "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "rotated_pools": n_pools}
+            "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "rotated_pools": n_pools,
+            "stream_read_us_per_call": sr_ms * 1e3, "stream_read_GBs": sr_bytes / (sr_ms * 1e-3) / 1e9,
+            "frac_of_stream_read": sr_ms / ms}
 
 
 def time_sampling(pkv, torch, inp, batch, vocab, rounds, seed, mode):
@@ -640,9 +662,11 @@ def main():
     attn = {}
     if not args.no_attn:
         attn["attn15"] = time_attention(pkv, torch, inp.ATTN15, 28, args.attn_rounds, seed=11)
-        log(f"attn15: {attn['attn15']['us_per_call']:.2f} us/call, {attn['attn15']['GBs']:.0f} GB/s")
+        log(f"attn15: {attn['attn15']['us_per_call']:.2f} us/call, {attn['attn15']['GBs']:.0f} GB/s "
+            f"(a streaming read of the same bytes: {attn['attn15']['stream_read_us_per_call']:.2f} us)")
         attn["fp8long"] = time_attention(pkv, torch, inp.FP8LONG, 8, args.attn_rounds, seed=12)
-        log(f"fp8long: {attn['fp8long']['us_per_call']:.2f} us/call, {attn['fp8long']['GBs']:.0f} GB/s")
+        log(f"fp8long: {attn['fp8long']['us_per_call']:.2f} us/call, {attn['fp8long']['GBs']:.0f} GB/s "
+            f"(a streaming read of the same bytes: {attn['fp8long']['stream_read_us_per_call']:.2f} us)")
 
     sampling = {}
     if not args.no_sample:
@@ -672,7 +696,9 @@ def main():
                                                         "attn15: 1.5B layer shape, batch 64, contexts U[128, 2048]",
                               "achieved": round(a["GBs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": round(a["GBs"] / HBM_PEAK_GBS, 4), "traffic": attention_traffic(),
-                              "bytes_per_launch": a["bytes_per_call"], "us_per_launch": round(a["us_per_call"], 3)}
+                              "bytes_per_launch": a["bytes_per_call"], "us_per_launch": round(a["us_per_call"], 3),
+                              "stream_read_GBs": round(a["stream_read_GBs"], 1),
+                              "frac_of_stream_read": round(a["frac_of_stream_read"], 4)}
     if roofline is None:
         roofline = roofline_attention
     cpu = None

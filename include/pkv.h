@@ -393,6 +393,19 @@ pkv_status pkv_prefill(const pkv_model* model, pkv_cache* cache, const int32_t* 
 pkv_status pkv_argmax(const void* logits, int batch, int vocab, int32_t* tokens, const int32_t* context_lens,
                       pkv_stream_t stream);
 
+/* Measurement reference (not a step of the path): one plain streaming read
+ * of `bytes` of device memory at `data` (16-byte aligned, bytes a positive
+ * multiple of 16), 16-byte loads, each workgroup over its own contiguous
+ * range.  Its time is what one launch of that many cold bytes can draw from
+ * HBM on this device, against which the attention's achieved GB/s is also
+ * reported (the rvLLM post, section "PagedAttention과 FlashAttention-3",
+ * states attention as bound by the KV bytes it reads).  sink: a device int32
+ * that is written (with 1) only if the XOR of every 32-bit word of some
+ * thread's share of the data equals 0x9e3779b9 (tests plant such a word).
+ * PKV_E_ARG for NULL pointers, a misaligned `data` or a bad size; nothing is
+ * enqueued then. */
+pkv_status pkv_stream_read(const void* data, size_t bytes, int32_t* sink, pkv_stream_t stream);
+
 /* Sampled token per row, after the forward pass (zingnex.cn article, section
  * 支持的参数: temperature (0 = greedy), top_p, top_k (-1 = disabled)).  All
  * per-row arrays are device memory, [batch]: temperature f32, top_k int32,

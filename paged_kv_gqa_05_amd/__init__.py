@@ -275,6 +275,16 @@ def argmax(logits, tokens, context_lens=None, stream=None):
                            _stream(stream)))
 
 
+def stream_read(data, sink, stream=None):
+    """Measurement reference: one streaming read of every byte of `data` (a
+    contiguous CUDA tensor, 16-byte aligned, size a multiple of 16); `sink`
+    (int32 CUDA tensor) is set to 1 only if the data hold the planted fold."""
+    if not data.is_cuda or not data.is_contiguous():
+        raise ValueError("data must be a contiguous CUDA tensor")
+    _need(sink, torch.int32, "sink")
+    _check(_lib.pkv_stream_read(_p(data), data.numel() * data.element_size(), _p(sink), _stream(stream)))
+
+
 class Graph:
     """One captured decode step; replay() launches it on the caller's stream."""
 

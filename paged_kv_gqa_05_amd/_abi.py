@@ -60,6 +60,7 @@ SIGNATURES = {
     "pkv_decode_step": (c_status, [vp, vp, i32p, i32p, C.c_int, i32p, C.c_int, C.c_int, vp, vp,
                                    vp, size_t, vp]),
     "pkv_argmax": (c_status, [vp, C.c_int, C.c_int, i32p, i32p, vp]),
+    "pkv_stream_read": (c_status, [vp, size_t, i32p, vp]),
     "pkv_prefill_workspace_bytes": (c_status, [vp, vp, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_size_t)]),
     "pkv_prefill": (c_status, [vp, vp, i32p, i32p, i32p, C.c_int, C.c_int, i32p, C.c_int, C.c_int, vp, vp,
                                C.c_size_t, vp]),

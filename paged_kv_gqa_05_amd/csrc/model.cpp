@@ -558,6 +558,14 @@ pkv_status pkv_argmax(const void* logits, int batch, int vocab, int32_t* tokens,
   return PKV_OK;
 }
 
+pkv_status pkv_stream_read(const void* data, size_t bytes, int32_t* sink, pkv_stream_t stream) {
+  if (!data || !sink) return fail(PKV_E_ARG, "NULL argument");
+  if (bytes == 0 || bytes % 16 != 0) return fail(PKV_E_ARG, "bytes must be a positive multiple of 16");
+  if (reinterpret_cast<uintptr_t>(data) % 16 != 0) return fail(PKV_E_ARG, "data must be 16-byte aligned");
+  PKV_HIP(launch_stream_read(data, bytes, sink, static_cast<hipStream_t>(stream)));
+  return PKV_OK;
+}
+
 pkv_status pkv_sample(const void* logits, int batch, int vocab, const float* temperature, const int32_t* top_k,
                       const float* top_p, const float* uniform, int32_t* tokens, const int32_t* context_lens,
                       pkv_stream_t stream) {

@@ -46,6 +46,9 @@ hipError_t launch_prefill_items(const PrefillAttnArgs& a, int group, hipStream_t
 // Attention of every layer, over the work list built above.
 hipError_t launch_prefill_attention(const PrefillAttnArgs& a, hipStream_t s);
 
+// One streaming read of `bytes` (a multiple of 16) at 16-byte aligned `data`;
+// *sink is set only if the data hold the planted fold value.
+hipError_t launch_stream_read(const void* data, size_t bytes, int32_t* sink, hipStream_t s);
 hipError_t launch_argmax(const void* logits, int batch, int vocab, int32_t* tokens, const int32_t* lens,
                          hipStream_t s);
 // r = f16(r + x), then x = 0, over n f16 elements; zeroes zero_n ints at zero_p.

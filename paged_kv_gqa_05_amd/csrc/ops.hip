@@ -140,6 +140,35 @@ hipError_t launch_prefill_rows(const int32_t* seq_starts, const int32_t* prior_l
   return hipGetLastError();
 }
 
+// A plain streaming read, the reference for what one launch of a given size
+// can draw from HBM: workgroup w reads its own contiguous range of 16-byte
+// units once, eight loads in flight per thread, and folds them with XOR; a
+// thread whose fold equals kStreamMagic sets *sink (so the loads cannot be
+// dropped, and a test can plant the value).
+constexpr uint32_t kStreamMagic = 0x9e3779b9u;
+
+__global__ void __launch_bounds__(256) stream_read_kernel(const uint4* __restrict__ p, size_t n, size_t per_wg,
+                                                          int32_t* __restrict__ sink) {
+  const size_t lo = (size_t)blockIdx.x * per_wg, hi = std::min(n, lo + per_wg);
+  uint4 acc = uint4{0, 0, 0, 0};
+  for (size_t i = lo + threadIdx.x; i < hi; i += 8 * 256) {
+    uint4 q[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t j = i + (size_t)u * 256;
+      q[u] = j < hi ? p[j] : uint4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc.x ^= q[u].x;
+      acc.y ^= q[u].y;
+      acc.z ^= q[u].z;
+      acc.w ^= q[u].w;
+    }
+  }
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == kStreamMagic) *sink = 1;
+}
+
 hipError_t launch_embed(const void* table, int table_rows, const int32_t* tokens, void* h, int batch, int hidden,
                         int* zero_p, int zero_n, hipStream_t s) {
   hipLaunchKernelGGL(embed_kernel, dim3(batch), dim3(256), 0, s, static_cast<const h16*>(table), table_rows, tokens,
@@ -160,6 +189,16 @@ hipError_t launch_argmax(const void* logits, int batch, int vocab, int32_t* toke
   const int vec = (vocab % 8 == 0) && (reinterpret_cast<uintptr_t>(logits) % 16 == 0);
   hipLaunchKernelGGL(argmax_kernel, dim3(batch), dim3(1024), 0, s, static_cast<const h16*>(logits), vocab,
                      tokens, vec, lens);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void* data, size_t bytes, int32_t* sink, hipStream_t s) {
+  const size_t n = bytes / 16;
+  // about 8 units a thread per workgroup, at most 2048 workgroups
+  const size_t grid = std::min<size_t>(std::max<size_t>((n + 2047) / 2048, 1), 2048);
+  const size_t per_wg = (n + grid - 1) / grid;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const uint4*>(data), n,
+                     per_wg, sink);
   return hipGetLastError();
 }
 

@@ -194,6 +194,18 @@ def test_sample_and_prefill_argument_errors():
     assert b"model / cache is NULL" in lib.pkv_last_error()
 
 
+def test_stream_read_argument_errors():
+    """pkv_stream_read rejects NULL pointers, sizes that are not a positive
+    multiple of 16 and misaligned data on the host (nothing is enqueued)."""
+    lib = pkv.lib()
+    sink = C.c_void_p(FAKE_DEV)
+    for data, nbytes, msg in ((None, 16, b"NULL"), (FAKE_DEV, 0, b"multiple of 16"),
+                              (FAKE_DEV, 24, b"multiple of 16"), (FAKE_DEV + 8, 32, b"aligned")):
+        assert lib.pkv_stream_read(data, nbytes, sink, None) == 1
+        assert msg in lib.pkv_last_error()
+    assert lib.pkv_stream_read(FAKE_DEV, 16, None, None) == 1
+
+
 def test_handle_alive_at_interpreter_exit_is_released_quietly():
     """An object still holding a native handle when the interpreter exits is
     destroyed by __del__ while the module's globals are being cleared; that
