@@ -272,6 +272,75 @@ def test_graph_replay_matches_eager_and_sees_new_metadata(lib):
     g.close()
 
 
+def test_long_context_layer_in_worklist_form(lib):
+    """40 rows x 2 KV heads with contexts of 600-4096 tokens: the layer's
+    attention runs in work-list form (long rows over a grid of several
+    rounds).  The layer matches the oracle, and the direct grid of the same
+    partitions (hook off) gives the same bits."""
+    rng = np.random.default_rng(4101)
+    lens = inp.context_lengths(rng, 40, 600, 4096, "loguniform")
+    lens[7] = 4096
+    case = inp.tiny_layer_case(seed=4102, batch=40, shape=MID, ctx_lens=lens)
+    rh, _, _ = _oracle_layer(MID, case)
+    outs = []
+    try:
+        for enable in (True, False):
+            lib.debug_attn_worklist(enable)
+            h, _, _ = _run_layer_gpu(lib, MID, case)
+            outs.append(h)
+    finally:
+        lib.debug_attn_worklist(True)
+    assert_parity(outs[0], rh, "long-context layer (work-list form)")
+    assert np.array_equal(outs[0].view(np.uint16), outs[1].view(np.uint16))
+
+
+def test_graph_replay_with_worklist_attention_matches_eager(lib):
+    """A captured step whose attention runs in work-list form (24 rows x 2 KV
+    heads, contexts up to 8000 over a random pre-filled cache): four replays
+    with advancing lengths equal the eager steps bit for bit, and so does the
+    eager step on the direct grid (hook off)."""
+    shape = MID
+    batch, mc = 24, 8192
+    rng = np.random.default_rng(4201)
+    w = inp.model_weights(shape, 4202, bias=True, norm_jitter=True, std=0.05)
+    model = lib.Model(shape, weights_to_device(w), max_positions=mc)
+    stride = mc // 16
+    nb = batch * stride + 5
+    cache = lib.KVCache(shape.n_layers, nb, shape.n_kv_heads, shape.head_dim)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4203)
+    for layer in range(shape.n_layers):
+        for t in cache.layer(layer):
+            t.normal_(generator=g)
+    bt = dev(rng.permutation(nb)[: batch * stride].astype(np.int32).reshape(batch, stride))
+    lens_h = inp.context_lengths(rng, batch, 600, 7990, "loguniform")
+    toks_h = rng.integers(0, shape.vocab, size=(5, batch)).astype(np.int32)
+    ws = torch.empty(lib.step_workspace_bytes(model, cache, batch, mc), dtype=torch.uint8, device="cuda")
+    logits = torch.empty(batch, shape.vocab, dtype=torch.float16, device="cuda")
+    toks, lens = dev(toks_h[0]), dev(lens_h)
+    graph = lib.Graph(model, cache, toks, bt, lens, mc, logits, ws)
+    try:
+        for t in range(4):
+            lens_h = lens_h + 1
+            toks.copy_(torch.from_numpy(toks_h[t]))
+            lens.copy_(torch.from_numpy(lens_h))
+            runs = []
+            for mode in ("eager", "direct", "graph"):
+                lib.debug_attn_worklist(mode != "direct")
+                if mode == "graph":
+                    graph.replay()
+                else:
+                    lib.decode_step(model, cache, toks, bt, lens, mc, logits, ws)
+                torch.cuda.synchronize()
+                runs.append(logits.cpu().numpy().copy())
+            assert np.all(np.isfinite(runs[0]))
+            for r in runs[1:]:
+                assert np.array_equal(r.view(np.uint16), runs[0].view(np.uint16)), t
+    finally:
+        lib.debug_attn_worklist(True)
+        graph.close()
+
+
 def test_graph_set_buckets_with_inactive_rows(lib):
     """Buckets 1/4/8 over shared buffers: 3 active rows run in bucket 4, then 6
     in bucket 8 (rows 3-5 join); active rows match the oracle, padding rows get
