@@ -9,8 +9,9 @@
 //
 // Design (MI355X, not the pages' FlashAttention-3 kernels):
 //  * One workgroup of W waves (4 or 8) per (row b, KV head g, partition of
-//    16 NT W tokens), blockIdx = (b * Hkv + g) * P + partition; partitions
-//    beyond a row's context exit at once.  The row's block-table entries and
+//    16 NT W tokens), partition-major: blockIdx = partition * B * Hkv +
+//    b * Hkv + g, so that every row's first partition is dispatched before
+//    any later one; partitions beyond a row's context exit at once.  The row's block-table entries and
 //    the query rows are loaded together with the context length, so a
 //    workgroup waits one memory round trip before its KV loads.
 //  * Wave w of a partition owns its blocks w, w + W, ... (at most NT) and loads

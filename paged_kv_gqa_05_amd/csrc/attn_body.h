@@ -578,11 +578,17 @@ __device__ __forceinline__ void attn_item(const SplitParams& p, const int wg, co
   ATTN_STAMP_INFO((polled ? 4 : 3) + 16 * np);
 }
 
-// The item of workgroup wg in the direct mapping: wg = (b * Hkv + g) * P + part.
+// The item of workgroup wg in the direct mapping, partition-major:
+// wg = part * (B * Hkv) + b * Hkv + g.  The hardware dispatches workgroups in
+// index order over a few microseconds, so every row's first (full) partition
+// starts before any row's later, shorter one: attn15 19.0-19.6 -> 18.3-19.0
+// us, 7B heads at batch 128 with 512-540-token contexts (second partitions of
+// 15-28 tokens) 47.8 -> 40.7-41.4 us.  Results do not depend on the order.
 template <int D, bool FP8, int NT, int kWaves, bool COH>
 __device__ __forceinline__ void attn_body(const SplitParams& p, const int wg) {
-  const int part_idx = wg % p.n_parts_max;
-  const int bg = wg / p.n_parts_max;
+  const int rows = p.batch * p.hkv;
+  const int part_idx = wg / rows;
+  const int bg = wg - part_idx * rows;
   const int b = bg / p.hkv;
   attn_item<D, FP8, NT, kWaves, COH>(p, wg, b, bg - b * p.hkv, part_idx);
 }
