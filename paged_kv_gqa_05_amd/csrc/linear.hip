@@ -54,6 +54,20 @@ hipError_t gemv_dispatch_lpr(const LinArgs& a, hipStream_t s) {
   const int steps = (a.K / 8 + LPR - 1) / LPR;
   if (steps <= 2) return gemv_dispatch_mt<LPR, EPI, NORM, 2>(a, s);
   if (steps <= 4) return gemv_dispatch_mt<LPR, EPI, NORM, 4>(a, s);
+  if constexpr (LPR == 256 && EPI == EPI_RESID) {
+    // rows a little over 8 steps of 256 lanes (the 7B down projection: 9.25)
+    // take one round of 10 steps at batch <= 2 rather than a round of 8 and
+    // a nearly empty second one (each lane's chunks and their order are the
+    // same, so are the bits)
+    if (steps > 8 && steps <= 10 && a.M <= 2) {
+      const int grid = a.n_out;
+      if (a.M <= 1)
+        hipLaunchKernelGGL((gemv_kernel<256, 1, 10, EPI, NORM>), dim3(grid), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((gemv_kernel<256, 2, 10, EPI, NORM>), dim3(grid), dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   return gemv_dispatch_mt<LPR, EPI, NORM, 8>(a, s);
 }
 
