@@ -144,7 +144,8 @@ AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int 
   // critical path, so partitions are as large as possible while every
   // workgroup of the call can still be resident at once:
   //  * 8 waves x 8 blocks (1024 tokens, one workgroup per CU) when a row can
-  //    exceed 512 tokens and the partitions fit in 256 workgroups;
+  //    exceed 512 tokens and the partitions fit in 256 workgroups, unless
+  //    that is one partition per row for fewer than 192 rows (then 4 x 4);
   //  * else 4 waves x 8 blocks (512 tokens, one per CU: 296 registers at f16);
   //  * else, when those exceed 256 workgroups, 4 waves x 4 blocks (256
   //    tokens, three per CU) if that fits in 768;
@@ -160,7 +161,12 @@ AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int 
   int waves = 4, nt = 8;
   // (at most 16 rows: 4-wave partitions, which the persistent batch-1 step
   // also runs; 8-wave ones would leave it)
-  if (mc > 512 && wgs(8, 8) <= 256 && rows > 16) {
+  if (mc > 512 && mc <= 1024 && rows > 16 && rows < 192) {
+    // one 8-wave partition per row would leave a quarter or more of the CUs
+    // idle: 256-token partitions instead (7B heads, batch 32, contexts
+    // 512-545, 128 rows: 12.2-13.1 -> 12.0-12.2 us)
+    nt = 4;
+  } else if (mc > 512 && wgs(8, 8) <= 256 && rows > 16) {
     waves = 8;
   } else {
     if (wgs(4, 8) > 256 && wgs(4, 4) <= 768) nt = 4;
