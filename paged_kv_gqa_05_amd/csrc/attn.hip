@@ -119,6 +119,12 @@ hipError_t launch_impl(const SplitParams& sp, const AttnPlan& plan, hipStream_t 
     return hipGetLastError();
   }
   if (plan.waves == 8) {
+    if constexpr (!FP8) {
+      if (plan.nt == 6) {
+        launch_cfg<D, FP8, 6, 8>(sp, plan, s);
+        return hipGetLastError();
+      }
+    }
     launch_cfg<D, FP8, 8, 8>(sp, plan, s);
   } else {
     switch (plan.nt) {
@@ -146,6 +152,8 @@ AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int 
   //  * 8 waves x 8 blocks (1024 tokens, one workgroup per CU) when a row can
   //    exceed 512 tokens and the partitions fit in 256 workgroups, unless
   //    that is one partition per row for fewer than 192 rows (then 4 x 4);
+  //  * with more rows of at most 768 f16 tokens, 8 waves x 6 blocks (one
+  //    partition per row over two rounds);
   //  * else 4 waves x 8 blocks (512 tokens, one per CU: 296 registers at f16);
   //  * else, when those exceed 256 workgroups, 4 waves x 4 blocks (256
   //    tokens, three per CU) if that fits in 768;
@@ -168,6 +176,13 @@ AttnPlan attn_plan(int batch, int hq, int hkv, int head_dim, int elt_bytes, int 
     nt = 4;
   } else if (mc > 512 && wgs(8, 8) <= 256 && rows > 16) {
     waves = 8;
+  } else if (elt_bytes == 2 && mc > 512 && mc <= 768 && rows > 256) {
+    // more than 256 rows of at most 768 tokens: one 8-wave partition of 6
+    // blocks a wave per row, so no row is split into a full partition and a
+    // few-token remainder with its merge (7B heads at batch 128, contexts
+    // 512-545, 512 rows: 40.9-41.8 -> 30.1-30.8 us; 8 x 8 blocks 31.7-32.5)
+    waves = 8;
+    nt = 6;
   } else {
     if (wgs(4, 8) > 256 && wgs(4, 4) <= 768) nt = 4;
     while (nt > 2 && wgs(4, nt) < 256 && ceil_div(mc, 64 * nt) > 1) nt /= 2;
