@@ -42,6 +42,7 @@ def oracle_attention(case):
     (9, 12, 2, 128, 900, 2000, 7),     # 18 pairs x 2 partitions dealt to the XCDs, last round partly empty
     (9, 12, 2, 128, 1, 4000, 9),       # the same with up to 4 partitions per pair
     (24, 28, 4, 128, 500, 1000, 10),   # 96 rows of at most 1024 tokens: 256-token partitions, merged
+    (130, 28, 4, 128, 500, 760, 11),   # 520 rows of at most 768 tokens: one 8-wave partition per row
 ])
 def test_attention_parity_f16(lib, b, hq, hkv, d, lo, hi, seed):
     case = inp.attention_case(b, hq, hkv, d, lo, hi, seed)
